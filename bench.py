@@ -1,0 +1,242 @@
+"""Benchmark: GEMM TFLOP/s and fraction of the MI355X MFMA (or HBM) roofline
+for each schedule (data-parallel, persistent, Stream-K, hybrid) on one GPU.
+
+A step is one C = A.B of the workload through the C ABI (every MAC, every
+Stream-K fixup, every store).  Each schedule is timed over --steps steps
+after --warmup untimed ones; before every step a 512 MiB fill evicts L2 and
+the Infinity Cache (outside the timed window), and HIP events on the launch
+stream bracket the GEMM alone.  The line's value is the best schedule's
+TFLOP/s; every schedule's figures are in "schedules".
+
+Prints exactly one JSON line on stdout; progress goes to stderr.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "f32": 157.3}  # dense MFMA, 2.4 GHz
+PEAK_HBM_GBS = 8000.0
+SCHEDULES = ("dp", "persistent", "streamk", "hybrid")
+METRIC = "GEMM TFLOP/s and % of MFMA peak per schedule (DP / persistent / Stream-K)"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("kernels.hip", "kernels.h", "schedule.h", "api.hip"):
+        with open(os.path.join(ROOT, "persistent_stream_tiling_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def workload_table():
+    from persistent_stream_tiling_amd import inputs
+    return dict(inputs.WORKLOADS, **inputs.irregular_workloads())
+
+
+def to_device(bits, dtype):
+    import torch
+    if dtype == "f32":
+        t = torch.from_numpy(np.ascontiguousarray(bits).view(np.float32))
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+        t = t.view(torch.float16 if dtype == "f16" else torch.bfloat16)
+    return t.to("cuda")
+
+
+def algorithmic_bytes(M, N, K, dtype, plan_info):
+    """A and B read once, C written once, Stream-K partials written and read once."""
+    e = 4 if dtype == "f32" else 2
+    base = (M * K + K * N) * e + M * N * 4
+    return base
+
+
+def partial_bytes(plan):
+    """Bytes of Stream-K partial tiles written (and read back) by one run."""
+    info = plan.info
+    n = 0
+    for w in range(info["launch_grid"] if info["tiles_sk"] else 0):
+        for (_, _, _, role, _) in plan.segments(w):
+            if role == 1:
+                n += 1
+    return n * info["bm"] * info["bn"] * 4
+
+
+def time_schedule(plan, a, b, c, ws, steps, warmup, flush):
+    import torch
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        plan.run(a, b, c, ws)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        flush.zero_()
+        starts[i].record(stream)
+        plan.run(a, b, c, ws)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    return ms, wall
+
+
+def cpu_baseline(a_bits, b_bits, M, N, K, dtype, seed, target_s):
+    """The oracle, as it is, on a bounded sample of output elements."""
+    import oracle
+    from persistent_stream_tiling_amd import inputs
+    threads = oracle.default_threads()
+    rows, cols = inputs.sample_positions(M, N, 4096, seed=seed)
+    t = time.perf_counter()
+    oracle.gemm_sampled(a_bits, b_bits, dtype, rows[:threads * 2], cols[:threads * 2], threads)
+    per = (time.perf_counter() - t) / (threads * 2)
+    n = int(min(4096, max(threads * 4, target_s / max(per, 1e-9))))
+    rows, cols = rows[:n], cols[:n]
+    t = time.perf_counter()
+    ref, scale = oracle.gemm_sampled(a_bits, b_bits, dtype, rows, cols, threads)
+    secs = time.perf_counter() - t
+    return {"value": 2.0 * K * n / secs / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{n} seeded output elements of the {M}x{N}x{K} {dtype} product "
+                      f"(fp64, {secs:.1f} s)"}, (rows, cols, ref, scale)
+
+
+def load_traffic(workload, schedule):
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        table = json.load(open(path))
+    except ValueError:
+        return None
+    rec = table.get(f"{workload}/{schedule}")
+    if not rec or rec.get("source_hash") != kernel_source_hash():
+        return None  # counters were taken on another kernel build
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="fp16_4096")
+    ap.add_argument("--schedules", default=",".join(SCHEDULES))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--report", default=None, help="also append per-schedule records here")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import persistent_stream_tiling_amd as gsk
+    from persistent_stream_tiling_amd import inputs, tuning
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    wl = workload_table()[args.workload]
+    M, N, K, dt = wl["M"], wl["N"], wl["K"], wl["dtype"]
+    log(f"[bench] {args.workload}: {M}x{N}x{K} {dt} {wl['dist']} seed {wl['seed']}")
+    a_bits, b_bits = inputs.operands(M, N, K, dt, wl["dist"], wl["seed"], wl["scale"])
+    a, b = to_device(a_bits, dt), to_device(b_bits, dt)
+    c = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    flops = 2.0 * M * N * K
+    bound = "hbm" if args.workload == "bf16_512x512x65536" else "mfma"
+
+    results = {}
+    for sched in args.schedules.split(","):
+        tiles = tuning.bench_tiles(args.workload, sched, dt)
+        plan = gsk.GemmPlan(M, N, K, dt, sched, **tiles)
+        ws = plan.new_workspace()
+        log(f"[bench] {sched}: {plan.describe()}")
+        ms, wall = time_schedule(plan, a, b, c, ws, args.steps, args.warmup, flush)
+        if ws is not None and plan.workspace_status(ws) != 0:
+            raise RuntimeError(f"{sched}: a Stream-K fixup wait gave up")
+        mean_ms = float(ms.mean())
+        tflops = flops / (mean_ms * 1e-3) / 1e12
+        bytes_alg = algorithmic_bytes(M, N, K, dt, plan.info) + 2 * partial_bytes(plan)
+        rec = {"tflops": round(tflops, 2), "ms": round(mean_ms, 5),
+               "ms_min": round(float(ms.min()), 5), "ms_median": round(float(np.median(ms)), 5),
+               "frac_mfma": round(tflops / PEAK_TFLOPS[dt], 4),
+               "hbm_gbs": round(bytes_alg / (mean_ms * 1e-3) / 1e9, 1),
+               "algorithmic_bytes": bytes_alg,
+               "tiles": tiles, "grid": plan.info["launch_grid"],
+               "tiles_sk": plan.info["tiles_sk"], "wall_s": round(wall, 3)}
+        results[sched] = (rec, plan, ws)
+        log(f"[bench] {sched}: {mean_ms:.4f} ms  {tflops:.1f} TFLOP/s  "
+            f"({100 * rec['frac_mfma']:.1f}% of MFMA peak), {rec['hbm_gbs']:.0f} GB/s algorithmic")
+
+    best = max(results, key=lambda s: results[s][0]["tflops"])
+    rec, plan, ws = results[best]
+
+    cpu = None
+    check = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample ...")
+        cpu, (rows, cols, ref, scale) = cpu_baseline(a_bits, b_bits, M, N, K, dt, wl["seed"] + 7,
+                                                     args.cpu_seconds)
+        plan.run(a, b, c, ws)
+        torch.cuda.synchronize()
+        got = c[torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()].cpu().numpy()
+        rel = np.abs(got.astype(np.float64) - ref) / np.maximum(scale, 1e-300)
+        check = {"samples": int(rows.size), "max_err_over_S": float(rel.max()),
+                 "tolerance": 1e-5 if dt == "f32" else 4e-3}
+        log(f"[bench] oracle check on {rows.size} samples: max |C-C_ref|/S = {rel.max():.3e}")
+
+    if bound == "mfma":
+        roof = {"bound": "mfma", "achieved": rec["tflops"], "peak": PEAK_TFLOPS[dt],
+                "unit": "TFLOP/s", "frac": round(rec["tflops"] / PEAK_TFLOPS[dt], 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": rec["hbm_gbs"], "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(rec["hbm_gbs"] / PEAK_HBM_GBS, 4)}
+    roof["traffic"] = load_traffic(args.workload, best)
+
+    line = {
+        "metric": METRIC,
+        "value": rec["tflops"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": rec["ms"],
+        "higher_is_better": True,
+        "scaling": "strong",
+        "vs_baseline": None,
+        "dtype": dt,
+        "data": "synthetic",
+        "config": {"workload": args.workload, "M": M, "N": N, "K": K,
+                   "distribution": wl["dist"], "schedule": best, "tiles": rec["tiles"],
+                   "grid": rec["grid"]},
+        "schedules": {s: r[0] for s, r in results.items()},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "oracle_check": check,
+        "kernel_source": kernel_source_hash(),
+    }
+    if args.report:
+        with open(args.report, "a") as f:
+            f.write(json.dumps(line) + "\n")
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

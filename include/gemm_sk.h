@@ -1,0 +1,200 @@
+/*
+ * gemm_sk -- tiled dense C = A.B on one MI355X (gfx950) with four work
+ * schedules: data-parallel tiles, a persistent grid, Stream-K, and the
+ * Stream-K + data-parallel hybrid.
+ *
+ * The operation.  C[i][j] = sum_k A[i][k] * B[k][j] for an M x K matrix A and
+ * a K x N matrix B ("naive vs persistent matmul" post on the Hugging Face
+ * activity feed page: the MxK . KxN product, computed one output tile at a
+ * time as a sum-reduction across K).  A and B are fp32, fp16 or bf16; the
+ * products are accumulated in fp32 (Triton issue #1393 "Stream-k matmul
+ * implementation very slow...", final revision, where the accumulator type is
+ * fp32 for fp16/bf16/fp32 inputs) and C is written as fp32.
+ *
+ * The schedules (same two pages):
+ *   GEMM_DP          one workgroup per output tile; the hardware hands CUs new
+ *                    workgroups as old ones finish (the post's "naive" matmul).
+ *   GEMM_PERSISTENT  g workgroups (default: one per CU) stay alive and loop over
+ *                    tiles p, p+g, p+2g, ... (the post's persistent matmul).
+ *   GEMM_STREAMK     the T * ipt MAC iterations of all tiles are split evenly
+ *                    over g workgroups, workgroup p getting iterations
+ *                    [p*q + min(p,r), (p+1)*q + min(p+1,r)) with q = I / g and
+ *                    r = I mod g (issue #1393, the first-wave kernel).  A tile
+ *                    shared by several workgroups is finished by a fixup.
+ *   GEMM_HYBRID      Stream-K over the first T_sk tiles, data-parallel over the
+ *                    rest, with T_sk = T mod g, plus g more when two_tiles is on
+ *                    and more than g tiles would remain (issue #1393, the host
+ *                    wrapper of the final revision).
+ *
+ * Fixup (replaces the pages' lock + float atomic_add).  Of the workgroups that
+ * share a split tile, the one covering the tile's first k-iteration (the
+ * "owner") waits for the others, which each store their fp32 partial tile in
+ * a workspace slot and raise a flag; the owner adds the partials to its own
+ * accumulator one by one in ascending workgroup order (= ascending k) and
+ * writes C.  There are no floating-point atomics, so one plan gives bitwise
+ * identical C on every run.  Different schedules may differ in the last bits.
+ *
+ * Layout.  A is M x K row-major (leading dimension K), B is K x N row-major
+ * (leading dimension N), C is M x N fp32 row-major (leading dimension N).  A, B
+ * and C are device pointers; A and B must be 16-byte aligned.  C is fully
+ * overwritten (no zero fill needed).  Rows whose byte length is not a multiple
+ * of 16 are repacked into the workspace before the multiply.
+ *
+ * Threading.  Plans are immutable after creation and may be shared between
+ * host threads.  gemm_last_error() is thread-local.
+ */
+#ifndef GEMM_SK_H
+#define GEMM_SK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { GEMM_F32 = 0, GEMM_F16 = 1, GEMM_BF16 = 2 } gemm_dtype;
+
+typedef enum {
+    GEMM_DP = 0,
+    GEMM_PERSISTENT = 1,
+    GEMM_STREAMK = 2,
+    GEMM_HYBRID = 3
+} gemm_schedule;
+
+/* gemm_tiles.flags */
+enum {
+    /* Hybrid: use one-tile Stream-K (T_sk = T mod g) instead of the default
+     * two-tile form (issue #1393, final revision's two_tiles switch). */
+    GEMM_FLAG_ONE_TILE = 1u << 0,
+    /* Do not remap workgroup ids so that each XCD gets a contiguous run of
+     * tiles (for measuring what the remap buys). */
+    GEMM_FLAG_NO_XCD_REMAP = 1u << 1
+};
+
+/* Tile and schedule knobs.  Every field 0 means "default". */
+typedef struct {
+    int32_t bm, bn;   /* output tile (multiples of 32 from the supported set;
+                         default per dtype and shape) */
+    int32_t bk;       /* k-depth of one MAC iteration: fixed at 128 bytes of
+                         input per row (64 for fp16/bf16, 32 for fp32); 0 or
+                         that value */
+    int32_t grid;     /* g: workgroups of the persistent / Stream-K launch;
+                         0 = number of CUs (issue #1393 uses the SM count) */
+    int32_t group_m;  /* tile-order group height (issue #1393 GROUP_M);
+                         0 = 8, < 0 = plain row-major tile order */
+    uint32_t flags;   /* GEMM_FLAG_* */
+} gemm_tiles;
+
+/* Device description for planning without touching a GPU (host tests). */
+typedef struct {
+    int32_t cus;       /* compute units, e.g. 256 on MI355X */
+    int32_t xcds;      /* dies that workgroups are dealt to in turn, e.g. 8 */
+    int32_t wg_per_cu; /* co-resident workgroups of the chosen kernel per CU;
+                          0 = 1 */
+} gemm_device_desc;
+
+typedef struct gemm_plan gemm_plan;
+
+/*
+ * Create a plan for C = A.B with the given shape, input dtype and schedule.
+ * tiles may be NULL (all defaults).  The device is the current HIP device.
+ * M, N, K >= 0 (M or N = 0: nothing to do; K = 0: C is zero-filled).
+ * Returns NULL on error (message in gemm_last_error()): negative sizes, a
+ * matrix too large for 32-bit indexing, an unknown dtype or schedule, an
+ * unsupported tile, or a Stream-K / hybrid grid larger than the number of
+ * workgroups that can be resident at once (the fixup waits on other
+ * workgroups, so all of them must be running together).
+ */
+gemm_plan *gemm_plan_create(int64_t M, int64_t N, int64_t K, gemm_dtype dtype,
+                            gemm_schedule schedule, const gemm_tiles *tiles);
+
+/* Same, for an explicit device description; needs no GPU.  A plan made this
+ * way can be inspected but gemm_run refuses it unless its description matches
+ * the current device. */
+gemm_plan *gemm_plan_create_for_device(int64_t M, int64_t N, int64_t K, gemm_dtype dtype,
+                                       gemm_schedule schedule, const gemm_tiles *tiles,
+                                       const gemm_device_desc *device);
+
+/*
+ * Enqueue C = A.B on stream (a hipStream_t; NULL = the default stream).
+ * Asynchronous: never allocates, never synchronizes.  workspace is a device
+ * buffer of at least gemm_plan_workspace_size(plan) bytes, zero-filled once
+ * when allocated; it may be NULL when that size is 0.  A run leaves the
+ * workspace's flags zero again, so it can be reused by later runs without
+ * clearing.  Two runs that overlap in time must not share a workspace.
+ * Returns 0, or -1 invalid argument (NULL or misaligned pointer), -2 workspace
+ * missing, -3 HIP launch error, -5 plan made for another device.
+ */
+int gemm_run(const gemm_plan *plan, const void *A, const void *B, float *C, void *workspace,
+             void *stream);
+
+/* Free a plan (NULL is ignored). */
+void gemm_plan_destroy(gemm_plan *plan);
+
+/* Bytes of workspace gemm_run needs (0 when none). */
+size_t gemm_plan_workspace_size(const gemm_plan *plan);
+
+/* Human-readable plan summary (tile grid, partition, launch) into buf;
+ * returns the length it needed (like snprintf), or -1 on a NULL plan. */
+int gemm_plan_describe(const gemm_plan *plan, char *buf, size_t len);
+
+/* Message of the last failed call on this host thread ("" if none). */
+const char *gemm_last_error(void);
+
+/* ---- introspection (host only; used by the tests and the benchmark) ---- */
+
+typedef struct {
+    int64_t M, N, K;
+    int32_t dtype, schedule;
+    int32_t bm, bn, bk, group_m;
+    uint32_t flags;
+    int32_t tiles_m, tiles_n;
+    int32_t tiles;        /* T */
+    int32_t iters_per_tile; /* ipt = ceil(K / bk) */
+    int32_t tiles_sk;     /* T_sk: tiles [0, T_sk) are split by Stream-K */
+    int32_t tiles_dp;     /* T - T_sk */
+    int64_t iters_sk;     /* T_sk * ipt */
+    int32_t q, r;         /* iters_sk = q * g + r */
+    int32_t g;            /* Stream-K / persistent workgroup count */
+    int32_t launch_grid;  /* workgroups launched */
+    int32_t threads;      /* threads per workgroup */
+    int32_t cus, xcds, wg_capacity;
+    int32_t pack_a, pack_b; /* operand repacked into the workspace */
+    size_t workspace;
+    size_t lds_bytes;
+} gemm_plan_info;
+
+int gemm_plan_get_info(const gemm_plan *plan, gemm_plan_info *out);
+
+enum { GEMM_ROLE_FULL = 0, GEMM_ROLE_CONTRIB = 1, GEMM_ROLE_OWNER = 2 };
+
+/* One unit of work of a workgroup: MAC iterations [k_begin, k_end) of a tile.
+ * FULL: the whole tile, stored to C.  CONTRIB: a tail of a split tile, stored
+ * to this workgroup's workspace slot.  OWNER: the head (k_begin = 0) of a split
+ * tile, finished with the partials of workgroups wg+1 .. peer_last. */
+typedef struct {
+    int32_t tile, k_begin, k_end, role, peer_last;
+} gemm_segment;
+
+/* The work of logical workgroup wg in execution order; returns the number of
+ * segments (may exceed max; only min(count, max) are written), or -1. */
+int gemm_plan_segments(const gemm_plan *plan, int32_t wg, gemm_segment *out, int32_t max);
+
+/* Output tile coordinates (tile row, tile column) of tile id t. */
+int gemm_plan_tile_coords(const gemm_plan *plan, int32_t t, int32_t *tile_m, int32_t *tile_n);
+
+/* Logical workgroup that hardware workgroup id hw runs (the XCD remap). */
+int32_t gemm_plan_logical_wg(const gemm_plan *plan, int32_t hw);
+
+/* Synchronously read the workspace status word written by the last run on
+ * stream: 0 = ok, 1 = a fixup wait gave up (the output is not valid and the
+ * workspace must be zero-filled again).  Returns 0 or a negative error. */
+int gemm_workspace_status(const gemm_plan *plan, const void *workspace, void *stream,
+                          int32_t *status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM_SK_H */

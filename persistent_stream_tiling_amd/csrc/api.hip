@@ -1,0 +1,504 @@
+// Host side of the C ABI: plan creation (tile grid, schedule partition,
+// workspace layout), introspection and the launch path.
+#include <hip/hip_runtime.h>
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <atomic>
+#include <new>
+#include <string>
+
+#include "gemm_sk.h"
+#include "kernels.h"
+#include "schedule.h"
+
+using namespace gsk;
+
+struct gemm_plan {
+    int64_t M, N, K;
+    int dtype, schedule;
+    int bm, bn, bk, group_m;
+    uint32_t flags;
+    const Variant *variant;
+    Partition P;
+    int64_t iters_sk;
+    int cus, xcds, wg_capacity;
+    int device;                // HIP device ordinal, -1 for a described device
+    int pack_a, pack_b;
+    int64_t lda, ldb;          // leading dimensions the kernel reads (packed or not)
+    size_t off_flags, off_partials, off_pack_a, off_pack_b, ws_size;
+    int32_t spin_limit;
+};
+
+namespace {
+
+thread_local std::string g_error;
+
+void set_error(const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_error = buf;
+}
+
+int elem_size(int dtype) { return dtype == GEMM_F32 ? 4 : 2; }
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+const Variant *find_variant(int dtype, int bm, int bn)
+{
+    int n = 0;
+    const Variant *v = variants(&n);
+    for (int i = 0; i < n; ++i)
+        if (v[i].dtype == dtype && v[i].bm == bm && v[i].bn == bn)
+            return &v[i];
+    return nullptr;
+}
+
+// Polls before a fixup wait gives up.  A poll is a sleep of ~128 cycles plus a
+// memory round trip, so this is about a second: orders of magnitude beyond a
+// real wait (one workgroup's Stream-K share, milliseconds at most), and it
+// turns a lost signal into an error instead of a hung GPU.
+constexpr int32_t kSpinLimit = 1 << 21;
+
+constexpr int kDiesPerGfx950 = 8;
+
+gemm_plan *create(int64_t M, int64_t N, int64_t K, gemm_dtype dtype, gemm_schedule schedule,
+                  const gemm_tiles *tiles_in, const gemm_device_desc &dev, int device,
+                  bool query_occupancy)
+{
+    if (M < 0 || N < 0 || K < 0) {
+        set_error("negative size M=%lld N=%lld K=%lld", (long long)M, (long long)N, (long long)K);
+        return nullptr;
+    }
+    if (dtype != GEMM_F32 && dtype != GEMM_F16 && dtype != GEMM_BF16) {
+        set_error("unknown dtype %d", (int)dtype);
+        return nullptr;
+    }
+    if (schedule < GEMM_DP || schedule > GEMM_HYBRID) {
+        set_error("unknown schedule %d", (int)schedule);
+        return nullptr;
+    }
+    if (dev.cus < 1 || dev.xcds < 1 || dev.wg_per_cu < 0) {
+        set_error("bad device description cus=%d xcds=%d wg_per_cu=%d", dev.cus, dev.xcds,
+                  dev.wg_per_cu);
+        return nullptr;
+    }
+    gemm_tiles t = {};
+    if (tiles_in)
+        t = *tiles_in;
+    const int E = elem_size(dtype);
+    if (t.bm == 0 && t.bn == 0) {
+        if (dtype == GEMM_F32) {
+            t.bm = t.bn = (M * N <= 512 * 512) ? 64 : 128;
+        } else {
+            t.bm = t.bn = 256;
+        }
+    } else if (t.bm == 0 || t.bn == 0) {
+        set_error("give both bm and bn, or neither");
+        return nullptr;
+    }
+    const Variant *var = find_variant(dtype, t.bm, t.bn);
+    if (!var) {
+        set_error("no kernel for dtype %d with a %dx%d tile", (int)dtype, t.bm, t.bn);
+        return nullptr;
+    }
+    if (t.bk != 0 && t.bk != var->bk) {
+        set_error("bk must be %d for this dtype (128 bytes of input per row)", var->bk);
+        return nullptr;
+    }
+    if (t.grid < 0) {
+        set_error("grid must be >= 0");
+        return nullptr;
+    }
+    const int V = 16 / E;
+    const int64_t lda = (K * E) % 16 ? cdiv(K, V) * V : K;
+    const int64_t ldb = (N * E) % 16 ? cdiv(N, V) * V : N;
+    // 32-bit index limits of the kernel: sizes, per-slab buffer offsets, tiles.
+    const int64_t lim = (int64_t)1 << 30;
+    if (M >= lim || N >= lim || K >= lim || (int64_t)var->bm * lda * E >= lim ||
+        (int64_t)var->bk * ldb * E >= lim) {
+        set_error("matrix too large for 32-bit indexing");
+        return nullptr;
+    }
+
+    gemm_plan *p = new (std::nothrow) gemm_plan();
+    if (!p) {
+        set_error("out of host memory");
+        return nullptr;
+    }
+    p->M = M;
+    p->N = N;
+    p->K = K;
+    p->dtype = dtype;
+    p->schedule = schedule;
+    p->bm = var->bm;
+    p->bn = var->bn;
+    p->bk = var->bk;
+    p->group_m = t.group_m == 0 ? 8 : (t.group_m < 0 ? 0 : t.group_m);
+    p->flags = t.flags;
+    p->variant = var;
+    p->cus = dev.cus;
+    p->xcds = (t.flags & GEMM_FLAG_NO_XCD_REMAP) ? 1 : dev.xcds;
+    p->device = device;
+    p->spin_limit = kSpinLimit;
+
+    int occ = dev.wg_per_cu > 0 ? dev.wg_per_cu : 1;
+    if (query_occupancy) {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, var->kernel, var->threads, 0) ==
+                hipSuccess &&
+            n > 0)
+            occ = n;
+    }
+    p->wg_capacity = dev.cus * occ;
+
+    Partition &P = p->P;
+    P.tiles_m = (int32_t)cdiv(M, var->bm);
+    P.tiles_n = (int32_t)cdiv(N, var->bn);
+    const int64_t T = (int64_t)P.tiles_m * P.tiles_n;
+    const int64_t ipt = cdiv(K, var->bk);
+    if (T >= lim || T * ipt >= ((int64_t)1 << 31)) {
+        set_error("too many tiles or MAC iterations for 32-bit indexing");
+        delete p;
+        return nullptr;
+    }
+    P.T = (int32_t)T;
+    P.ipt = (int32_t)ipt;
+    P.group_m = p->group_m;
+    P.xcds = p->xcds;
+    const int32_t g = t.grid > 0 ? t.grid : dev.cus;
+    int64_t T_sk = 0;
+    switch (schedule) {
+    case GEMM_DP:
+        P.g = 0;
+        P.grid = (int32_t)T;
+        break;
+    case GEMM_PERSISTENT:
+        P.g = g;
+        P.grid = (int32_t)(T < g ? T : g);
+        break;
+    case GEMM_STREAMK:
+        T_sk = T;
+        P.g = g;
+        P.grid = g;
+        break;
+    case GEMM_HYBRID:
+        // Issue #1393, final revision: the last (partial) wave goes to Stream-K,
+        // plus one more full wave when two_tiles is on and more than g tiles
+        // would stay data-parallel.
+        T_sk = T % g;
+        if (!(t.flags & GEMM_FLAG_ONE_TILE) && T - T_sk > g)
+            T_sk += g;
+        P.g = g;
+        P.grid = T_sk > 0 ? g : (int32_t)(T < g ? T : g);
+        break;
+    }
+    if (ipt == 0 || T == 0)
+        T_sk = 0;  // nothing to split: K = 0 is a fill, an empty C is a no-op
+    P.T_sk = (int32_t)T_sk;
+    p->iters_sk = T_sk * ipt;
+    if (T_sk > 0) {
+        P.q = (int32_t)(p->iters_sk / g);
+        P.r = (int32_t)(p->iters_sk % g);
+        if (g > p->wg_capacity) {
+            set_error("Stream-K grid %d exceeds the %d workgroups that can be resident at once; "
+                      "the fixup needs them all running together",
+                      g, p->wg_capacity);
+            delete p;
+            return nullptr;
+        }
+    } else {
+        P.q = P.r = 0;
+    }
+
+    // Workspace: [status word | flags (g) | partial tiles (g slots) | packed A | packed B]
+    p->pack_a = lda != K && M > 0 && K > 0;
+    p->pack_b = ldb != N && N > 0 && K > 0;
+    p->lda = lda;
+    p->ldb = ldb;
+    size_t off = 0;
+    if (T_sk > 0) {
+        off = 256;
+        p->off_flags = off;
+        off = align_up(off + sizeof(int32_t) * (size_t)g, 256);
+        p->off_partials = off;
+        off += sizeof(float) * (size_t)g * var->bm * var->bn;
+    }
+    if (p->pack_a) {
+        off = align_up(off, 256);
+        p->off_pack_a = off;
+        off += (size_t)M * lda * E;
+    }
+    if (p->pack_b) {
+        off = align_up(off, 256);
+        p->off_pack_b = off;
+        off += (size_t)K * ldb * E;
+    }
+    p->ws_size = off ? align_up(off, 256) : 0;
+    return p;
+}
+
+const char *sched_name(int s)
+{
+    static const char *names[] = {"dp", "persistent", "streamk", "hybrid"};
+    return (s >= 0 && s < 4) ? names[s] : "?";
+}
+
+const char *dtype_name(int d)
+{
+    static const char *names[] = {"f32", "f16", "bf16"};
+    return (d >= 0 && d < 3) ? names[d] : "?";
+}
+
+}  // namespace
+
+extern "C" {
+
+gemm_plan *gemm_plan_create(int64_t M, int64_t N, int64_t K, gemm_dtype dtype,
+                            gemm_schedule schedule, const gemm_tiles *tiles)
+{
+    int device = 0;
+    if (hipGetDevice(&device) != hipSuccess) {
+        set_error("no HIP device");
+        return nullptr;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) !=
+            hipSuccess ||
+        cus < 1) {
+        set_error("cannot query the compute-unit count of device %d", device);
+        return nullptr;
+    }
+    gemm_device_desc dev = {cus, kDiesPerGfx950, 0};
+    return create(M, N, K, dtype, schedule, tiles, dev, device, true);
+}
+
+gemm_plan *gemm_plan_create_for_device(int64_t M, int64_t N, int64_t K, gemm_dtype dtype,
+                                       gemm_schedule schedule, const gemm_tiles *tiles,
+                                       const gemm_device_desc *device)
+{
+    if (!device) {
+        set_error("device description is NULL");
+        return nullptr;
+    }
+    return create(M, N, K, dtype, schedule, tiles, *device, -1, false);
+}
+
+void gemm_plan_destroy(gemm_plan *plan) { delete plan; }
+
+size_t gemm_plan_workspace_size(const gemm_plan *plan) { return plan ? plan->ws_size : 0; }
+
+const char *gemm_last_error(void) { return g_error.c_str(); }
+
+int gemm_plan_get_info(const gemm_plan *p, gemm_plan_info *o)
+{
+    if (!p || !o) {
+        set_error("NULL argument");
+        return -1;
+    }
+    memset(o, 0, sizeof *o);
+    o->M = p->M;
+    o->N = p->N;
+    o->K = p->K;
+    o->dtype = p->dtype;
+    o->schedule = p->schedule;
+    o->bm = p->bm;
+    o->bn = p->bn;
+    o->bk = p->bk;
+    o->group_m = p->group_m;
+    o->flags = p->flags;
+    o->tiles_m = p->P.tiles_m;
+    o->tiles_n = p->P.tiles_n;
+    o->tiles = p->P.T;
+    o->iters_per_tile = p->P.ipt;
+    o->tiles_sk = p->P.T_sk;
+    o->tiles_dp = p->P.T - p->P.T_sk;
+    o->iters_sk = p->iters_sk;
+    o->q = p->P.q;
+    o->r = p->P.r;
+    o->g = p->P.g;
+    o->launch_grid = p->P.grid;
+    o->threads = p->variant->threads;
+    o->cus = p->cus;
+    o->xcds = p->xcds;
+    o->wg_capacity = p->wg_capacity;
+    o->pack_a = p->pack_a;
+    o->pack_b = p->pack_b;
+    o->workspace = p->ws_size;
+    o->lds_bytes = p->variant->lds_bytes;
+    return 0;
+}
+
+int gemm_plan_describe(const gemm_plan *p, char *buf, size_t len)
+{
+    if (!p) {
+        set_error("NULL plan");
+        return -1;
+    }
+    return snprintf(buf, buf ? len : 0,
+                    "M,N,K=%lld,%lld,%lld %s %s tile=%dx%dx%d group_m=%d | tiles %dx%d=%d "
+                    "ipt=%d | T_sk=%d T_dp=%d I_sk=%lld g=%d q=%d r=%d | grid=%d x %d threads, "
+                    "lds=%zu B, capacity=%d wg, xcds=%d | pack A=%d B=%d | workspace=%zu B",
+                    (long long)p->M, (long long)p->N, (long long)p->K, dtype_name(p->dtype),
+                    sched_name(p->schedule), p->bm, p->bn, p->bk, p->group_m, p->P.tiles_m,
+                    p->P.tiles_n, p->P.T, p->P.ipt, p->P.T_sk, p->P.T - p->P.T_sk,
+                    (long long)p->iters_sk, p->P.g, p->P.q, p->P.r, p->P.grid,
+                    p->variant->threads, p->variant->lds_bytes, p->wg_capacity, p->xcds,
+                    p->pack_a, p->pack_b, p->ws_size);
+}
+
+int gemm_plan_segments(const gemm_plan *p, int32_t wg, gemm_segment *out, int32_t max)
+{
+    if (!p || wg < 0 || wg >= (p->P.grid > 0 ? p->P.grid : 1) || (max > 0 && !out)) {
+        set_error("bad argument");
+        return -1;
+    }
+    if (p->P.T == 0 || p->P.ipt == 0)
+        return 0;
+    WorkCursor c = work_begin(p->P, wg);
+    WorkItem w;
+    int n = 0;
+    while (work_next(p->P, wg, c, w)) {
+        if (n < max)
+            out[n] = gemm_segment{w.tile, w.kb, w.ke, w.role, w.peer_last};
+        ++n;
+    }
+    return n;
+}
+
+int gemm_plan_tile_coords(const gemm_plan *p, int32_t t, int32_t *tm, int32_t *tn)
+{
+    if (!p || t < 0 || t >= p->P.T || !tm || !tn) {
+        set_error("bad argument");
+        return -1;
+    }
+    tile_coords(p->P, t, tm, tn);
+    return 0;
+}
+
+int32_t gemm_plan_logical_wg(const gemm_plan *p, int32_t hw)
+{
+    if (!p || hw < 0 || hw >= p->P.grid) {
+        set_error("bad argument");
+        return -1;
+    }
+    return logical_wg(hw, p->P.grid, p->P.xcds);
+}
+
+int gemm_run(const gemm_plan *p, const void *A, const void *B, float *C, void *workspace,
+             void *stream_v)
+{
+    if (!p) {
+        set_error("NULL plan");
+        return -1;
+    }
+    hipStream_t stream = (hipStream_t)stream_v;
+    if (p->M == 0 || p->N == 0)
+        return 0;
+    if (!C) {
+        set_error("C is NULL");
+        return -1;
+    }
+    if (p->device < 0) {
+        set_error("plan was made for a described device; create it with gemm_plan_create");
+        return -5;
+    }
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess || cur != p->device) {
+        set_error("plan was made for device %d, current device is %d", p->device, cur);
+        return -5;
+    }
+    if (p->K == 0) {
+        if (launch_zero(C, p->M * p->N, stream)) {
+            set_error("zero-fill launch failed: %s", hipGetErrorString(hipGetLastError()));
+            return -3;
+        }
+        return 0;
+    }
+    if (!A || !B) {
+        set_error("A or B is NULL");
+        return -1;
+    }
+    if (p->ws_size && !workspace) {
+        set_error("this plan needs %zu bytes of workspace", p->ws_size);
+        return -2;
+    }
+    if (((uintptr_t)A & 15) || ((uintptr_t)B & 15) || ((uintptr_t)C & 3) ||
+        ((uintptr_t)workspace & 255)) {
+        set_error("A and B must be 16-byte aligned, C 4-byte aligned, workspace 256-byte aligned");
+        return -1;
+    }
+    const int E = elem_size(p->dtype);
+    uint8_t *ws = (uint8_t *)workspace;
+    const uint8_t *a = (const uint8_t *)A;
+    const uint8_t *b = (const uint8_t *)B;
+    if (p->pack_a) {
+        if (launch_pack(A, ws + p->off_pack_a, p->M, p->K, p->K, p->lda, E, stream)) {
+            set_error("pack launch failed");
+            return -3;
+        }
+        a = ws + p->off_pack_a;
+    }
+    if (p->pack_b) {
+        if (launch_pack(B, ws + p->off_pack_b, p->K, p->N, p->N, p->ldb, E, stream)) {
+            set_error("pack launch failed");
+            return -3;
+        }
+        b = ws + p->off_pack_b;
+    }
+    KernelArgs args;
+    args.A = a;
+    args.B = b;
+    args.C = C;
+    args.status = p->P.T_sk > 0 ? (int32_t *)ws : nullptr;
+    args.flags = p->P.T_sk > 0 ? (int32_t *)(ws + p->off_flags) : nullptr;
+    args.partials = p->P.T_sk > 0 ? (float *)(ws + p->off_partials) : nullptr;
+    args.M = (int32_t)p->M;
+    args.N = (int32_t)p->N;
+    args.K = (int32_t)p->K;
+    args.lda = (int32_t)p->lda;
+    args.ldb = (int32_t)p->ldb;
+    args.ldc = (int32_t)p->N;
+    args.c_vec = (p->N % 4 == 0) && (((uintptr_t)C & 15) == 0);
+    args.spin_limit = p->spin_limit;
+    args.P = p->P;
+    if (p->variant->launch(args, p->P.grid, stream)) {
+        set_error("kernel launch failed: %s", hipGetErrorString(hipGetLastError()));
+        return -3;
+    }
+    return 0;
+}
+
+int gemm_workspace_status(const gemm_plan *p, const void *workspace, void *stream,
+                          int32_t *status)
+{
+    if (!p || !status) {
+        set_error("NULL argument");
+        return -1;
+    }
+    *status = 0;
+    if (p->P.T_sk == 0)
+        return 0;
+    if (!workspace) {
+        set_error("NULL workspace");
+        return -2;
+    }
+    hipStream_t s = (hipStream_t)stream;
+    if (hipMemcpyAsync(status, workspace, sizeof(int32_t), hipMemcpyDeviceToHost, s) !=
+            hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess) {
+        set_error("status read failed: %s", hipGetErrorString(hipGetLastError()));
+        return -3;
+    }
+    return 0;
+}
+
+}  // extern "C"

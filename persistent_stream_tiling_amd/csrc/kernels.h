@@ -1,0 +1,50 @@
+// Internal interface between the host API (api.hip) and the gfx950 kernels
+// (kernels.hip).  Not part of the public C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "schedule.h"
+
+namespace gsk {
+
+// Everything one GEMM launch needs, passed by value as the kernel argument.
+struct KernelArgs {
+    const uint8_t *A;      // M x lda elements, row-major, 16-byte aligned rows
+    const uint8_t *B;      // K x ldb elements, row-major, 16-byte aligned rows
+    float *C;              // M x ldc floats
+    float *partials;       // Stream-K partial tiles: one bm*bn slot per workgroup
+    int32_t *flags;        // one "partial ready" flag per workgroup (0 between runs)
+    int32_t *status;       // workspace status word (1 = a fixup wait gave up)
+    int32_t M, N, K;
+    int32_t lda, ldb, ldc; // leading dimensions in elements
+    int32_t c_vec;         // 1: C rows allow 16-byte stores
+    int32_t spin_limit;    // polls before a fixup wait gives up
+    Partition P;
+};
+
+// One compiled GEMM kernel: input dtype and workgroup tile.
+struct Variant {
+    int dtype;             // gemm_dtype
+    int bm, bn, bk;
+    int threads;
+    size_t lds_bytes;
+    int (*launch)(const KernelArgs &args, int grid, hipStream_t stream);
+    const void *kernel;    // for occupancy queries
+};
+
+// All compiled variants; *count receives the number of entries.
+const Variant *variants(int *count);
+
+// Copy a rows x cols matrix of elem_size-byte elements with leading
+// dimension ld_src into a dense rows x ld_dst buffer (ld_dst >= cols, a
+// multiple of 16 bytes), zero-filling columns [cols, ld_dst).
+int launch_pack(const void *src, void *dst, int64_t rows, int64_t cols, int64_t ld_src,
+                int64_t ld_dst, int elem_size, hipStream_t stream);
+
+// C[0 .. count) = 0 (the K = 0 product).
+int launch_zero(float *C, int64_t count, hipStream_t stream);
+
+}  // namespace gsk

@@ -1,0 +1,164 @@
+// Work decomposition shared by the host planner and the gfx950 kernel.
+//
+// Everything here is integer arithmetic on tile and iteration indices.  The
+// same inline functions run on the host (planning, introspection, the
+// coverage tests) and inside the kernel, so what the tests check is what the
+// GPU executes.
+//
+// Vocabulary (Triton issue #1393 "Stream-k matmul implementation very
+// slow...", final revision):
+//   T      output tiles, tiles_m * tiles_n
+//   ipt    MAC iterations per tile, ceil(K / bk)
+//   g      workgroups of the Stream-K / persistent launch
+//   T_sk   tiles [0, T_sk) whose iterations are spread over the g workgroups
+//   q, r   T_sk * ipt = q * g + r; workgroup p owns iterations
+//          [p*q + min(p, r), (p+1)*q + min(p+1, r))
+#pragma once
+
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#define GSK_HD __host__ __device__ __forceinline__
+#else
+#define GSK_HD inline
+#endif
+
+namespace gsk {
+
+struct Partition {
+    int32_t tiles_m, tiles_n;
+    int32_t T;        // output tiles
+    int32_t ipt;      // MAC iterations per tile
+    int32_t T_sk;     // tiles split by Stream-K (a prefix of the tile ids)
+    int32_t g;        // Stream-K workgroups
+    int32_t q, r;     // T_sk * ipt = q * g + r
+    int32_t grid;     // launched workgroups (also the data-parallel tile stride)
+    int32_t group_m;  // tile-order group height; <= 0 means row-major order
+    int32_t xcds;     // dies that hardware workgroup ids are dealt to in turn
+};
+
+GSK_HD int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
+
+// First Stream-K iteration of workgroup p (p may equal g: the end of the
+// last range).  Ranges are contiguous, ascending in p, and differ in length
+// by at most one (issue #1393, the first-wave kernel's start/last iteration).
+GSK_HD int64_t sk_begin(const Partition &P, int64_t p)
+{
+    return p * P.q + min64(p, P.r);
+}
+
+// The workgroup whose Stream-K range holds global iteration it
+// (0 <= it < T_sk * ipt): the inverse of sk_begin.
+GSK_HD int32_t sk_wg_of_iter(const Partition &P, int64_t it)
+{
+    int64_t long_part = (int64_t)P.r * (P.q + 1);  // the r ranges of length q+1
+    if (it < long_part)
+        return (int32_t)(it / (P.q + 1));
+    return (int32_t)(P.r + (it - long_part) / P.q);  // q > 0 whenever this is reached
+}
+
+// Output tile (tile_m, tile_n) of tile id t.  With group_m > 0 the ids walk
+// down a band of group_m tile rows before moving one tile column right, so
+// tiles that run at the same time share A row panels and B column panels in
+// cache (issue #1393's GROUP_M re-ordering "for better L2 performance").
+GSK_HD void tile_coords(const Partition &P, int32_t t, int32_t *tm, int32_t *tn)
+{
+    if (P.group_m <= 0) {
+        *tm = t / P.tiles_n;
+        *tn = t - (t / P.tiles_n) * P.tiles_n;
+        return;
+    }
+    int32_t band = P.group_m * P.tiles_n;        // tiles per band of group_m rows
+    int32_t b = t / band;
+    int32_t first_row = b * P.group_m;
+    int32_t rows = P.tiles_m - first_row;        // the last band may be shorter
+    if (rows > P.group_m)
+        rows = P.group_m;
+    int32_t in_band = t - b * band;
+    *tm = first_row + in_band % rows;
+    *tn = in_band / rows;
+}
+
+// Logical workgroup run by hardware workgroup id hw.  The dispatcher deals
+// consecutive hardware ids to the xcds dies in turn (id mod xcds), and each
+// die has its own L2.  The remap hands die x a contiguous block of logical
+// ids instead, so neighbouring tiles (which share operand panels) run on the
+// same die.  It is a bijection on [0, grid).
+GSK_HD int32_t logical_wg(int32_t hw, int32_t grid, int32_t xcds)
+{
+    if (xcds <= 1)
+        return hw;
+    int32_t die = hw % xcds;
+    int32_t slot = hw / xcds;
+    int32_t per_die = grid / xcds;
+    int32_t extra = grid - per_die * xcds;       // the first `extra` dies get one more
+    return die * per_die + (die < extra ? die : extra) + slot;
+}
+
+enum Role { ROLE_FULL = 0, ROLE_CONTRIB = 1, ROLE_OWNER = 2 };
+
+struct WorkItem {
+    int32_t tile;       // tile id
+    int32_t kb, ke;     // MAC iterations [kb, ke) of the tile
+    int32_t role;       // Role
+    int32_t peer_last;  // OWNER: last workgroup holding a partial of this tile
+};
+
+struct WorkCursor {
+    int64_t it, end;    // Stream-K iterations still to walk
+    int32_t dp_tile;    // next data-parallel tile
+};
+
+GSK_HD WorkCursor work_begin(const Partition &P, int32_t p)
+{
+    WorkCursor c;
+    if (P.T_sk > 0 && p < P.g) {
+        c.it = sk_begin(P, p);
+        c.end = sk_begin(P, p + 1);
+    } else {
+        c.it = c.end = 0;
+    }
+    c.dp_tile = P.T_sk + p;
+    return c;
+}
+
+// Next unit of work of workgroup p.  The Stream-K range is cut at tile
+// boundaries (issue #1393, the final revision's while loop over
+// [start_iter, last_iter)); then the data-parallel tiles T_sk + p,
+// T_sk + p + grid, ... follow.  Only the first Stream-K segment can start
+// inside a tile (CONTRIB) and only the last can stop inside one (OWNER).
+GSK_HD bool work_next(const Partition &P, int32_t p, WorkCursor &c, WorkItem &w)
+{
+    if (c.it < c.end) {
+        int32_t tile = (int32_t)(c.it / P.ipt);
+        int32_t kb = (int32_t)(c.it - (int64_t)tile * P.ipt);
+        int64_t left = c.end - c.it;
+        int32_t ke = (P.ipt - kb <= left) ? P.ipt : kb + (int32_t)left;
+        w.tile = tile;
+        w.kb = kb;
+        w.ke = ke;
+        w.peer_last = p;
+        if (kb != 0) {
+            w.role = ROLE_CONTRIB;
+        } else if (ke == P.ipt) {
+            w.role = ROLE_FULL;
+        } else {
+            w.role = ROLE_OWNER;
+            w.peer_last = sk_wg_of_iter(P, (int64_t)tile * P.ipt + P.ipt - 1);
+        }
+        c.it += ke - kb;
+        return true;
+    }
+    if (c.dp_tile < P.T) {
+        w.tile = c.dp_tile;
+        w.kb = 0;
+        w.ke = P.ipt;
+        w.role = ROLE_FULL;
+        w.peer_last = p;
+        c.dp_tile += P.grid;
+        return true;
+    }
+    return false;
+}
+
+}  // namespace gsk

@@ -12,9 +12,30 @@ with round-to-nearest-even:
 Every generator returns raw bit patterns (``uint32`` for fp32, ``uint16`` for
 fp16/bf16) so the GPU and the oracle read identical bits.
 """
+import os
 import random
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
+
+# Values are drawn in fixed chunks of this many elements, chunk i from its own
+# PCG64 stream seeded with (seed, i), so they do not depend on the thread count.
+CHUNK = 1 << 22
+
+
+def _threads():
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _chunked(n, fn):
+    """Run fn(i, lo, hi) over the fixed chunks of [0, n) on a thread pool."""
+    spans = [(i, lo, min(lo + CHUNK, n)) for i, lo in enumerate(range(0, n, CHUNK))]
+    if len(spans) <= 1:
+        for sp in spans:
+            fn(*sp)
+        return
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(lambda sp: fn(*sp), spans))
 
 DTYPE_BITS = {"f32": np.uint32, "f16": np.uint16, "bf16": np.uint16}
 ELEM_SIZE = {"f32": 4, "f16": 2, "bf16": 2}
@@ -22,13 +43,29 @@ ELEM_SIZE = {"f32": 4, "f16": 2, "bf16": 2}
 
 def f32_to_bf16_bits(x):
     """Round float32 values to bfloat16 (nearest, ties to even); NaN stays NaN."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    out = rounded.astype(np.uint16)
-    nan = np.isnan(np.asarray(x, dtype=np.float32))
-    if nan.any():
-        out[nan] = ((u[nan] >> 16) | 0x40).astype(np.uint16)
-    return out
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    shape = x.shape
+    u = x.reshape(-1).view(np.uint32)
+    out = np.empty(u.size, dtype=np.uint16)
+
+    def one(_, lo, hi):
+        uc = u[lo:hi]
+        nan = np.isnan(uc.view(np.float32))
+        t = uc >> 16
+        t &= 1
+        t += 0x7FFF
+        if nan.any():
+            t += np.where(nan, np.uint32(0), uc)
+        else:
+            t += uc  # never wraps: non-NaN patterns are at most 0xff800000
+        t >>= 16
+        o = t.astype(np.uint16)
+        if nan.any():
+            o[nan] = ((uc[nan] >> 16) | 0x40).astype(np.uint16)
+        out[lo:hi] = o
+
+    _chunked(u.size, one)
+    return out.reshape(shape)
 
 
 def to_bits(x32, dtype):
@@ -45,18 +82,27 @@ def to_bits(x32, dtype):
 
 def draw(shape, dist, seed, scale=1.0):
     """float32 samples: 'normal' = N(0,1), 'uniform' = U[-1,1), 'int4' = integers in [-4,4]."""
-    rng = np.random.Generator(np.random.PCG64(seed))
-    if dist == "normal":
-        x = rng.standard_normal(shape, dtype=np.float32)
-    elif dist == "uniform":
-        x = (2.0 * rng.random(shape, dtype=np.float32) - 1.0)
-    elif dist == "int4":
-        x = rng.integers(-4, 5, size=shape).astype(np.float32)
-    else:
+    if dist not in ("normal", "uniform", "int4"):
         raise ValueError(f"unknown distribution {dist!r}")
-    if scale != 1.0:
-        x = x * np.float32(scale)
-    return np.ascontiguousarray(x, dtype=np.float32)
+    x = np.empty(shape, dtype=np.float32)
+    flat = x.reshape(-1)
+
+    def one(i, lo, hi):
+        rng = np.random.Generator(np.random.PCG64([seed, i]))
+        part = flat[lo:hi]
+        if dist == "normal":
+            rng.standard_normal(out=part, dtype=np.float32)
+        elif dist == "uniform":
+            rng.random(out=part, dtype=np.float32)
+            part *= np.float32(2.0)
+            part -= np.float32(1.0)
+        else:
+            part[:] = rng.integers(-4, 5, size=hi - lo)
+        if scale != 1.0:
+            part *= np.float32(scale)
+
+    _chunked(flat.size, one)
+    return x
 
 
 def operands(M, N, K, dtype, dist, seed, scale=1.0):

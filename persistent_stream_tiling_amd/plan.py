@@ -1,0 +1,169 @@
+"""Plan objects and the ``matmul`` convenience call (argument marshalling only)."""
+import ctypes
+
+from ._lib import DTYPES, SCHEDULES, DeviceDesc, PlanInfo, Segment, Tiles, last_error, load
+
+_TORCH_DTYPES = None
+
+
+def _torch_dtypes():
+    global _TORCH_DTYPES
+    if _TORCH_DTYPES is None:
+        import torch
+        _TORCH_DTYPES = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}
+    return _TORCH_DTYPES
+
+
+def _code(table, key, what):
+    if isinstance(key, int):
+        return key
+    try:
+        return table[key]
+    except KeyError:
+        raise ValueError(f"unknown {what} {key!r}; expected one of {sorted(table)}") from None
+
+
+class GemmPlan:
+    """A plan for C = A.B (M x K times K x N, fp32 C) under one schedule.
+
+    ``schedule`` is "dp", "persistent", "streamk" or "hybrid"; ``dtype`` is
+    "f32", "f16" or "bf16".  Tile knobs default to the library's choice.
+    With ``device`` = (cus, xcds, wg_per_cu) the plan is made for a described
+    device without touching a GPU (inspection only).
+    """
+
+    def __init__(self, M, N, K, dtype, schedule="hybrid", bm=0, bn=0, bk=0, grid=0, group_m=0,
+                 flags=0, device=None):
+        self._lib = load()
+        self._h = None
+        tiles = Tiles(bm, bn, bk, grid, group_m, flags)
+        d = _code(DTYPES, dtype, "dtype")
+        s = _code(SCHEDULES, schedule, "schedule")
+        if device is not None:
+            desc = DeviceDesc(*device)
+            h = self._lib.gemm_plan_create_for_device(M, N, K, d, s, ctypes.byref(tiles),
+                                                      ctypes.byref(desc))
+        else:
+            h = self._lib.gemm_plan_create(M, N, K, d, s, ctypes.byref(tiles))
+        if not h:
+            raise ValueError(f"gemm_plan_create failed: {last_error()}")
+        self._h = h
+        info = PlanInfo()
+        if self._lib.gemm_plan_get_info(h, ctypes.byref(info)) != 0:
+            raise RuntimeError(last_error())
+        self.info = info.as_dict()
+        self.M, self.N, self.K = M, N, K
+        self.dtype = dtype if isinstance(dtype, str) else {v: k for k, v in DTYPES.items()}[d]
+        self.schedule = schedule
+        self.workspace_bytes = int(self._lib.gemm_plan_workspace_size(h))
+
+    # -- introspection --------------------------------------------------
+    def describe(self):
+        n = self._lib.gemm_plan_describe(self._h, None, 0)
+        buf = ctypes.create_string_buffer(n + 1)
+        self._lib.gemm_plan_describe(self._h, buf, n + 1)
+        return buf.value.decode()
+
+    def segments(self, wg):
+        """[(tile, k_begin, k_end, role, peer_last), ...] of logical workgroup wg."""
+        n = self._lib.gemm_plan_segments(self._h, wg, None, 0)
+        if n < 0:
+            raise ValueError(last_error())
+        arr = (Segment * max(n, 1))()
+        self._lib.gemm_plan_segments(self._h, wg, arr, n)
+        return [(s.tile, s.k_begin, s.k_end, s.role, s.peer_last) for s in arr[:n]]
+
+    def tile_coords(self, t):
+        tm, tn = ctypes.c_int32(), ctypes.c_int32()
+        if self._lib.gemm_plan_tile_coords(self._h, t, ctypes.byref(tm), ctypes.byref(tn)):
+            raise ValueError(last_error())
+        return tm.value, tn.value
+
+    def logical_wg(self, hw):
+        v = self._lib.gemm_plan_logical_wg(self._h, hw)
+        if v < 0:
+            raise ValueError(last_error())
+        return v
+
+    # -- execution ------------------------------------------------------
+    def new_workspace(self, device=None):
+        """A zero-filled workspace tensor (None when the plan needs none)."""
+        if self.workspace_bytes == 0:
+            return None
+        import torch
+        return torch.zeros(self.workspace_bytes, dtype=torch.uint8,
+                           device=device or torch.device("cuda"))
+
+    def run(self, A, B, C, workspace=None, stream=None):
+        """Enqueue C = A.B on ``stream`` (default: torch's current stream).
+
+        A, B, C and workspace are torch tensors (or raw device addresses)."""
+        import torch
+
+        def ptr(x):
+            if x is None:
+                return None
+            return x.data_ptr() if isinstance(x, torch.Tensor) else int(x)
+
+        if stream is None:
+            stream = torch.cuda.current_stream().cuda_stream
+        elif isinstance(stream, torch.cuda.Stream):
+            stream = stream.cuda_stream
+        rc = self._lib.gemm_run(self._h, ptr(A), ptr(B), ptr(C), ptr(workspace), stream)
+        if rc != 0:
+            raise RuntimeError(f"gemm_run failed ({rc}): {last_error()}")
+
+    def workspace_status(self, workspace, stream=None):
+        import torch
+        if stream is None:
+            stream = torch.cuda.current_stream().cuda_stream
+        st = ctypes.c_int32()
+        ws = workspace.data_ptr() if workspace is not None else None
+        rc = self._lib.gemm_workspace_status(self._h, ws, stream, ctypes.byref(st))
+        if rc:
+            raise RuntimeError(last_error())
+        return st.value
+
+    def close(self):
+        if self._h:
+            self._lib.gemm_plan_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def plan_for_device(M, N, K, dtype, schedule, cus=256, xcds=8, wg_per_cu=1, **tiles):
+    """A plan for a described device (no GPU needed); for inspecting schedules."""
+    return GemmPlan(M, N, K, dtype, schedule, device=(cus, xcds, wg_per_cu), **tiles)
+
+
+_PLANS = {}
+
+
+def matmul(a, b, schedule="hybrid", **tiles):
+    """C = a @ b (fp32) for contiguous CUDA tensors a (M x K) and b (K x N) of
+    float32, float16 or bfloat16, through the library's kernels."""
+    import torch
+    if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[0]:
+        raise ValueError(f"incompatible shapes {tuple(a.shape)} and {tuple(b.shape)}")
+    if a.dtype != b.dtype or a.dtype not in _torch_dtypes():
+        raise ValueError(f"unsupported dtypes {a.dtype}, {b.dtype}")
+    if not (a.is_cuda and b.is_cuda):
+        raise ValueError("a and b must be on the GPU")
+    a, b = a.contiguous(), b.contiguous()
+    M, K = a.shape
+    N = b.shape[1]
+    key = (M, N, K, a.dtype, schedule, tuple(sorted(tiles.items())), a.device.index)
+    entry = _PLANS.get(key)
+    if entry is None:
+        plan = GemmPlan(M, N, K, _torch_dtypes()[a.dtype], schedule, **tiles)
+        entry = (plan, plan.new_workspace(a.device))
+        _PLANS[key] = entry
+    plan, ws = entry
+    c = torch.empty((M, N), dtype=torch.float32, device=a.device)
+    plan.run(a, b, c, ws)
+    return c

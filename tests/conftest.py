@@ -17,3 +17,11 @@ def pytest_configure(config):
 def oracle_lib():
     import oracle
     return oracle.load()
+
+
+def pytest_runtest_setup(item):
+    # name a GPU case on the real stderr before it runs, so a run that dies on
+    # the GPU still says which case it was in
+    if item.get_closest_marker("gpu"):
+        sys.__stderr__.write(f"[start] {item.nodeid}\n")
+        sys.__stderr__.flush()

@@ -1,0 +1,74 @@
+"""The C-ABI library builds, loads and exports every symbol its header declares (no GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import persistent_stream_tiling_amd as gsk
+from persistent_stream_tiling_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gemm_sk.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gemm_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("gemm_plan_create", "gemm_run", "gemm_plan_destroy",
+                     "gemm_plan_workspace_size", "gemm_plan_describe", "gemm_last_error"):
+        assert required in names
+    assert set(names) == set(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_structs_match_header_layout(tmp_path):
+    # the ctypes mirrors against what a C compiler makes of the header
+    src = tmp_path / "sizes.c"
+    src.write_text("""#include <stdio.h>
+#include <stddef.h>
+#include "gemm_sk.h"
+int main(void) {
+  printf("%zu %zu %zu %zu %zu %zu %zu\\n", sizeof(gemm_tiles), sizeof(gemm_device_desc),
+         sizeof(gemm_segment), sizeof(gemm_plan_info), offsetof(gemm_plan_info, iters_sk),
+         offsetof(gemm_plan_info, workspace), offsetof(gemm_plan_info, lds_bytes));
+  return 0;
+}
+""")
+    exe = tmp_path / "sizes"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True,
+                                          check=True).stdout.split()]
+    want = [ctypes.sizeof(_lib.Tiles), ctypes.sizeof(_lib.DeviceDesc),
+            ctypes.sizeof(_lib.Segment), ctypes.sizeof(_lib.PlanInfo),
+            _lib.PlanInfo.iters_sk.offset, _lib.PlanInfo.workspace.offset,
+            _lib.PlanInfo.lds_bytes.offset]
+    assert got == want
+
+
+def test_no_gpu_means_no_plan_and_a_message():
+    # on a machine without a GPU gemm_plan_create must fail cleanly, never fall back
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    with pytest.raises(ValueError, match="gemm_plan_create failed"):
+        gsk.GemmPlan(64, 64, 64, "f16", "dp")
+
+
+def test_destroy_null_and_describe_null_are_safe():
+    lib = gsk.load()
+    lib.gemm_plan_destroy(None)
+    assert lib.gemm_plan_describe(None, None, 0) == -1
+    assert lib.gemm_plan_workspace_size(None) == 0

@@ -1,0 +1,257 @@
+"""Host-side checks of the work decomposition (no GPU).
+
+The planner and the kernel share one set of inline schedule functions, so
+these checks cover exactly what the GPU executes:
+
+* every (tile, k-iteration) pair is covered exactly once, for every schedule,
+* Stream-K ranges are contiguous, ascending and balanced to within one
+  iteration (issue #1393, the first-wave kernel's per-program range),
+* the hybrid split follows the final revision's host formula,
+* each split tile has exactly one owner (the workgroup holding k = 0), which
+  waits only on later workgroups whose contribution is their first segment,
+  so the waits cannot form a cycle,
+* the tile order and the die remap are bijections.
+"""
+import random
+
+import numpy as np
+import pytest
+
+import persistent_stream_tiling_amd as gsk
+from persistent_stream_tiling_amd import inputs
+
+SCHEDULES = ("dp", "persistent", "streamk", "hybrid")
+
+
+def plan(M, N, K, dtype="f16", schedule="hybrid", cus=256, wg_per_cu=1, **kw):
+    return gsk.plan_for_device(M, N, K, dtype, schedule, cus=cus, xcds=8, wg_per_cu=wg_per_cu, **kw)
+
+
+def all_segments(p):
+    return [p.segments(w) for w in range(p.info["launch_grid"])]
+
+
+def check_plan(p):
+    info = p.info
+    T, ipt, g = info["tiles"], info["iters_per_tile"], info["g"]
+    T_sk, q, r = info["tiles_sk"], info["q"], info["r"]
+    segs = all_segments(p)
+    cover = np.zeros((max(T, 1), max(ipt, 1)), dtype=np.int32)
+    tile_workers = {}
+    for w, ss in enumerate(segs):
+        for i, (tile, kb, ke, role, peer_last) in enumerate(ss):
+            assert 0 <= tile < T and 0 <= kb < ke <= ipt
+            cover[tile, kb:ke] += 1
+            tile_workers.setdefault(tile, []).append((w, kb, ke, role, peer_last, i))
+            if role == gsk.ROLE_CONTRIB:
+                assert i == 0 and kb > 0, "only a first segment may start inside a tile"
+            if role == gsk.ROLE_OWNER:
+                assert kb == 0 and ke < ipt
+                assert i == len([s for s in ss if s[0] < T_sk]) - 1, \
+                    "an owner segment is the last Stream-K segment"
+            if role == gsk.ROLE_FULL:
+                assert kb == 0 and ke == ipt
+    if T and ipt:
+        assert (cover == 1).all(), "every (tile, k-iteration) pair exactly once"
+
+    # Stream-K ranges: contiguous, ascending, lengths q or q+1
+    if T_sk:
+        assert info["iters_sk"] == T_sk * ipt == q * g + r
+        prev_end = 0
+        for w in range(g):
+            its = [t * ipt + k for (t, kb, ke, _, _) in segs[w] if t < T_sk for k in range(kb, ke)]
+            begin = w * q + min(w, r)
+            end = (w + 1) * q + min(w + 1, r)
+            assert its == list(range(begin, end))
+            assert begin == prev_end
+            prev_end = end
+            assert end - begin in (q, q + 1)
+        assert prev_end == T_sk * ipt
+
+    # fixup roles: one owner per split tile, peers = the later workgroups on it
+    for tile, ws in tile_workers.items():
+        if len(ws) == 1:
+            assert ws[0][3] == gsk.ROLE_FULL
+            continue
+        owners = [x for x in ws if x[3] == gsk.ROLE_OWNER]
+        assert len(owners) == 1
+        ow, _, _, _, peer_last, _ = owners[0]
+        contribs = sorted(x[0] for x in ws if x[3] == gsk.ROLE_CONTRIB)
+        assert contribs == list(range(ow + 1, peer_last + 1))
+        for x in ws:
+            if x[3] == gsk.ROLE_CONTRIB:
+                assert x[5] == 0 and x[0] > ow  # signalled before the worker ever waits
+    return segs
+
+
+CONFIGS = [
+    (256, 256, 256, "f32", dict(bm=64, bn=64)),
+    (4096, 4096, 4096, "f16", {}),
+    (4096, 4096, 4096, "f16", dict(bm=256, bn=128)),
+    (4096, 4096, 4096, "f16", dict(bm=128, bn=128)),
+    (1536, 1536, 8192, "f16", {}),
+    (1536, 1536, 8192, "f16", dict(bm=128, bn=128)),
+    (512, 512, 65536, "bf16", {}),
+    (512, 512, 65536, "bf16", dict(bm=128, bn=128)),
+    (2372, 5997, 6089, "bf16", {}),
+    (1095, 6981, 15363, "bf16", dict(bm=128, bn=256)),
+]
+
+
+@pytest.mark.parametrize("schedule", SCHEDULES)
+@pytest.mark.parametrize("cfg", CONFIGS, ids=lambda c: f"{c[0]}x{c[1]}x{c[2]}{c[3]}{c[4]}")
+def test_invariants_on_workloads(cfg, schedule):
+    M, N, K, dt, kw = cfg
+    check_plan(plan(M, N, K, dt, schedule, **kw))
+
+
+def test_invariants_large_mlp_shape():
+    for schedule in SCHEDULES:
+        check_plan(plan(8192, 28672, 8192, "bf16", schedule))
+
+
+def test_invariants_random_sweep():
+    # shapes and grids in the spirit of issue #1393's sweep: the CU count,
+    # twice it, the tile count, and random even grids
+    rnd = random.Random(1393)
+    for _ in range(60):
+        M, N = rnd.randint(1, 3000), rnd.randint(1, 3000)
+        K = rnd.randint(1, 5000)
+        bm, bn = rnd.choice([(64, 64), (128, 128), (256, 128), (128, 256), (256, 256)])
+        tiles = -(-M // bm) * -(-N // bn)
+        g = rnd.choice([256, 512, max(1, min(tiles, 511)), rnd.randrange(2, 512, 2), 1, 7])
+        one_tile = rnd.random() < 0.5
+        for schedule in SCHEDULES:
+            p = plan(M, N, K, "bf16", schedule, wg_per_cu=2, bm=bm, bn=bn, grid=g,
+                     flags=gsk.FLAG_ONE_TILE if one_tile else 0)
+            check_plan(p)
+
+
+def hybrid_split(T, g, two_tiles):
+    # issue #1393, final revision's host wrapper, restated
+    T_sk = T % g
+    if two_tiles and T - T_sk > g:
+        T_sk += g
+    return T_sk
+
+
+@pytest.mark.parametrize("T_shape", [(4096, 4096), (1536, 1536), (512, 512), (8192, 28672),
+                                     (2372, 5997), (6620, 3734), (1000, 1000)])
+@pytest.mark.parametrize("g", [256, 128, 200, 512])
+@pytest.mark.parametrize("two_tiles", [True, False])
+def test_hybrid_split_formula(T_shape, g, two_tiles):
+    M, N = T_shape
+    p = plan(M, N, 4096, "f16", "hybrid", wg_per_cu=2, grid=g,
+             flags=0 if two_tiles else gsk.FLAG_ONE_TILE)
+    T = p.info["tiles"]
+    assert p.info["tiles_sk"] == hybrid_split(T, g, two_tiles)
+    assert p.info["tiles_dp"] == T - p.info["tiles_sk"]
+    if p.info["tiles_dp"]:
+        assert p.info["tiles_dp"] % g == 0 or T < g, "data-parallel part is whole waves"
+
+
+def test_pages_demo_partitions():
+    # second revision's demo: 256 x 512 x 2048, 64^3 blocks, grid 82 -> 32 tiles of
+    # 32 iterations; 1024 iterations over 82 programs: 12 each, the first 40 get 13
+    p = plan(256, 512, 2048, "f16", "streamk", bm=64, bn=64, grid=82)
+    i = p.info
+    assert (i["tiles"], i["iters_per_tile"], i["iters_sk"], i["q"], i["r"]) == (32, 32, 1024, 12, 40)
+    lengths = [sum(ke - kb for (_, kb, ke, _, _) in p.segments(w)) for w in range(82)]
+    assert lengths == [13] * 40 + [12] * 42
+    # first revision's demo: 256 x 512 x 32768, grid 32 -> one whole tile per program,
+    # so Stream-K degenerates to data-parallel ("expected to have similar timings")
+    p = plan(256, 512, 32768, "f16", "streamk", bm=64, bn=64, grid=32)
+    assert (p.info["q"], p.info["r"], p.info["iters_per_tile"]) == (512, 0, 512)
+    for w in range(32):
+        assert [s[3] for s in p.segments(w)] == [gsk.ROLE_FULL]
+    # under the final revision's hybrid formula the same case is all data-parallel
+    assert plan(256, 512, 32768, "f16", "hybrid", bm=64, bn=64, grid=32).info["tiles_sk"] == 0
+    # grid 0 in the pages means plain tiling; here that is the dp schedule
+    assert plan(256, 512, 2048, "f16", "dp", bm=64, bn=64).info["tiles_sk"] == 0
+
+
+def test_dp_is_one_tile_per_workgroup():
+    p = plan(1000, 700, 300, "f16", "dp", bm=128, bn=128)
+    assert p.info["launch_grid"] == p.info["tiles"]
+    for w in range(p.info["launch_grid"]):
+        assert p.segments(w) == [(w, 0, p.info["iters_per_tile"], gsk.ROLE_FULL, w)]
+
+
+def test_persistent_strides_by_grid():
+    p = plan(4096, 4096, 512, "f16", "persistent", bm=128, bn=128)
+    g = p.info["launch_grid"]
+    assert g == 256
+    for w in (0, 5, 255):
+        assert [s[0] for s in p.segments(w)] == [w + i * g for i in range(4)]
+
+
+def test_tile_coords_bijection_and_grouping():
+    p = plan(4096, 2048, 64, "f16", "dp", bm=128, bn=128)  # 32 x 16 tiles
+    seen = {p.tile_coords(t) for t in range(p.info["tiles"])}
+    assert seen == {(m, n) for m in range(32) for n in range(16)}
+    assert [p.tile_coords(t) for t in range(10)] == [(m, 0) for m in range(8)] + [(0, 1), (1, 1)]
+    # ragged last band: 10 tile rows, group 8 -> the last band has 2 rows
+    p = plan(1280, 384, 64, "f16", "dp", bm=128, bn=128)
+    coords = [p.tile_coords(t) for t in range(p.info["tiles"])]
+    assert sorted(coords) == [(m, n) for m in range(10) for n in range(3)]
+    assert coords[24:] == [(8, 0), (9, 0), (8, 1), (9, 1), (8, 2), (9, 2)]
+    # linear order when grouping is off
+    p = plan(1280, 384, 64, "f16", "dp", bm=128, bn=128, group_m=-1)
+    assert [p.tile_coords(t) for t in range(4)] == [(0, 0), (0, 1), (0, 2), (1, 0)]
+
+
+@pytest.mark.parametrize("grid", [1, 7, 8, 36, 255, 256, 1000, 3584])
+def test_die_remap_is_a_bijection_with_contiguous_blocks(grid):
+    p = plan(grid * 64, 64, 64, "f16", "dp", bm=64, bn=64)
+    assert p.info["launch_grid"] == grid
+    logical = [p.logical_wg(h) for h in range(grid)]
+    assert sorted(logical) == list(range(grid))
+    for die in range(8):
+        block = [logical[h] for h in range(die, grid, 8)]
+        assert block == list(range(block[0], block[0] + len(block))) if block else True
+
+
+def test_streamk_grid_must_fit_resident_capacity():
+    with pytest.raises(ValueError, match="resident"):
+        plan(1536, 1536, 8192, "f16", "streamk", grid=300)
+    plan(1536, 1536, 8192, "f16", "streamk", grid=300, wg_per_cu=2)
+    plan(4096, 4096, 64, "f16", "persistent", grid=1000)  # no waits: any grid is fine
+
+
+def test_rejects_bad_arguments():
+    with pytest.raises(ValueError, match="negative"):
+        plan(-1, 4, 4)
+    with pytest.raises(ValueError, match="no kernel"):
+        plan(64, 64, 64, "f16", "dp", bm=96, bn=96)
+    with pytest.raises(ValueError, match="bk"):
+        plan(64, 64, 64, "f16", "dp", bk=32)
+    with pytest.raises(ValueError, match="unknown schedule"):
+        plan(64, 64, 64, "f16", "zigzag")
+
+
+def test_workspace_layout():
+    p = plan(1536, 1536, 8192, "f16", "streamk")
+    ws = p.workspace_bytes
+    assert ws >= 256 + 4 * 256 + 4 * 256 * 256 * 256
+    assert plan(4096, 4096, 4096, "f16", "dp").workspace_bytes == 0
+    assert plan(4096, 4096, 4096, "f16", "persistent").workspace_bytes == 0
+    # rows that are not 16-byte multiples are repacked: the workspace holds the copies
+    p = plan(2372, 5997, 6089, "bf16", "dp")
+    assert p.info["pack_a"] and p.info["pack_b"]
+    assert p.workspace_bytes >= 2372 * 6096 * 2 + 6089 * 6000 * 2
+
+
+def test_empty_shapes_plan():
+    for M, N, K in ((0, 5, 5), (5, 0, 5), (5, 5, 0), (0, 0, 0)):
+        for s in SCHEDULES:
+            p = plan(M, N, K, "f16", s)
+            assert p.info["tiles_sk"] == 0
+
+
+def test_irregular_shape_list_is_reproducible():
+    shapes = inputs.irregular_shapes()
+    assert len(shapes) == 16
+    assert shapes[0] == (2372, 5997, 6089) and shapes[-1] == (2108, 4087, 8760)
+    for m, n, k in shapes:
+        assert 1000 <= m <= 8192 and 1000 <= n <= 8192 and 1000 <= k <= 16384
+        assert m % 128 and n % 128 and k % 128
