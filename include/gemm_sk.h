@@ -69,21 +69,28 @@ enum {
     GEMM_FLAG_ONE_TILE = 1u << 0,
     /* Do not remap workgroup ids so that each XCD gets a contiguous run of
      * tiles (for measuring what the remap buys). */
-    GEMM_FLAG_NO_XCD_REMAP = 1u << 1
+    GEMM_FLAG_NO_XCD_REMAP = 1u << 1,
+    /* fp16/bf16: use the kernel that stages A and B through registers (bk 64)
+     * instead of the direct-to-LDS ring kernel (bk 32). */
+    GEMM_FLAG_REGISTER_STAGED = 1u << 2
 };
 
 /* Tile and schedule knobs.  Every field 0 means "default". */
 typedef struct {
     int32_t bm, bn;   /* output tile (multiples of 32 from the supported set;
                          default per dtype and shape) */
-    int32_t bk;       /* k-depth of one MAC iteration: fixed at 128 bytes of
-                         input per row (64 for fp16/bf16, 32 for fp32); 0 or
-                         that value */
+    int32_t bk;       /* k-depth of one MAC iteration, fixed per kernel: 32
+                         for the fp16/bf16 ring kernel, 64 for the fp16/bf16
+                         register-staged one, 32 for fp32; 0 = any */
     int32_t grid;     /* g: workgroups of the persistent / Stream-K launch;
                          0 = number of CUs (issue #1393 uses the SM count) */
     int32_t group_m;  /* tile-order group height (issue #1393 GROUP_M);
                          0 = 8, < 0 = plain row-major tile order */
     uint32_t flags;   /* GEMM_FLAG_* */
+    int32_t wave_m, wave_n; /* waves per workgroup along M and N (each wave
+                               computes a (bm/wave_m) x (bn/wave_n) block);
+                               0 = the default layout for the tile */
+    int32_t stages;   /* LDS ring depth of the fp16/bf16 ring kernel; 0 = default */
 } gemm_tiles;
 
 /* Device description for planning without touching a GPU (host tests). */
@@ -149,6 +156,9 @@ typedef struct {
     int32_t dtype, schedule;
     int32_t bm, bn, bk, group_m;
     uint32_t flags;
+    int32_t wave_m, wave_n;
+    int32_t kernel_kind;  /* 0 register-staged, 1 direct-to-LDS ring */
+    int32_t stages;
     int32_t tiles_m, tiles_n;
     int32_t tiles;        /* T */
     int32_t iters_per_tile; /* ipt = ceil(K / bk) */

@@ -9,6 +9,7 @@ F32, F16, BF16 = 0, 1, 2
 DP, PERSISTENT, STREAMK, HYBRID = 0, 1, 2, 3
 FLAG_ONE_TILE = 1 << 0
 FLAG_NO_XCD_REMAP = 1 << 1
+FLAG_REGISTER_STAGED = 1 << 2
 ROLE_FULL, ROLE_CONTRIB, ROLE_OWNER = 0, 1, 2
 
 SCHEDULES = {"dp": DP, "persistent": PERSISTENT, "streamk": STREAMK, "hybrid": HYBRID}
@@ -17,7 +18,9 @@ DTYPES = {"f32": F32, "f16": F16, "bf16": BF16}
 
 class Tiles(ctypes.Structure):
     _fields_ = [("bm", ctypes.c_int32), ("bn", ctypes.c_int32), ("bk", ctypes.c_int32),
-                ("grid", ctypes.c_int32), ("group_m", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+                ("grid", ctypes.c_int32), ("group_m", ctypes.c_int32), ("flags", ctypes.c_uint32),
+                ("wave_m", ctypes.c_int32), ("wave_n", ctypes.c_int32),
+                ("stages", ctypes.c_int32)]
 
 
 class DeviceDesc(ctypes.Structure):
@@ -29,6 +32,8 @@ class PlanInfo(ctypes.Structure):
                 ("dtype", ctypes.c_int32), ("schedule", ctypes.c_int32),
                 ("bm", ctypes.c_int32), ("bn", ctypes.c_int32), ("bk", ctypes.c_int32),
                 ("group_m", ctypes.c_int32), ("flags", ctypes.c_uint32),
+                ("wave_m", ctypes.c_int32), ("wave_n", ctypes.c_int32),
+                ("kernel_kind", ctypes.c_int32), ("stages", ctypes.c_int32),
                 ("tiles_m", ctypes.c_int32), ("tiles_n", ctypes.c_int32),
                 ("tiles", ctypes.c_int32), ("iters_per_tile", ctypes.c_int32),
                 ("tiles_sk", ctypes.c_int32), ("tiles_dp", ctypes.c_int32),
@@ -56,11 +61,12 @@ EXPORTS = ("gemm_plan_create", "gemm_plan_create_for_device", "gemm_run", "gemm_
 _lib = None
 
 
-def load(path=LIB_PATH):
+def load(path=None):
     """Load libgemmsk.so; raises if it has not been built (there is no fallback)."""
     global _lib
     if _lib is not None:
         return _lib
+    path = path or LIB_PATH
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with persistent_stream_tiling_amd._build "
                            "(or __graft_entry__.build()); there is no CPU fallback")

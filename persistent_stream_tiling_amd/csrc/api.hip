@@ -52,13 +52,23 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-const Variant *find_variant(int dtype, int bm, int bn)
+// The first compiled variant matching the request (0 = any): the table lists
+// each dtype's preferred kernel for a tile first.
+const Variant *find_variant(int dtype, const gemm_tiles &t)
 {
+    // fp16/bf16 prefer the direct-to-LDS ring kernel and fall back to the
+    // register-staged one for tiles it does not cover (unless staged loads were
+    // asked for explicitly).
+    const bool staged_only = (t.flags & GEMM_FLAG_REGISTER_STAGED) || dtype == GEMM_F32;
     int n = 0;
     const Variant *v = variants(&n);
-    for (int i = 0; i < n; ++i)
-        if (v[i].dtype == dtype && v[i].bm == bm && v[i].bn == bn)
-            return &v[i];
+    for (int kind = staged_only ? 0 : 1; kind >= 0; --kind)
+        for (int i = 0; i < n; ++i)
+            if (v[i].dtype == dtype && v[i].bm == t.bm && v[i].bn == t.bn && v[i].kind == kind &&
+                (t.wave_m == 0 || v[i].wave_m == t.wave_m) &&
+                (t.wave_n == 0 || v[i].wave_n == t.wave_n) && (t.bk == 0 || v[i].bk == t.bk) &&
+                (t.stages == 0 || v[i].stages == t.stages))
+                return &v[i];
     return nullptr;
 }
 
@@ -105,13 +115,11 @@ gemm_plan *create(int64_t M, int64_t N, int64_t K, gemm_dtype dtype, gemm_schedu
         set_error("give both bm and bn, or neither");
         return nullptr;
     }
-    const Variant *var = find_variant(dtype, t.bm, t.bn);
+    const Variant *var = find_variant(dtype, t);
     if (!var) {
-        set_error("no kernel for dtype %d with a %dx%d tile", (int)dtype, t.bm, t.bn);
-        return nullptr;
-    }
-    if (t.bk != 0 && t.bk != var->bk) {
-        set_error("bk must be %d for this dtype (128 bytes of input per row)", var->bk);
+        set_error("no kernel for dtype %d with tile %dx%d, bk %d, waves %dx%d, stages %d, "
+                  "flags 0x%x",
+                  (int)dtype, t.bm, t.bn, t.bk, t.wave_m, t.wave_n, t.stages, t.flags);
         return nullptr;
     }
     if (t.grid < 0) {
@@ -208,6 +216,11 @@ gemm_plan *create(int64_t M, int64_t N, int64_t K, gemm_dtype dtype, gemm_schedu
     if (T_sk > 0) {
         P.q = (int32_t)(p->iters_sk / g);
         P.r = (int32_t)(p->iters_sk % g);
+        if ((int64_t)g * var->bm * var->bn * 4 >= ((int64_t)1 << 31)) {
+            set_error("Stream-K grid %d too large for the partial-tile workspace indexing", g);
+            delete p;
+            return nullptr;
+        }
         if (g > p->wg_capacity) {
             set_error("Stream-K grid %d exceeds the %d workgroups that can be resident at once; "
                       "the fixup needs them all running together",
@@ -315,6 +328,10 @@ int gemm_plan_get_info(const gemm_plan *p, gemm_plan_info *o)
     o->bk = p->bk;
     o->group_m = p->group_m;
     o->flags = p->flags;
+    o->wave_m = p->variant->wave_m;
+    o->wave_n = p->variant->wave_n;
+    o->kernel_kind = p->variant->kind;
+    o->stages = p->variant->stages;
     o->tiles_m = p->P.tiles_m;
     o->tiles_n = p->P.tiles_n;
     o->tiles = p->P.T;
@@ -344,11 +361,13 @@ int gemm_plan_describe(const gemm_plan *p, char *buf, size_t len)
         return -1;
     }
     return snprintf(buf, buf ? len : 0,
-                    "M,N,K=%lld,%lld,%lld %s %s tile=%dx%dx%d group_m=%d | tiles %dx%d=%d "
+                    "M,N,K=%lld,%lld,%lld %s %s tile=%dx%dx%d waves=%dx%d %s%d group_m=%d | tiles %dx%d=%d "
                     "ipt=%d | T_sk=%d T_dp=%d I_sk=%lld g=%d q=%d r=%d | grid=%d x %d threads, "
                     "lds=%zu B, capacity=%d wg, xcds=%d | pack A=%d B=%d | workspace=%zu B",
                     (long long)p->M, (long long)p->N, (long long)p->K, dtype_name(p->dtype),
-                    sched_name(p->schedule), p->bm, p->bn, p->bk, p->group_m, p->P.tiles_m,
+                    sched_name(p->schedule), p->bm, p->bn, p->bk, p->variant->wave_m,
+                    p->variant->wave_n, p->variant->kind ? "ring" : "staged",
+                    p->variant->kind ? p->variant->stages : 2, p->group_m, p->P.tiles_m,
                     p->P.tiles_n, p->P.T, p->P.ipt, p->P.T_sk, p->P.T - p->P.T_sk,
                     (long long)p->iters_sk, p->P.g, p->P.q, p->P.r, p->P.grid,
                     p->variant->threads, p->variant->lds_bytes, p->wg_capacity, p->xcds,

@@ -29,8 +29,11 @@ struct KernelArgs {
 struct Variant {
     int dtype;             // gemm_dtype
     int bm, bn, bk;
+    int wave_m, wave_n;    // wave grid of the workgroup
     int threads;
     size_t lds_bytes;
+    int kind;              // 0: register-staged loads, 1: direct-to-LDS ring
+    int stages;            // LDS ring depth of kind 1 (0 for kind 0)
     int (*launch)(const KernelArgs &args, int grid, hipStream_t stream);
     const void *kernel;    // for occupancy queries
 };

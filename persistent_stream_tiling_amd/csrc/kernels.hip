@@ -50,6 +50,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base)
                                              kRsrcWord3);
 }
 
+// Bits of a float, taken by value.  (A bit cast applied directly to one
+// subscripted element of a vector lvalue was lowered to a read of element 0;
+// every scalar reinterpretation in this file goes through here.)
+__device__ __forceinline__ uint32_t bits_of(float x) { return __builtin_bit_cast(uint32_t, x); }
+
 __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t rsrc, uint32_t off)
 {
     return __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)off, 0, 0);
@@ -95,12 +100,14 @@ __device__ __forceinline__ void mfma_step(f32x16 &acc, const u32x4 &bt, const u3
                                                       __builtin_bit_cast(bf16x8, a), acc, 0, 0, 0);
     } else {
         // fp32: a lane's chunk is 4 consecutive k; instruction e takes element e
-        // from both operands, so the same k meets the same k.
+        // from both operands, so the same k meets the same k.  (The whole vector
+        // is reinterpreted first: a bit cast of one subscripted element of a
+        // vector lvalue was lowered to a read of element 0.)
+        const f32x4 btf = __builtin_bit_cast(f32x4, bt);
+        const f32x4 af = __builtin_bit_cast(f32x4, a);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__builtin_bit_cast(float, bt[e]),
-                                                       __builtin_bit_cast(float, a[e]), acc, 0, 0,
-                                                       0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(btf[e], af[e], acc, 0, 0, 0);
     }
 }
 
@@ -142,6 +149,137 @@ __device__ __forceinline__ void lds_store_words(uint8_t *p, const uint32_t *w)
     } else {
         *(uint32_t *)p = w[0];
     }
+}
+
+// Store one 32x32 accumulator block (rows row0 + 32*mt.., columns col0 +
+// 32*nt.. of the tile) to C through a buffer descriptor based at the tile's
+// first row; an element outside C gets an out-of-range offset so its write is
+// dropped: no branches around the stores.
+__device__ __forceinline__ void store_block(const f32x16 &blk, const KernelArgs &args,
+                                            __amdgpu_buffer_rsrc_t c_rsrc, int m0, int n0,
+                                            int row, int col, int half)
+{
+    const bool row_ok = m0 + row < args.M;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const int n = n0 + col + 8 * g + 4 * half;
+        const uint32_t off = (uint32_t)((row * args.ldc + n) * 4);
+        const u32x4 u = u32x4{bits_of(blk[4 * g]),
+                              bits_of(blk[4 * g + 1]),
+                              bits_of(blk[4 * g + 2]),
+                              bits_of(blk[4 * g + 3])};
+        if (args.c_vec) {
+            // N % 4 == 0: a vector is either wholly inside C or wholly outside
+            __builtin_amdgcn_raw_buffer_store_b128(u, c_rsrc,
+                                                   (int)(row_ok && n < args.N ? off : kOutOfRange),
+                                                   0, 0);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                __builtin_amdgcn_raw_buffer_store_b32(
+                    u[e], c_rsrc, (int)(row_ok && n + e < args.N ? off + 4 * e : kOutOfRange), 0,
+                    0);
+        }
+    }
+}
+
+// Finish one unit of work: a Stream-K tail is parked in the workgroup's
+// partial slot and signalled; a split tile's head waits for its later
+// workgroups and adds their partials; then the tile is stored to C.
+//
+// Accumulator layout (shared by both kernels): acc[mt][nt] is the 32x32 MFMA
+// block at rows row0 + 32*mt, columns col0 + 32*nt of the tile, issued with
+// swapped operands so that lane l holds C[row0 + 32*mt + l%32][col0 + 32*nt +
+// 8*g + 4*(l/32) + e] in register 4*g + e.  A partial slot holds the blocks in
+// this fragment order (lane-contiguous 16-byte vectors), so writes and reads of
+// it are fully coalesced.  Partial slots are addressed through a buffer
+// descriptor: lane offset in a VGPR and the fragment's offset as a scalar
+// constant, so no per-fragment 64-bit addresses stay alive.
+template <int BM, int BN, int MT, int NT>
+__device__ __forceinline__ void finish_tile(f32x16 (&acc)[MT][NT], const KernelArgs &args,
+                                            const WorkItem &w, int p, int m0, int n0, int wave,
+                                            int lane, int row0, int col0)
+{
+    const int tid = threadIdx.x;
+    const int half = lane >> 5, l32 = lane & 31;
+    const uint32_t lane_off = (uint32_t)lane * 16;
+    if (w.role == ROLE_CONTRIB) {
+        // Tail of a split tile: park it in this workgroup's slot, then signal.
+        const __amdgpu_buffer_rsrc_t slot = make_rsrc(args.partials + (int64_t)p * (BM * BN));
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int f = ((wave * MT + mt) * NT + nt) * 4 + g;
+                    const u32x4 u = u32x4{bits_of(acc[mt][nt][4 * g]),
+                                          bits_of(acc[mt][nt][4 * g + 1]),
+                                          bits_of(acc[mt][nt][4 * g + 2]),
+                                          bits_of(acc[mt][nt][4 * g + 3])};
+                    __builtin_amdgcn_raw_buffer_store_b128(u, slot, (int)lane_off, f * 1024, 0);
+                }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __syncthreads();
+        if (tid == 0)
+            __hip_atomic_store(args.flags + p, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
+    const __amdgpu_buffer_rsrc_t c_rsrc = make_rsrc(args.C + (int64_t)m0 * args.ldc);
+    if (w.role == ROLE_OWNER) {
+        // Head of a split tile: wait for every later workgroup on the tile,
+        // then add their partials in ascending workgroup (= ascending k) order.
+        if (tid == 0) {
+            for (int q = p + 1; q <= w.peer_last; ++q) {
+                int spins = 0;
+                while (__hip_atomic_load(args.flags + q, __ATOMIC_ACQUIRE,
+                                         __HIP_MEMORY_SCOPE_AGENT) == 0) {
+                    if (++spins > args.spin_limit) {
+                        __hip_atomic_store(args.status, 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(2);
+                }
+                // Consumed: leave the flag clear for the next run.
+                __hip_atomic_store(args.flags + q, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        __syncthreads();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        // Block by block: add the peers' partials in ascending order, store.
+        const __amdgpu_buffer_rsrc_t slots = make_rsrc(args.partials);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                f32x16 blk = acc[mt][nt];
+                const uint32_t frag_off = (((wave * MT + mt) * NT + nt) * 4 * 64) * 16 + lane_off;
+                for (int q = p + 1; q <= w.peer_last; ++q) {
+                    // slot offsets stay below 2^31 bytes (g * bm * bn * 4 is checked at plan time)
+                    const uint32_t off = (uint32_t)q * (uint32_t)(BM * BN * 4) + frag_off;
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const f32x4 v = __builtin_bit_cast(
+                            f32x4, __builtin_amdgcn_raw_buffer_load_b128(slots, (int)off,
+                                                                         g * 1024, 0));
+                        blk[4 * g] += v[0];
+                        blk[4 * g + 1] += v[1];
+                        blk[4 * g + 2] += v[2];
+                        blk[4 * g + 3] += v[3];
+                    }
+                }
+                store_block(blk, args, c_rsrc, m0, n0, row0 + mt * 32 + l32, col0 + nt * 32,
+                            half);
+            }
+        return;
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+            store_block(acc[mt][nt], args, c_rsrc, m0, n0, row0 + mt * 32 + l32, col0 + nt * 32,
+                        half);
 }
 
 template <int DT, int BM, int BN, int WM, int WN>
@@ -286,6 +424,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(KernelArgs args)
         int s = 0;
         for (int kk = w.kb; kk + 1 < w.ke; ++kk) {
             load_slab(kk + 1);
+            // Keep the next slab's global loads at the top of the iteration so
+            // their latency overlaps this slab's MFMAs (the scheduler would
+            // otherwise sink them next to the LDS writes that consume them).
+            __builtin_amdgcn_sched_barrier(0);
             compute_slab(s);
             store_slab(s ^ 1);
             __syncthreads();
@@ -293,92 +435,298 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(KernelArgs args)
         }
         compute_slab(s);
 
-        // Fragment f of this thread: block (mt, nt), row group g (4 rows of C^T,
-        // i.e. 4 consecutive columns of C).
-        if (w.role == ROLE_CONTRIB) {
-            // Tail of a split tile: park it in this workgroup's slot, then signal.
-            float *slot = args.partials + (int64_t)p * (BM * BN);
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const int f = ((wave * MT + mt) * NT + nt) * 4 + g;
-                        *(f32x4 *)(slot + (f * 64 + lane) * 4) =
-                            f32x4{acc[mt][nt][4 * g], acc[mt][nt][4 * g + 1],
-                                  acc[mt][nt][4 * g + 2], acc[mt][nt][4 * g + 3]};
-                    }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-            __syncthreads();
-            if (tid == 0)
-                __hip_atomic_store(args.flags + p, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-            continue;
-        }
-        if (w.role == ROLE_OWNER) {
-            // Head of a split tile: wait for every later workgroup on the tile,
-            // then add their partials in ascending workgroup (= ascending k) order.
-            if (tid == 0) {
-                for (int q = p + 1; q <= w.peer_last; ++q) {
-                    int spins = 0;
-                    while (__hip_atomic_load(args.flags + q, __ATOMIC_ACQUIRE,
-                                             __HIP_MEMORY_SCOPE_AGENT) == 0) {
-                        if (++spins > args.spin_limit) {
-                            __hip_atomic_store(args.status, 1, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
-                            break;
-                        }
-                        __builtin_amdgcn_s_sleep(2);
-                    }
-                    // Consumed: leave the flag clear for the next run.
-                    __hip_atomic_store(args.flags + q, 0, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-                }
-            }
-            __syncthreads();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-            for (int q = p + 1; q <= w.peer_last; ++q) {
-                const float *slot = args.partials + (int64_t)q * (BM * BN);
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                        for (int g = 0; g < 4; ++g) {
-                            const int f = ((wave * MT + mt) * NT + nt) * 4 + g;
-                            f32x4 v = *(const f32x4 *)(slot + (f * 64 + lane) * 4);
-                            acc[mt][nt][4 * g] += v[0];
-                            acc[mt][nt][4 * g + 1] += v[1];
-                            acc[mt][nt][4 * g + 2] += v[2];
-                            acc[mt][nt][4 * g + 3] += v[3];
-                        }
-            }
-        }
+        finish_tile<BM, BN, MT, NT>(acc, args, w, p, m0, n0, wave, lane,
+                                    wy * Cfg::WTM, wx * Cfg::WTN);
+    }
+}
 
-        // Store the tile: lane holds C[m][n .. n+3] for each fragment.
+// ---------------------------------------------------------------------------
+// fp16/bf16 kernel with direct global -> LDS loads and an S-stage LDS ring.
+//
+// Each MAC iteration covers BK = 32 values of k.  Its slab of A (BM rows of 64
+// bytes) and B (32 rows of BN values, row-major as in memory) is copied by
+// buffer loads that write LDS directly, S - 1 iterations ahead of its use, so
+// the copy has S - 2 whole iterations of MFMA work to hide behind and needs no
+// registers.  A rows are read as k-contiguous MFMA fragments with 16-byte
+// reads; B is read with the transposing LDS read (each 16-lane group turns a
+// 4 x 16 block of row-major values into per-lane runs of 4 k), so it never
+// passes through registers on its way in.
+//
+// Swizzles (16-byte chunk index XOR a function of the row):
+//   A: chunk ^ (((row >> 1) ^ (row >> 3)) & 3)   64-byte rows
+//   B: chunk ^ kB[k & 3], kB = {0, 6, 10, 12}    BN * 2-byte rows
+// A fragment reads (32 consecutive rows, one chunk) and B transposing reads
+// (4 consecutive k-rows x 32 bytes per 16-lane group) then hit distinct banks.
+//
+// Per iteration and wave: wait for the next stage's copies, barrier, launch
+// the copy S - 1 iterations ahead into the stage everybody has finished with,
+// read the next stage's first fragments while this stage's second half of
+// MFMAs runs.  One barrier per iteration.
+template <int DT, int BM, int BN, int WM, int WN, int S>
+struct DmaTile {
+    static constexpr int NW = WM * WN, NTH = 64 * NW;
+    static constexpr int BK = 32;
+    static constexpr int B_ROW = BN * 2;                   // bytes per B k-row
+    static constexpr int A_STAGE = BM * 64, B_STAGE = BK * BN * 2;
+    static constexpr int STAGE = A_STAGE + B_STAGE;
+    static constexpr int LDS = S * STAGE;
+    static constexpr int A_INSTR = A_STAGE / 1024 / NW;    // 1 KiB copies per wave and stage
+    static constexpr int B_INSTR = B_STAGE / 1024 / NW;
+    static constexpr int LPI = A_INSTR + B_INSTR;
+    static constexpr int WTM = BM / WM, WTN = BN / WN, MT = WTM / 32, NT = WTN / 32;
+    static_assert(DT == 1 || DT == 2, "fp16 / bf16 only");
+    static_assert(A_INSTR * 1024 * NW == A_STAGE && B_INSTR * 1024 * NW == B_STAGE,
+                  "stage copies must split evenly over the waves");
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0 && BN >= 128, "tile shape");
+    static_assert(S >= 3 && LPI * (S - 2) <= 63, "ring depth");
+    static_assert(LDS <= 160 * 1024, "LDS budget");
+};
+
+__device__ __forceinline__ uint32_t swz_a(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+
+__device__ __forceinline__ uint32_t swz_b(int krow)
+{
+    return (0xCA60u >> ((krow & 3) * 4)) & 0xF;  // {0, 6, 10, 12}[krow & 3]
+}
+
+// s_waitcnt vmcnt(n * LPI) for a runtime n in [0, 3]
+template <int LPI>
+__device__ __forceinline__ void wait_copies(int n)
+{
+    if (n <= 0)
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else if (n == 1)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPI) : "memory");
+    else if (n == 2)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LPI) : "memory");
+    else
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * LPI) : "memory");
+}
+
+__device__ __forceinline__ void barrier_only()
+{
+    // A workgroup barrier with no memory fence: the copies it orders are
+    // already complete (s_waitcnt above); the asm keeps the compiler from
+    // moving LDS accesses across it.
+    asm volatile("s_barrier" ::: "memory");
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+#define GSK_LDS(T, p) ((__attribute__((address_space(3))) T *)(p))
+
+// Raw buffer descriptor (base, no stride, 2^31 - 1 bytes, untyped) as four
+// scalar words, for the copy issued from inline assembly below.
+__device__ __forceinline__ i32x4 rsrc_words(const void *base)
+{
+    const uint64_t b = (uint64_t)base;
+    return i32x4{(int)(uint32_t)b, (int)((uint32_t)(b >> 32) & 0xffff), 0x7fffffff, kRsrcWord3};
+}
+
+// Copy 16 bytes per lane from buffer offset voff (0x80000000: out of range,
+// zeros) into LDS at lds_addr + 16 * lane (lds_addr wave-uniform).  Issued as
+// inline assembly so that the compiler does not treat it as an outstanding LDS
+// write: it would otherwise wait for every copy in flight before each
+// transposing LDS read, which defeats the ring.  The ring's own s_waitcnt
+// vmcnt() waits and barriers order these copies against the reads.
+__device__ __forceinline__ void copy16(i32x4 rsrc, uint32_t voff, uint32_t lds_addr)
+{
+    asm volatile("s_mov_b32 m0, %0\n\t"
+                 "s_nop 0\n\t"
+                 "buffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(rsrc)
+                 : "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_address(const uint8_t *p)
+{
+    return (uint32_t)(uintptr_t)GSK_LDS(const uint8_t, p);
+}
+
+template <int DT, int BM, int BN, int WM, int WN, int S>
+__global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel_dma(KernelArgs args)
+{
+    using Cfg = DmaTile<DT, BM, BN, WM, WN, S>;
+    constexpr int NW = Cfg::NW, MT = Cfg::MT, NT = Cfg::NT, LPI = Cfg::LPI;
+    constexpr int A_INSTR = Cfg::A_INSTR, B_INSTR = Cfg::B_INSTR;
+    constexpr int A_STAGE = Cfg::A_STAGE, STAGE = Cfg::STAGE, B_ROW = Cfg::B_ROW;
+    constexpr int NMFMA = MT * NT;  // MFMAs per slab
+
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[Cfg::LDS];
+
+    const Partition &P = args.P;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wy = wave / WN, wx = wave - (wave / WN) * WN;
+    const int half = lane >> 5, l32 = lane & 31;
+    const int p = logical_wg((int32_t)blockIdx.x, P.grid, P.xcds);
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_address(lds));
+
+    // Copy geometry of this lane (fixed for the kernel).  Copy j of this wave
+    // fills the 1 KiB block j * NW + wave of the stage's A (or B) region; the
+    // lane writes bytes [16 * lane, 16 * lane + 16) of it.
+    int a_row[A_INSTR], a_chunk[A_INSTR];
+#pragma unroll
+    for (int j = 0; j < A_INSTR; ++j) {
+        const int o = (j * NW + wave) * 1024 + lane * 16;
+        a_row[j] = o >> 6;
+        a_chunk[j] = ((o >> 4) & 3) ^ swz_a(o >> 6);
+    }
+    int b_krow[B_INSTR], b_chunk[B_INSTR];
+#pragma unroll
+    for (int j = 0; j < B_INSTR; ++j) {
+        const int o = (j * NW + wave) * 1024 + lane * 16;
+        b_krow[j] = o / B_ROW;
+        b_chunk[j] = ((o % B_ROW) >> 4) ^ swz_b(o / B_ROW);
+    }
+
+    // Fragment read offsets within a stage (slab st = 0, 1 of 16 k each).
+    uint32_t a_rd[2][MT];
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-            const int m = m0 + wy * Cfg::WTM + mt * 32 + l32;
-            if (m >= args.M)
-                continue;
-            float *crow = args.C + (int64_t)m * args.ldc;
+            const int row = wy * Cfg::WTM + mt * 32 + l32;
+            a_rd[st][mt] = row * 64 + (((2 * st + half) ^ swz_a(row)) << 4);
+        }
+    uint32_t b_rd[2][NT][2];
+    {
+        const int g = lane >> 4, si = lane & 15;
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int n = n0 + wx * Cfg::WTN + nt * 32 + 8 * g + 4 * half;
-                    f32x4 v = f32x4{acc[mt][nt][4 * g], acc[mt][nt][4 * g + 1],
-                                    acc[mt][nt][4 * g + 2], acc[mt][nt][4 * g + 3]};
-                    if (args.c_vec && n + 3 < args.N) {
-                        *(f32x4 *)(crow + n) = v;
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (n + e < args.N)
-                                crow[n + e] = v[e];
-                    }
+                for (int t = 0; t < 2; ++t) {
+                    const int krow = 16 * st + 8 * (g >> 1) + 4 * t + (si >> 2);
+                    const int n = wx * Cfg::WTN + nt * 32 + 16 * (g & 1) + 4 * (si & 3);
+                    b_rd[st][nt][t] = A_STAGE + krow * B_ROW +
+                                      (((n >> 3) ^ swz_b(krow)) << 4) + (n & 7) * 2;
                 }
+    }
+
+    f32x16 acc[MT][NT];
+
+    WorkCursor cur = work_begin(P, p);
+    WorkItem w;
+    while (work_next(P, p, cur, w)) {
+        int tm, tn;
+        tile_coords(P, w.tile, &tm, &tn);
+        const int m0 = tm * BM, n0 = tn * BN;
+
+        uint32_t a_off[A_INSTR];
+#pragma unroll
+        for (int j = 0; j < A_INSTR; ++j)
+            a_off[j] = m0 + a_row[j] < args.M
+                           ? (uint32_t)(a_row[j] * args.lda * 2 + a_chunk[j] * 16)
+                           : kOutOfRange;
+        uint32_t b_off[B_INSTR];
+#pragma unroll
+        for (int j = 0; j < B_INSTR; ++j)
+            b_off[j] = n0 + b_chunk[j] * 8 < args.N
+                           ? (uint32_t)(b_krow[j] * args.ldb * 2 + b_chunk[j] * 16)
+                           : kOutOfRange;
+
+        // The j-th copy (A copies first, then B) of MAC iteration kk into stage s.
+        auto copy_one = [&](int kk, int s, int j) {
+            const int k0 = kk * Cfg::BK;
+            const int k_left = args.K - k0;
+            if (j < A_INSTR) {
+                const i32x4 ra = rsrc_words(args.A + ((int64_t)m0 * args.lda + k0) * 2);
+                copy16(ra, a_chunk[j] * 8 < k_left ? a_off[j] : kOutOfRange,
+                       lds0 + s * STAGE + (j * NW + wave) * 1024);
+            } else {
+                const int jb = j - A_INSTR;
+                const i32x4 rb = rsrc_words(args.B + ((int64_t)k0 * args.ldb + n0) * 2);
+                copy16(rb, b_krow[jb] < k_left ? b_off[jb] : kOutOfRange,
+                       lds0 + s * STAGE + A_STAGE + (jb * NW + wave) * 1024);
+            }
+        };
+        auto read_a = [&](int s, int st, int mt) {
+            return *(const u32x4 *)(lds + s * STAGE + a_rd[st][mt]);
+        };
+        auto read_b = [&](int s, int st, int nt) {
+            const uint8_t *base = lds + s * STAGE;
+            const i16x4 lo =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16(GSK_LDS(i16x4, base + b_rd[st][nt][0]));
+            const i16x4 hi =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16(GSK_LDS(i16x4, base + b_rd[st][nt][1]));
+            const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+            return u32x4{l2[0], l2[1], h2[0], h2[1]};
+        };
+
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                acc[mt][nt] = f32x16{};
+
+        const int n = w.ke - w.kb;  // MAC iterations of this item (>= 1)
+        // All waves are done with the previous item's stages before refilling.
+        barrier_only();
+#pragma unroll
+        for (int j = 0; j < S - 1; ++j)
+            if (j < n)
+#pragma unroll
+                for (int c = 0; c < LPI; ++c)
+                    copy_one(w.kb + j, j, c);
+        wait_copies<LPI>(n - 1 < S - 2 ? n - 1 : S - 2);
+        barrier_only();
+
+        u32x4 fa0[MT], fb0[NT], fa1[MT], fb1[NT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+            fa0[mt] = read_a(0, 0, mt);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+            fb0[nt] = read_b(0, 0, nt);
+
+        int s = 0;
+        for (int i = 0; i < n; ++i) {
+            const int s_next = s + 1 == S ? 0 : s + 1;
+            // (a) first slab's MFMAs, with the second slab's fragment reads
+            //     issued one per MFMA while the MFMAs run
+#pragma unroll
+            for (int j = 0; j < NMFMA; ++j) {
+                mfma_step<DT>(acc[j / NT][j % NT], fb0[j % NT], fa0[j / NT]);
+                if (j < MT)
+                    fa1[j] = read_a(s, 1, j);
+                else if (j < MT + NT)
+                    fb1[j - MT] = read_b(s, 1, j - MT);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            const bool more = i + 1 < n;
+            if (more) {
+                // (b) next stage complete in every wave; everyone is past the
+                //     stage the next copy will overwrite
+                const int after = n - 2 - i < S - 3 ? n - 2 - i : S - 3;
+                wait_copies<LPI>(after);
+                barrier_only();
+            }
+            // (c) second slab's MFMAs, with the copies S - 1 iterations ahead
+            //     and the next stage's first-slab reads in between
+            const bool copy = i + S - 1 < n;
+            const int s_fill = s == 0 ? S - 1 : s - 1;  // stage of iteration i - 1
+#pragma unroll
+            for (int j = 0; j < NMFMA; ++j) {
+                mfma_step<DT>(acc[j / NT][j % NT], fb1[j % NT], fa1[j / NT]);
+                if (j < LPI && copy)
+                    copy_one(w.kb + i + S - 1, s_fill, j);
+                if (more) {
+                    if (j < MT)
+                        fa0[j] = read_a(s_next, 0, j);
+                    else if (j < MT + NT)
+                        fb0[j - MT] = read_b(s_next, 0, j - MT);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            s = s_next;
         }
+
+        finish_tile<BM, BN, MT, NT>(acc, args, w, p, m0, n0, wave, lane, wy * Cfg::WTM,
+                                    wx * Cfg::WTN);
     }
 }
 
@@ -390,19 +738,39 @@ static int launch_gemm(const KernelArgs &args, int grid, hipStream_t stream)
     return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
-#define GSK_VARIANT(DT, BM, BN, WM, WN)                                                          \
-    Variant{DT, BM, BN, Tile<DT, BM, BN, WM, WN>::BK, Tile<DT, BM, BN, WM, WN>::NTH,             \
-            (size_t)Tile<DT, BM, BN, WM, WN>::LDS, &launch_gemm<DT, BM, BN, WM, WN>,             \
-            (const void *)&gemm_kernel<DT, BM, BN, WM, WN>}
+template <int DT, int BM, int BN, int WM, int WN, int S>
+static int launch_gemm_dma(const KernelArgs &args, int grid, hipStream_t stream)
+{
+    hipLaunchKernelGGL((gemm_kernel_dma<DT, BM, BN, WM, WN, S>), dim3(grid),
+                       dim3(DmaTile<DT, BM, BN, WM, WN, S>::NTH), 0, stream, args);
+    return hipGetLastError() == hipSuccess ? 0 : -3;
+}
 
+// Register-staged kernel (fp32, and fp16/bf16 for comparison)
+#define GSK_STAGED(DT, BM, BN, WM, WN)                                                           \
+    Variant{DT, BM, BN, Tile<DT, BM, BN, WM, WN>::BK, WM, WN, Tile<DT, BM, BN, WM, WN>::NTH,     \
+            (size_t)Tile<DT, BM, BN, WM, WN>::LDS, 0, 0, &launch_gemm<DT, BM, BN, WM, WN>,        \
+            (const void *)&gemm_kernel<DT, BM, BN, WM, WN>}
+// Direct-to-LDS ring kernel (fp16/bf16)
+#define GSK_DMA(DT, BM, BN, WM, WN, S)                                                           \
+    Variant{DT, BM, BN, 32, WM, WN, DmaTile<DT, BM, BN, WM, WN, S>::NTH,                         \
+            (size_t)DmaTile<DT, BM, BN, WM, WN, S>::LDS, 1, S,                                   \
+            &launch_gemm_dma<DT, BM, BN, WM, WN, S>,                                             \
+            (const void *)&gemm_kernel_dma<DT, BM, BN, WM, WN, S>}
+
+// The first entry matching a request wins, so each dtype's preferred kernel
+// for a tile comes first.
 static const Variant kVariants[] = {
-    GSK_VARIANT(1, 256, 256, 2, 2), GSK_VARIANT(1, 256, 128, 2, 2),
-    GSK_VARIANT(1, 128, 256, 2, 2), GSK_VARIANT(1, 128, 128, 2, 2),
-    GSK_VARIANT(1, 64, 64, 2, 2),
-    GSK_VARIANT(2, 256, 256, 2, 2), GSK_VARIANT(2, 256, 128, 2, 2),
-    GSK_VARIANT(2, 128, 256, 2, 2), GSK_VARIANT(2, 128, 128, 2, 2),
-    GSK_VARIANT(2, 64, 64, 2, 2),
-    GSK_VARIANT(0, 128, 128, 2, 2), GSK_VARIANT(0, 64, 64, 2, 2),
+    GSK_DMA(1, 256, 256, 2, 2, 4), GSK_DMA(1, 256, 256, 2, 4, 4), GSK_DMA(1, 256, 256, 4, 2, 4),
+    GSK_DMA(1, 256, 256, 2, 2, 5), GSK_DMA(1, 256, 128, 2, 2, 4), GSK_DMA(1, 128, 256, 2, 2, 4),
+    GSK_DMA(1, 128, 128, 2, 2, 4),
+    GSK_DMA(2, 256, 256, 2, 2, 4), GSK_DMA(2, 256, 256, 2, 4, 4), GSK_DMA(2, 256, 256, 4, 2, 4),
+    GSK_DMA(2, 256, 256, 2, 2, 5), GSK_DMA(2, 256, 128, 2, 2, 4), GSK_DMA(2, 128, 256, 2, 2, 4),
+    GSK_DMA(2, 128, 128, 2, 2, 4),
+    GSK_STAGED(1, 256, 256, 2, 2), GSK_STAGED(1, 256, 256, 4, 2), GSK_STAGED(1, 128, 128, 2, 2),
+    GSK_STAGED(1, 64, 64, 2, 2),
+    GSK_STAGED(2, 256, 256, 2, 2), GSK_STAGED(2, 128, 128, 2, 2), GSK_STAGED(2, 64, 64, 2, 2),
+    GSK_STAGED(0, 128, 128, 2, 2), GSK_STAGED(0, 64, 64, 2, 2),
 };
 
 const Variant *variants(int *count)

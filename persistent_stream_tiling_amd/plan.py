@@ -33,10 +33,10 @@ class GemmPlan:
     """
 
     def __init__(self, M, N, K, dtype, schedule="hybrid", bm=0, bn=0, bk=0, grid=0, group_m=0,
-                 flags=0, device=None):
+                 flags=0, wave_m=0, wave_n=0, stages=0, device=None):
         self._lib = load()
         self._h = None
-        tiles = Tiles(bm, bn, bk, grid, group_m, flags)
+        tiles = Tiles(bm, bn, bk, grid, group_m, flags, wave_m, wave_n, stages)
         d = _code(DTYPES, dtype, "dtype")
         s = _code(SCHEDULES, schedule, "schedule")
         if device is not None:

@@ -223,8 +223,8 @@ def test_rejects_bad_arguments():
         plan(-1, 4, 4)
     with pytest.raises(ValueError, match="no kernel"):
         plan(64, 64, 64, "f16", "dp", bm=96, bn=96)
-    with pytest.raises(ValueError, match="bk"):
-        plan(64, 64, 64, "f16", "dp", bk=32)
+    with pytest.raises(ValueError, match="no kernel"):
+        plan(64, 64, 64, "f16", "dp", bk=48)
     with pytest.raises(ValueError, match="unknown schedule"):
         plan(64, 64, 64, "f16", "zigzag")
 
