@@ -98,19 +98,21 @@ def cpu_baseline(a_bits, b_bits, M, N, K, dtype, seed, target_s):
     import oracle
     from persistent_stream_tiling_amd import inputs
     threads = oracle.default_threads()
-    rows, cols = inputs.sample_positions(M, N, 4096, seed=seed)
+    # calibrate on a small sample, then size the timed sample to ~target_s
+    rows, cols = inputs.sample_positions(M, N, threads * 4, seed=seed)
     t = time.perf_counter()
-    oracle.gemm_sampled(a_bits, b_bits, dtype, rows[:threads * 2], cols[:threads * 2], threads)
-    per = (time.perf_counter() - t) / (threads * 2)
-    n = int(min(4096, max(threads * 4, target_s / max(per, 1e-9))))
-    rows, cols = rows[:n], cols[:n]
+    oracle.gemm_sampled(a_bits, b_bits, dtype, rows, cols, threads)
+    per = (time.perf_counter() - t) / rows.size
+    n = int(min(M * N, max(threads * 8, target_s / max(per, 1e-9))))
+    rows, cols = inputs.sample_positions(M, N, n, seed=seed + 1)
     t = time.perf_counter()
     ref, scale = oracle.gemm_sampled(a_bits, b_bits, dtype, rows, cols, threads)
     secs = time.perf_counter() - t
     return {"value": 2.0 * K * n / secs / 1e12, "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{n} seeded output elements of the {M}x{N}x{K} {dtype} product "
-                      f"(fp64, {secs:.1f} s)"}, (rows, cols, ref, scale)
+            "sample": f"{n} seeded output elements of the {M}x{N}x{K} {dtype} product, each a "
+                      f"{K}-term fp64 dot product ({secs:.1f} s on {threads} threads)"}, \
+        (rows, cols, ref, scale)
 
 
 def load_traffic(workload, schedule):

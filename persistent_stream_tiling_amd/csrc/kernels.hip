@@ -761,15 +761,18 @@ static int launch_gemm_dma(const KernelArgs &args, int grid, hipStream_t stream)
 // The first entry matching a request wins, so each dtype's preferred kernel
 // for a tile comes first.
 static const Variant kVariants[] = {
-    GSK_DMA(1, 256, 256, 2, 2, 4), GSK_DMA(1, 256, 256, 2, 4, 4), GSK_DMA(1, 256, 256, 4, 2, 4),
-    GSK_DMA(1, 256, 256, 2, 2, 5), GSK_DMA(1, 256, 128, 2, 2, 4), GSK_DMA(1, 128, 256, 2, 2, 4),
+    GSK_DMA(1, 256, 256, 4, 2, 4), GSK_DMA(1, 256, 256, 4, 2, 5), GSK_DMA(1, 256, 256, 2, 4, 4),
+    GSK_DMA(1, 256, 256, 2, 2, 4), GSK_DMA(1, 256, 256, 2, 2, 5), GSK_DMA(1, 256, 128, 2, 2, 4),
+    GSK_DMA(1, 256, 128, 4, 2, 4), GSK_DMA(1, 128, 256, 2, 2, 4), GSK_DMA(1, 128, 256, 2, 4, 4),
     GSK_DMA(1, 128, 128, 2, 2, 4),
-    GSK_DMA(2, 256, 256, 2, 2, 4), GSK_DMA(2, 256, 256, 2, 4, 4), GSK_DMA(2, 256, 256, 4, 2, 4),
-    GSK_DMA(2, 256, 256, 2, 2, 5), GSK_DMA(2, 256, 128, 2, 2, 4), GSK_DMA(2, 128, 256, 2, 2, 4),
+    GSK_DMA(2, 256, 256, 4, 2, 4), GSK_DMA(2, 256, 256, 4, 2, 5), GSK_DMA(2, 256, 256, 2, 4, 4),
+    GSK_DMA(2, 256, 256, 2, 2, 4), GSK_DMA(2, 256, 256, 2, 2, 5), GSK_DMA(2, 256, 128, 2, 2, 4),
+    GSK_DMA(2, 256, 128, 4, 2, 4), GSK_DMA(2, 128, 256, 2, 2, 4), GSK_DMA(2, 128, 256, 2, 4, 4),
     GSK_DMA(2, 128, 128, 2, 2, 4),
-    GSK_STAGED(1, 256, 256, 2, 2), GSK_STAGED(1, 256, 256, 4, 2), GSK_STAGED(1, 128, 128, 2, 2),
+    GSK_STAGED(1, 256, 256, 4, 2), GSK_STAGED(1, 256, 256, 2, 2), GSK_STAGED(1, 128, 128, 2, 2),
     GSK_STAGED(1, 64, 64, 2, 2),
-    GSK_STAGED(2, 256, 256, 2, 2), GSK_STAGED(2, 128, 128, 2, 2), GSK_STAGED(2, 64, 64, 2, 2),
+    GSK_STAGED(2, 256, 256, 4, 2), GSK_STAGED(2, 256, 256, 2, 2), GSK_STAGED(2, 128, 128, 2, 2),
+    GSK_STAGED(2, 64, 64, 2, 2),
     GSK_STAGED(0, 128, 128, 2, 2), GSK_STAGED(0, 64, 64, 2, 2),
 };
 

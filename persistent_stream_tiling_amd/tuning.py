@@ -11,9 +11,20 @@ _DEFAULTS = {
     "bf16": dict(bm=256, bn=256),
 }
 
-# workload name -> schedule -> tiles; anything missing falls back to the dtype default
+# workload name -> schedule -> tiles; anything missing falls back to the dtype
+# default.  Chosen from a sweep of tile shapes, wave grids and ring depths on
+# MI355X (best mean time per schedule).
 BENCH_TILES = {
+    # 16 tiles of 64x64 (the configuration names this tile)
     "fp32_256": {s: dict(bm=64, bn=64) for s in SCHEDULES},
+    # 256 tiles of 256x256: exactly one tile per CU
+    "fp16_4096": {s: dict(bm=256, bn=256, stages=5) for s in SCHEDULES},
+    # 144 tiles of 128x128 on 256 CUs (36 at 256x256)
+    "fp16_1536x1536x8192": {s: dict(bm=128, bn=128) for s in SCHEDULES},
+    # 16 tiles of 128x128, each split over 16 workgroups by Stream-K
+    "bf16_512x512x65536": dict(dp=dict(bm=64, bn=64), persistent=dict(bm=64, bn=64),
+                               streamk=dict(bm=128, bn=128), hybrid=dict(bm=128, bn=128)),
+    "bf16_8192x28672x8192": {s: dict(bm=256, bn=256, stages=5) for s in SCHEDULES},
 }
 
 
