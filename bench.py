@@ -33,11 +33,8 @@ def log(msg):
 
 
 def kernel_source_hash():
-    h = hashlib.sha256()
-    for f in ("kernels.hip", "kernels.h", "schedule.h", "api.hip"):
-        with open(os.path.join(ROOT, "persistent_stream_tiling_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
+    from persistent_stream_tiling_amd.profiling import source_hash
+    return source_hash()
 
 
 def workload_table():
@@ -139,6 +136,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--report", default=None, help="also append per-schedule records here")
+    ap.add_argument("--traffic-run", default=None, metavar="SCHEDULE",
+                    help="no timing: run a 256 MiB device copy, then this schedule's GEMM, "
+                         "three times each (for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -163,6 +163,25 @@ def main():
     flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
     flops = 2.0 * M * N * K
     bound = "hbm" if args.workload == "bf16_512x512x65536" else "mfma"
+
+    if args.traffic_run:
+        from persistent_stream_tiling_amd.profiling import COPY_BYTES
+        src = torch.ones(COPY_BYTES, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        tiles = tuning.bench_tiles(args.workload, args.traffic_run, dt)
+        plan = gsk.GemmPlan(M, N, K, dt, args.traffic_run, **tiles)
+        ws = plan.new_workspace()
+        for _ in range(3):
+            flush.zero_()
+            dst.copy_(src)
+        for _ in range(3):
+            flush.zero_()
+            plan.run(a, b, c, ws)
+        torch.cuda.synchronize()
+        alg = algorithmic_bytes(M, N, K, dt, plan.info) + 2 * partial_bytes(plan)
+        print(json.dumps({"traffic_run": args.workload, "schedule": args.traffic_run,
+                          "algorithmic_bytes": alg, "plan": plan.describe()}), flush=True)
+        return
 
     results = {}
     for sched in args.schedules.split(","):

@@ -1,0 +1,143 @@
+"""Turn rocprofv3 CSV output of bench.py runs into the short summaries kept
+under profiles/ (kernel-time table, HBM traffic per launch).
+
+  python -m persistent_stream_tiling_amd.profiling trace  --csv DIR --out FILE --cmd "..."
+  python -m persistent_stream_tiling_amd.profiling traffic --fetch DIR --write DIR \
+        --workload NAME --schedule NAME --out profiles/traffic.json --cmd "..."
+
+`trace` reads a --kernel-trace --stats run of `bench.py` and reports, per
+schedule, the mean duration of the GEMM kernel over the timed steps (the
+bench runs the schedules one after the other: warm-up launches, then the
+timed ones).  `traffic` reads two --pmc runs of `bench.py --traffic-run`
+(FETCH_SIZE, then WRITE_SIZE), calibrates each counter against the plain
+device copy of known size that run performs first, and stores the GEMM
+kernel's HBM bytes per launch.
+"""
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import statistics
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+COPY_BYTES = 256 << 20  # the copy in bench.py --traffic-run (read and written once)
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in ("kernels.hip", "kernels.h", "schedule.h", "api.hip"):
+        with open(os.path.join(ROOT, "persistent_stream_tiling_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _find(dirname, suffix):
+    hits = sorted(glob.glob(os.path.join(dirname, "**", "*" + suffix), recursive=True))
+    if not hits:
+        raise FileNotFoundError(f"no *{suffix} under {dirname}")
+    return hits[0]
+
+
+def _is_gemm(name):
+    return "gsk::gemm_kernel" in name
+
+
+def trace_summary(csv_dir, schedules, warmup, steps, cmd):
+    rows = list(csv.DictReader(open(_find(csv_dir, "kernel_trace.csv"))))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    gemm = [r for r in rows if _is_gemm(r["Kernel_Name"])]
+    per = warmup + steps
+    lines = [f"# rocprofv3 kernel trace: `{cmd}`", "",
+             f"Kernel source hash: {source_hash()}", "",
+             "| schedule | kernel | launches | mean us (timed steps) | min us | max us |",
+             "|---|---|---|---|---|---|"]
+    out = {}
+    for i, s in enumerate(schedules):
+        block = gemm[i * per:(i + 1) * per]
+        timed = block[warmup:]
+        if not timed:
+            break
+        d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in timed]
+        name = timed[0]["Kernel_Name"].split("(")[0].replace("void ", "")
+        out[s] = statistics.mean(d)
+        lines.append(f"| {s} | `{name}` | {len(timed)} | {statistics.mean(d):.2f} | "
+                     f"{min(d):.2f} | {max(d):.2f} |")
+    stats_path = glob.glob(os.path.join(csv_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if stats_path:
+        lines += ["", "rocprofv3 --stats (all launches of each kernel symbol, warm-ups included):",
+                  "", "| kernel | calls | average us | percent |", "|---|---|---|---|"]
+        for r in csv.DictReader(open(stats_path[0])):
+            lines.append(f"| `{r['Name'][:80]}` | {r['Calls']} | "
+                         f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} |")
+    return "\n".join(lines) + "\n", out
+
+
+def _counter_per_dispatch(csv_dir, counter):
+    rows = list(csv.DictReader(open(_find(csv_dir, "counter_collection.csv"))))
+    vals = {}
+    for r in rows:
+        if r["Counter_Name"] != counter:
+            continue
+        vals.setdefault(int(r["Dispatch_Id"]), [r["Kernel_Name"], 0.0])
+        vals[int(r["Dispatch_Id"])][1] += float(r["Counter_Value"])
+    return [vals[k] for k in sorted(vals)]
+
+
+def traffic(fetch_dir, write_dir):
+    res = {}
+    for key, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
+        disp = _counter_per_dispatch(d, counter)
+        copies = [v for n, v in disp if not _is_gemm(n) and "copy" in n.lower()]
+        gemms = [v for n, v in disp if _is_gemm(n)]
+        if not copies or not gemms:
+            raise RuntimeError(f"{counter}: need copy and gemm dispatches, got {[n for n, _ in disp]}")
+        kib_copy = statistics.median(copies)
+        factor = COPY_BYTES / (kib_copy * 1024.0)     # true bytes per counted byte
+        res[key] = {"copy_kib": kib_copy, "factor": factor,
+                    "gemm_kib": statistics.median(gemms),
+                    "gemm_bytes": statistics.median(gemms) * 1024.0 * factor}
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd_name", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("--csv", required=True)
+    t.add_argument("--out", required=True)
+    t.add_argument("--cmd", required=True)
+    t.add_argument("--schedules", default="dp,persistent,streamk,hybrid")
+    t.add_argument("--warmup", type=int, default=5)
+    t.add_argument("--steps", type=int, default=20)
+    f = sub.add_parser("traffic")
+    f.add_argument("--fetch", required=True)
+    f.add_argument("--write", required=True)
+    f.add_argument("--workload", required=True)
+    f.add_argument("--schedule", required=True)
+    f.add_argument("--algorithmic-bytes", type=float, required=True)
+    f.add_argument("--out", required=True)
+    f.add_argument("--cmd", required=True)
+    a = ap.parse_args()
+    if a.cmd_name == "trace":
+        text, _ = trace_summary(a.csv, a.schedules.split(","), a.warmup, a.steps, a.cmd)
+        open(a.out, "w").write(text)
+        print(text)
+    else:
+        r = traffic(a.fetch, a.write)
+        table = json.load(open(a.out)) if os.path.exists(a.out) else {}
+        total = r["fetch"]["gemm_bytes"] + r["write"]["gemm_bytes"]
+        table[f"{a.workload}/{a.schedule}"] = {
+            "bytes_per_launch": total, "fetch_bytes": r["fetch"]["gemm_bytes"],
+            "write_bytes": r["write"]["gemm_bytes"],
+            "fetch_calibration": r["fetch"]["factor"], "write_calibration": r["write"]["factor"],
+            "algorithmic_bytes": a.algorithmic_bytes,
+            "traffic_over_algorithmic": total / a.algorithmic_bytes,
+            "source_hash": source_hash(), "command": a.cmd}
+        json.dump(table, open(a.out, "w"), indent=1, sort_keys=True)
+        print(json.dumps(table[f"{a.workload}/{a.schedule}"], indent=1))
+
+
+if __name__ == "__main__":
+    main()
