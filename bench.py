@@ -96,7 +96,7 @@ def cpu_baseline(a_bits, b_bits, M, N, K, dtype, seed, target_s):
     from persistent_stream_tiling_amd import inputs
     threads = oracle.default_threads()
     # calibrate on a small sample, then size the timed sample to ~target_s
-    rows, cols = inputs.sample_positions(M, N, threads * 4, seed=seed)
+    rows, cols = inputs.sample_positions(M, N, threads * 256, seed=seed)
     t = time.perf_counter()
     oracle.gemm_sampled(a_bits, b_bits, dtype, rows, cols, threads)
     per = (time.perf_counter() - t) / rows.size
