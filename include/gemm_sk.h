@@ -31,8 +31,10 @@
  * "owner") waits for the others, which each store their fp32 partial tile in
  * a workspace slot and raise a flag; the owner adds the partials to its own
  * accumulator one by one in ascending workgroup order (= ascending k) and
- * writes C.  There are no floating-point atomics, so one plan gives bitwise
- * identical C on every run.  Different schedules may differ in the last bits.
+ * writes C.  For tiles cut into many pieces the same sums can instead be
+ * spread over all of the tile's workgroups (GEMM_FLAG_FIXUP_SPLIT).  There are
+ * no floating-point atomics, so one plan gives bitwise identical C on every
+ * run.  Different schedules may differ in the last bits.
  *
  * Layout.  A is M x K row-major (leading dimension K), B is K x N row-major
  * (leading dimension N), C is M x N fp32 row-major (leading dimension N).  A, B
@@ -72,7 +74,17 @@ enum {
     GEMM_FLAG_NO_XCD_REMAP = 1u << 1,
     /* fp16/bf16: use the kernel that stages A and B through registers (bk 64)
      * instead of the direct-to-LDS ring kernel (bk 32). */
-    GEMM_FLAG_REGISTER_STAGED = 1u << 2
+    GEMM_FLAG_REGISTER_STAGED = 1u << 2,
+    /* Stream-K fixup mode (default: split when some tile is cut into three or
+     * more pieces, else head-adds):
+     *  HEAD  the workgroup holding a split tile's k = 0 adds the other pieces
+     *        one by one and stores the tile;
+     *  SPLIT every piece is parked in the workspace; after their MAC work the
+     *        tile's workgroups each add up and store a share of its blocks.
+     * Both add the pieces of every element in ascending k order, so they give
+     * identical bits. */
+    GEMM_FLAG_FIXUP_HEAD = 1u << 3,
+    GEMM_FLAG_FIXUP_SPLIT = 1u << 4
 };
 
 /* Tile and schedule knobs.  Every field 0 means "default". */
@@ -159,6 +171,8 @@ typedef struct {
     int32_t wave_m, wave_n;
     int32_t kernel_kind;  /* 0 register-staged, 1 direct-to-LDS ring */
     int32_t stages;
+    int32_t split_fixup;  /* 1 when the Stream-K fixup is split (see flags) */
+    int32_t max_pieces;   /* most workgroups sharing one Stream-K tile */
     int32_t tiles_m, tiles_n;
     int32_t tiles;        /* T */
     int32_t iters_per_tile; /* ipt = ceil(K / bk) */

@@ -10,6 +10,8 @@ DP, PERSISTENT, STREAMK, HYBRID = 0, 1, 2, 3
 FLAG_ONE_TILE = 1 << 0
 FLAG_NO_XCD_REMAP = 1 << 1
 FLAG_REGISTER_STAGED = 1 << 2
+FLAG_FIXUP_HEAD = 1 << 3
+FLAG_FIXUP_SPLIT = 1 << 4
 ROLE_FULL, ROLE_CONTRIB, ROLE_OWNER = 0, 1, 2
 
 SCHEDULES = {"dp": DP, "persistent": PERSISTENT, "streamk": STREAMK, "hybrid": HYBRID}
@@ -34,6 +36,7 @@ class PlanInfo(ctypes.Structure):
                 ("group_m", ctypes.c_int32), ("flags", ctypes.c_uint32),
                 ("wave_m", ctypes.c_int32), ("wave_n", ctypes.c_int32),
                 ("kernel_kind", ctypes.c_int32), ("stages", ctypes.c_int32),
+                ("split_fixup", ctypes.c_int32), ("max_pieces", ctypes.c_int32),
                 ("tiles_m", ctypes.c_int32), ("tiles_n", ctypes.c_int32),
                 ("tiles", ctypes.c_int32), ("iters_per_tile", ctypes.c_int32),
                 ("tiles_sk", ctypes.c_int32), ("tiles_dp", ctypes.c_int32),

@@ -28,8 +28,9 @@ struct gemm_plan {
     int device;                // HIP device ordinal, -1 for a described device
     int pack_a, pack_b;
     int64_t lda, ldb;          // leading dimensions the kernel reads (packed or not)
-    size_t off_flags, off_partials, off_pack_a, off_pack_b, ws_size;
+    size_t off_flags, off_counters, off_partials, off_pack_a, off_pack_b, ws_size;
     int32_t spin_limit;
+    int split_fixup, max_pieces;
 };
 
 namespace {
@@ -216,11 +217,6 @@ gemm_plan *create(int64_t M, int64_t N, int64_t K, gemm_dtype dtype, gemm_schedu
     if (T_sk > 0) {
         P.q = (int32_t)(p->iters_sk / g);
         P.r = (int32_t)(p->iters_sk % g);
-        if ((int64_t)g * var->bm * var->bn * 4 >= ((int64_t)1 << 31)) {
-            set_error("Stream-K grid %d too large for the partial-tile workspace indexing", g);
-            delete p;
-            return nullptr;
-        }
         if (g > p->wg_capacity) {
             set_error("Stream-K grid %d exceeds the %d workgroups that can be resident at once; "
                       "the fixup needs them all running together",
@@ -228,22 +224,50 @@ gemm_plan *create(int64_t M, int64_t N, int64_t K, gemm_dtype dtype, gemm_schedu
             delete p;
             return nullptr;
         }
+        // Fixup mode: split when some tile is cut into three or more pieces.
+        p->max_pieces = 1;
+        for (int32_t t = 0; t < P.T_sk; ++t) {
+            int32_t f, l;
+            tile_workers(P, t, &f, &l);
+            if (l - f + 1 > p->max_pieces)
+                p->max_pieces = l - f + 1;
+        }
+        if (t.flags & GEMM_FLAG_FIXUP_SPLIT)
+            p->split_fixup = 1;
+        else if (t.flags & GEMM_FLAG_FIXUP_HEAD)
+            p->split_fixup = 0;
+        else
+            p->split_fixup = p->max_pieces >= 3;
+        const int64_t slots = p->split_fixup ? 2 * (int64_t)g : g;
+        if (slots * var->bm * var->bn * 4 >= ((int64_t)1 << 31)) {
+            set_error("Stream-K grid %d too large for the partial-tile workspace indexing", g);
+            delete p;
+            return nullptr;
+        }
     } else {
         P.q = P.r = 0;
+        p->max_pieces = 1;
+        p->split_fixup = 0;
     }
 
-    // Workspace: [status word | flags (g) | partial tiles (g slots) | packed A | packed B]
+    // Workspace: [status word | flags | per-tile counters (split fixup) |
+    //             partial tiles | packed A | packed B]; head fixup: one flag and
+    //             slot per workgroup, split fixup: two of each.
     p->pack_a = lda != K && M > 0 && K > 0;
     p->pack_b = ldb != N && N > 0 && K > 0;
     p->lda = lda;
     p->ldb = ldb;
     size_t off = 0;
     if (T_sk > 0) {
+        const size_t slots = p->split_fixup ? 2 * (size_t)g : (size_t)g;
         off = 256;
         p->off_flags = off;
-        off = align_up(off + sizeof(int32_t) * (size_t)g, 256);
+        off = align_up(off + sizeof(int32_t) * slots, 256);
+        p->off_counters = off;
+        if (p->split_fixup)
+            off = align_up(off + sizeof(int32_t) * (size_t)T_sk, 256);
         p->off_partials = off;
-        off += sizeof(float) * (size_t)g * var->bm * var->bn;
+        off += sizeof(float) * slots * var->bm * var->bn;
     }
     if (p->pack_a) {
         off = align_up(off, 256);
@@ -332,6 +356,8 @@ int gemm_plan_get_info(const gemm_plan *p, gemm_plan_info *o)
     o->wave_n = p->variant->wave_n;
     o->kernel_kind = p->variant->kind;
     o->stages = p->variant->stages;
+    o->split_fixup = p->split_fixup;
+    o->max_pieces = p->max_pieces;
     o->tiles_m = p->P.tiles_m;
     o->tiles_n = p->P.tiles_n;
     o->tiles = p->P.T;
@@ -363,7 +389,8 @@ int gemm_plan_describe(const gemm_plan *p, char *buf, size_t len)
     return snprintf(buf, buf ? len : 0,
                     "M,N,K=%lld,%lld,%lld %s %s tile=%dx%dx%d waves=%dx%d %s%d group_m=%d | tiles %dx%d=%d "
                     "ipt=%d | T_sk=%d T_dp=%d I_sk=%lld g=%d q=%d r=%d | grid=%d x %d threads, "
-                    "lds=%zu B, capacity=%d wg, xcds=%d | pack A=%d B=%d | workspace=%zu B",
+                    "lds=%zu B, capacity=%d wg, xcds=%d | fixup=%s pieces<=%d | pack A=%d B=%d | "
+                    "workspace=%zu B",
                     (long long)p->M, (long long)p->N, (long long)p->K, dtype_name(p->dtype),
                     sched_name(p->schedule), p->bm, p->bn, p->bk, p->variant->wave_m,
                     p->variant->wave_n, p->variant->kind ? "ring" : "staged",
@@ -371,7 +398,8 @@ int gemm_plan_describe(const gemm_plan *p, char *buf, size_t len)
                     p->P.tiles_n, p->P.T, p->P.ipt, p->P.T_sk, p->P.T - p->P.T_sk,
                     (long long)p->iters_sk, p->P.g, p->P.q, p->P.r, p->P.grid,
                     p->variant->threads, p->variant->lds_bytes, p->wg_capacity, p->xcds,
-                    p->pack_a, p->pack_b, p->ws_size);
+                    p->P.T_sk == 0 ? "none" : (p->split_fixup ? "split" : "head"),
+                    p->max_pieces, p->pack_a, p->pack_b, p->ws_size);
 }
 
 int gemm_plan_segments(const gemm_plan *p, int32_t wg, gemm_segment *out, int32_t max)
@@ -480,6 +508,8 @@ int gemm_run(const gemm_plan *p, const void *A, const void *B, float *C, void *w
     args.status = p->P.T_sk > 0 ? (int32_t *)ws : nullptr;
     args.flags = p->P.T_sk > 0 ? (int32_t *)(ws + p->off_flags) : nullptr;
     args.partials = p->P.T_sk > 0 ? (float *)(ws + p->off_partials) : nullptr;
+    args.counters = p->P.T_sk > 0 ? (int32_t *)(ws + p->off_counters) : nullptr;
+    args.split_fixup = p->split_fixup;
     args.M = (int32_t)p->M;
     args.N = (int32_t)p->N;
     args.K = (int32_t)p->K;

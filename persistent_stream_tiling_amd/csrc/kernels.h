@@ -15,9 +15,13 @@ struct KernelArgs {
     const uint8_t *A;      // M x lda elements, row-major, 16-byte aligned rows
     const uint8_t *B;      // K x ldb elements, row-major, 16-byte aligned rows
     float *C;              // M x ldc floats
-    float *partials;       // Stream-K partial tiles: one bm*bn slot per workgroup
-    int32_t *flags;        // one "partial ready" flag per workgroup (0 between runs)
+    float *partials;       // Stream-K partial tiles: bm*bn floats per slot
+    int32_t *flags;        // one "partial ready" flag per slot (0 between runs)
+    int32_t *counters;     // split fixup: readers done per split tile (0 between runs)
     int32_t *status;       // workspace status word (1 = a fixup wait gave up)
+    int32_t split_fixup;   // 0: the head's workgroup adds every partial;
+                           // 1: every piece is parked and the tile's workgroups
+                           //    each reduce a share of its blocks
     int32_t M, N, K;
     int32_t lda, ldb, ldc; // leading dimensions in elements
     int32_t c_vec;         // 1: C rows allow 16-byte stores

@@ -41,6 +41,12 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr uint32_t kOutOfRange = 0x80000000u;
+// Cache-policy operand of a buffer access that is coherent at agent scope
+// (sc1): it neither hits a stale copy in this die's L2 nor leaves its write
+// there.  Stream-K partials and flags cross dies through these, so the fixup
+// needs no whole-L2 write-back or invalidate (an agent-scope fence costs every
+// workgroup on the die its cached operand tiles).
+constexpr int kAgentCoherent = 16;
 // Buffer descriptor word 3 for gfx9-family raw (untyped, stride 0) buffers.
 constexpr int kRsrcWord3 = 0x00020000;
 
@@ -183,6 +189,19 @@ __device__ __forceinline__ void store_block(const f32x16 &blk, const KernelArgs 
     }
 }
 
+// Wait (thread 0) until flags[slot] is set; bounded, see spin_limit.
+__device__ __forceinline__ void wait_flag(const KernelArgs &args, int32_t slot)
+{
+    int spins = 0;
+    while (__hip_atomic_load(args.flags + slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
+        if (++spins > args.spin_limit) {
+            __hip_atomic_store(args.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+    }
+}
+
 // Finish one unit of work: a Stream-K tail is parked in the workgroup's
 // partial slot and signalled; a split tile's head waits for its later
 // workgroups and adds their partials; then the tile is stored to C.
@@ -203,9 +222,14 @@ __device__ __forceinline__ void finish_tile(f32x16 (&acc)[MT][NT], const KernelA
     const int tid = threadIdx.x;
     const int half = lane >> 5, l32 = lane & 31;
     const uint32_t lane_off = (uint32_t)lane * 16;
-    if (w.role == ROLE_CONTRIB) {
-        // Tail of a split tile: park it in this workgroup's slot, then signal.
-        const __amdgpu_buffer_rsrc_t slot = make_rsrc(args.partials + (int64_t)p * (BM * BN));
+    if (w.role == ROLE_CONTRIB || (w.role == ROLE_OWNER && args.split_fixup)) {
+        // A piece of a split tile: park it in this workgroup's slot, then
+        // signal.  (With the split fixup the head piece is parked too, and the
+        // tile's workgroups reduce it together after their MAC work.)
+        const int32_t slot_id =
+            args.split_fixup ? split_slot(p, w.role == ROLE_OWNER) : p;
+        const __amdgpu_buffer_rsrc_t slot =
+            make_rsrc(args.partials + (int64_t)slot_id * (BM * BN));
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -217,12 +241,15 @@ __device__ __forceinline__ void finish_tile(f32x16 (&acc)[MT][NT], const KernelA
                                           bits_of(acc[mt][nt][4 * g + 1]),
                                           bits_of(acc[mt][nt][4 * g + 2]),
                                           bits_of(acc[mt][nt][4 * g + 3])};
-                    __builtin_amdgcn_raw_buffer_store_b128(u, slot, (int)lane_off, f * 1024, 0);
+                    __builtin_amdgcn_raw_buffer_store_b128(u, slot, (int)lane_off, f * 1024,
+                                                           kAgentCoherent);
                 }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        // every lane's coherent stores have completed before the flag goes up
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         if (tid == 0)
-            __hip_atomic_store(args.flags + p, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(args.flags + slot_id, 1, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
         return;
     }
     const __amdgpu_buffer_rsrc_t c_rsrc = make_rsrc(args.C + (int64_t)m0 * args.ldc);
@@ -231,22 +258,14 @@ __device__ __forceinline__ void finish_tile(f32x16 (&acc)[MT][NT], const KernelA
         // then add their partials in ascending workgroup (= ascending k) order.
         if (tid == 0) {
             for (int q = p + 1; q <= w.peer_last; ++q) {
-                int spins = 0;
-                while (__hip_atomic_load(args.flags + q, __ATOMIC_ACQUIRE,
-                                         __HIP_MEMORY_SCOPE_AGENT) == 0) {
-                    if (++spins > args.spin_limit) {
-                        __hip_atomic_store(args.status, 1, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-                        break;
-                    }
-                    __builtin_amdgcn_s_sleep(2);
-                }
+                wait_flag(args, q);
                 // Consumed: leave the flag clear for the next run.
                 __hip_atomic_store(args.flags + q, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
+        // the partials are read below with agent-coherent loads issued after
+        // the flags were seen
         __syncthreads();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         // Block by block: add the peers' partials in ascending order, store.
         const __amdgpu_buffer_rsrc_t slots = make_rsrc(args.partials);
 #pragma unroll
@@ -262,7 +281,7 @@ __device__ __forceinline__ void finish_tile(f32x16 (&acc)[MT][NT], const KernelA
                     for (int g = 0; g < 4; ++g) {
                         const f32x4 v = __builtin_bit_cast(
                             f32x4, __builtin_amdgcn_raw_buffer_load_b128(slots, (int)off,
-                                                                         g * 1024, 0));
+                                                                         g * 1024, kAgentCoherent));
                         blk[4 * g] += v[0];
                         blk[4 * g + 1] += v[1];
                         blk[4 * g + 2] += v[2];
@@ -280,6 +299,84 @@ __device__ __forceinline__ void finish_tile(f32x16 (&acc)[MT][NT], const KernelA
         for (int nt = 0; nt < NT; ++nt)
             store_block(acc[mt][nt], args, c_rsrc, m0, n0, row0 + mt * 32 + l32, col0 + nt * 32,
                         half);
+}
+
+// Split fixup, after the workgroup's MAC work: for each split tile it took
+// part in, reduce its share of the tile's 32x32 blocks.  Every element adds
+// the pieces in ascending k order (head piece first), which is the order the
+// head's workgroup would use, so the result does not depend on who reduces.
+// The last workgroup to finish with a tile clears its flags and counter.
+// Blocks are numbered in the writer's fragment order (wave, mt, nt).
+template <int BM, int BN, int WM, int WN>
+__device__ __forceinline__ void reduce_split_tiles(const KernelArgs &args, int p, int wave,
+                                                   int lane)
+{
+    constexpr int WTM = BM / WM, WTN = BN / WN, MT = WTM / 32, NT = WTN / 32;
+    constexpr int NW = WM * WN, NBLK = NW * MT * NT;
+    const Partition &P = args.P;
+    const int tid = threadIdx.x, half = lane >> 5, l32 = lane & 31;
+    int32_t tiles[2];
+    const int ntiles = split_tiles_of(P, p, tiles);
+    for (int it = 0; it < ntiles; ++it) {
+        const int32_t t = tiles[it];
+        int32_t pf, pl;
+        tile_workers(P, t, &pf, &pl);
+        const int32_t parts = pl - pf + 1;
+        int32_t b0, b1;
+        split_share(p - pf, parts, NBLK, &b0, &b1);
+        if (tid == 0)
+            for (int32_t q = pf; q <= pl; ++q)
+                wait_flag(args, split_slot(q, q == pf));
+        __syncthreads();
+        int tm, tn;
+        tile_coords(P, t, &tm, &tn);
+        const int m0 = tm * BM, n0 = tn * BN;
+        const __amdgpu_buffer_rsrc_t c_rsrc = make_rsrc(args.C + (int64_t)m0 * args.ldc);
+        const __amdgpu_buffer_rsrc_t slots = make_rsrc(args.partials);
+        const uint32_t slot_bytes = (uint32_t)(BM * BN * 4);
+        for (int b = b0 + wave; b < b1; b += NW) {
+            const int ww = b / (MT * NT), mt = (b / NT) % MT, nt = b % NT;
+            const uint32_t frag_off = (uint32_t)(b * 4 * 64 + lane) * 16;
+            f32x16 blk;
+            for (int32_t q = pf; q <= pl; ++q) {
+                const uint32_t off = (uint32_t)split_slot(q, q == pf) * slot_bytes + frag_off;
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const f32x4 v = __builtin_bit_cast(
+                        f32x4, __builtin_amdgcn_raw_buffer_load_b128(slots, (int)off, g * 1024,
+                                                                     kAgentCoherent));
+                    if (q == pf) {
+                        blk[4 * g] = v[0];
+                        blk[4 * g + 1] = v[1];
+                        blk[4 * g + 2] = v[2];
+                        blk[4 * g + 3] = v[3];
+                    } else {
+                        blk[4 * g] += v[0];
+                        blk[4 * g + 1] += v[1];
+                        blk[4 * g + 2] += v[2];
+                        blk[4 * g + 3] += v[3];
+                    }
+                }
+            }
+            store_block(blk, args, c_rsrc, m0, n0, (ww / WN) * WTM + mt * 32 + l32,
+                        (ww % WN) * WTN + nt * 32, half);
+        }
+        // this workgroup's reads of the tile's slots are complete (their values
+        // are already summed) before it counts itself done
+        __syncthreads();
+        if (tid == 0) {
+            const int32_t done = __hip_atomic_fetch_add(args.counters + t, 1, __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_AGENT);
+            if (done == parts - 1) {
+                // every reader of this tile is finished: leave it clean for the next run
+                for (int32_t q = pf; q <= pl; ++q)
+                    __hip_atomic_store(args.flags + split_slot(q, q == pf), 0, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(args.counters + t, 0, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    }
 }
 
 template <int DT, int BM, int BN, int WM, int WN>
@@ -438,6 +535,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(KernelArgs args)
         finish_tile<BM, BN, MT, NT>(acc, args, w, p, m0, n0, wave, lane,
                                     wy * Cfg::WTM, wx * Cfg::WTN);
     }
+    if (args.split_fixup)
+        reduce_split_tiles<BM, BN, WM, WN>(args, p, wave, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -728,6 +827,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel_dma(KernelArgs ar
         finish_tile<BM, BN, MT, NT>(acc, args, w, p, m0, n0, wave, lane, wy * Cfg::WTM,
                                     wx * Cfg::WTN);
     }
+    if (args.split_fixup)
+        reduce_split_tiles<BM, BN, WM, WN>(args, p, wave, lane);
 }
 
 template <int DT, int BM, int BN, int WM, int WN>

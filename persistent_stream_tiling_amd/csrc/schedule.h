@@ -161,4 +161,48 @@ GSK_HD bool work_next(const Partition &P, int32_t p, WorkCursor &c, WorkItem &w)
     return false;
 }
 
+// Workgroups [*first, *last] share Stream-K tile t (t < T_sk); they are
+// more than one exactly when the tile is split.
+GSK_HD void tile_workers(const Partition &P, int32_t t, int32_t *first, int32_t *last)
+{
+    *first = sk_wg_of_iter(P, (int64_t)t * P.ipt);
+    *last = sk_wg_of_iter(P, (int64_t)t * P.ipt + P.ipt - 1);
+}
+
+// Workspace slot of workgroup p's piece of a split tile: a piece that starts
+// inside the tile (always the workgroup's first segment) uses slot 2p, the
+// head piece (k = 0, always the workgroup's last segment) slot 2p + 1.
+GSK_HD int32_t split_slot(int32_t p, bool head) { return 2 * p + (head ? 1 : 0); }
+
+// Split tiles workgroup p took part in (at most two: the tile its range
+// starts in and the tile it ends in); returns how many were written.
+GSK_HD int split_tiles_of(const Partition &P, int32_t p, int32_t out[2])
+{
+    int n = 0;
+    if (P.T_sk <= 0 || p >= P.g)
+        return 0;
+    const int64_t b = sk_begin(P, p), e = sk_begin(P, p + 1);
+    if (b >= e)
+        return 0;
+    const int32_t t0 = (int32_t)(b / P.ipt), t1 = (int32_t)((e - 1) / P.ipt);
+    int32_t f, l;
+    tile_workers(P, t0, &f, &l);
+    if (f != l)
+        out[n++] = t0;
+    if (t1 != t0) {
+        tile_workers(P, t1, &f, &l);
+        if (f != l)
+            out[n++] = t1;
+    }
+    return n;
+}
+
+// Share of blocks [*b0, *b1) of a split tile (nblocks 32x32 blocks) reduced
+// by the i-th of its n workgroups.
+GSK_HD void split_share(int32_t i, int32_t n, int32_t nblocks, int32_t *b0, int32_t *b1)
+{
+    *b0 = (int32_t)((int64_t)i * nblocks / n);
+    *b1 = (int32_t)((int64_t)(i + 1) * nblocks / n);
+}
+
 }  // namespace gsk

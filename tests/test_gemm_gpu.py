@@ -85,11 +85,70 @@ def test_stream_k_long_k_integer_exact():
     rows, cols = inputs.sample_positions(M, N, 2048, seed=6, tails=True)
     ref, _ = oracle.gemm_sampled(a, b, "bf16", rows, cols)
     da, db = to_device(a, "bf16"), to_device(b, "bf16")
+    import persistent_stream_tiling_amd as gsk
     for tiles in (dict(bm=128, bn=128), dict(bm=64, bn=64), dict(bm=256, bn=256)):
         for g in (256, 100, 3):
-            plan, _, c = run_gemm(da, db, M, N, K, "bf16", "streamk", grid=g, **tiles)
-            got = c.cpu().numpy()[rows, cols]
-            compare(got, ref, None, "bf16", exact=True, what=plan.describe())
+            for flag in (gsk.FLAG_FIXUP_HEAD, gsk.FLAG_FIXUP_SPLIT):
+                plan, _, c = run_gemm(da, db, M, N, K, "bf16", "streamk", grid=g, flags=flag,
+                                      **tiles)
+                got = c.cpu().numpy()[rows, cols]
+                compare(got, ref, None, "bf16", exact=True, what=plan.describe())
+
+
+@pytest.mark.parametrize("tiles", [dict(bm=128, bn=128), dict(bm=256, bn=256), dict(bm=64, bn=64)],
+                         ids=lambda t: f"{t['bm']}x{t['bn']}")
+def test_split_and_head_fixups_agree_bitwise(tiles):
+    # both fixups add every element's pieces in ascending k order
+    M, N, K = 512, 384, 16384
+    a, b = inputs.operands(M, N, K, "bf16", "normal", seed=21)
+    da, db = to_device(a, "bf16"), to_device(b, "bf16")
+    import persistent_stream_tiling_amd as gsk
+    outs = {}
+    for name, flag in (("head", gsk.FLAG_FIXUP_HEAD), ("split", gsk.FLAG_FIXUP_SPLIT)):
+        plan, ws, c = run_gemm(da, db, M, N, K, "bf16", "streamk", flags=flag, **tiles)
+        assert plan.info["max_pieces"] >= 2
+        assert plan.workspace_status(ws) == 0
+        # flags and counters are left zero for the next run
+        g = plan.info["g"]
+        slots = 2 * g if plan.info["split_fixup"] else g
+        flags_end = 256 + 4 * slots
+        wsn = ws.cpu().numpy()
+        assert not wsn[256:flags_end].any()
+        if plan.info["split_fixup"]:
+            counters = (flags_end + 255) // 256 * 256
+            assert not wsn[counters:counters + 4 * plan.info["tiles_sk"]].any()
+        outs[name] = c.cpu().numpy()
+        # and a second run on the same workspace gives the same bits
+        c2 = torch.empty_like(c)
+        plan.run(da, db, c2, ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(c2.cpu().numpy().view(np.uint32), outs[name].view(np.uint32))
+    assert np.array_equal(outs["head"].view(np.uint32), outs["split"].view(np.uint32))
+    rows, cols = inputs.sample_positions(M, N, 512, seed=1)
+    ref, scale = oracle.gemm_sampled(a, b, "bf16", rows, cols)
+    compare(outs["split"][rows, cols], ref, scale, "bf16", what="split fixup")
+
+
+@pytest.mark.parametrize("fixup", ["head", "split"])
+def test_workspace_reuse_with_new_inputs(fixup):
+    # partial slots are reused run after run; a stale copy of a slot in some
+    # die's L2 would show up as a wrong result on the next run's new inputs
+    import persistent_stream_tiling_amd as gsk
+    flag = gsk.FLAG_FIXUP_HEAD if fixup == "head" else gsk.FLAG_FIXUP_SPLIT
+    M, N, K = 384, 512, 12288
+    plan = gsk.GemmPlan(M, N, K, "f16", "streamk", bm=128, bn=128, flags=flag)
+    assert plan.info["max_pieces"] >= 3
+    ws = plan.new_workspace()
+    rows, cols = inputs.sample_positions(M, N, 1024, seed=2)
+    for seed in (31, 32, 33, 34):
+        a, b = inputs.operands(M, N, K, "f16", "int4", seed=seed)
+        ref, _ = oracle.gemm_sampled(a, b, "f16", rows, cols)
+        c = torch.full((M, N), float("nan"), device="cuda")
+        plan.run(to_device(a, "f16"), to_device(b, "f16"), c, ws)
+        torch.cuda.synchronize()
+        compare(c.cpu().numpy()[rows, cols], ref, None, "f16", exact=True,
+                what=f"{fixup} seed {seed}")
+        assert plan.workspace_status(ws) == 0
 
 
 @pytest.mark.parametrize("schedule", ["streamk", "hybrid"])

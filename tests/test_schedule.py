@@ -255,3 +255,34 @@ def test_irregular_shape_list_is_reproducible():
     for m, n, k in shapes:
         assert 1000 <= m <= 8192 and 1000 <= n <= 8192 and 1000 <= k <= 16384
         assert m % 128 and n % 128 and k % 128
+
+
+def test_fixup_mode_choice_and_workspace():
+    # 512 x 512 x 65536 at 128^2: 16 tiles, each cut into 16 pieces -> split by default
+    p = plan(512, 512, 65536, "bf16", "streamk", bm=128, bn=128)
+    assert p.info["max_pieces"] == 16 and p.info["split_fixup"] == 1
+    g = p.info["g"]
+    assert p.workspace_bytes >= 256 + 4 * 2 * g + 4 * p.info["tiles_sk"] + 2 * g * 128 * 128 * 4
+    head = plan(512, 512, 65536, "bf16", "streamk", bm=128, bn=128, flags=gsk.FLAG_FIXUP_HEAD)
+    assert head.info["split_fixup"] == 0 and head.workspace_bytes < p.workspace_bytes
+    # second revision's demo: 13 or 12 iterations of 32-iteration tiles -> at most 4 pieces
+    p = plan(256, 512, 2048, "f16", "streamk", bm=64, bn=64, grid=82)
+    assert p.info["max_pieces"] == 4 and p.info["split_fixup"] == 1
+    # whole tiles only: nothing to fix up
+    p = plan(4096, 4096, 4096, "f16", "streamk")
+    assert p.info["max_pieces"] == 1 and p.info["split_fixup"] == 0
+    p = plan(1536, 1536, 8192, "f16", "streamk", bm=128, bn=128, flags=gsk.FLAG_FIXUP_SPLIT)
+    assert p.info["split_fixup"] == 1
+
+
+def test_split_tiles_per_workgroup_at_most_two():
+    # every workgroup takes part in at most two split tiles (its first and
+    # last); the split fixup relies on it for its two slots
+    for (M, N, K, bm, g) in ((1536, 1536, 8192, 256, 256), (512, 512, 65536, 128, 256),
+                             (300, 200, 704, 64, 37), (1000, 1000, 333, 128, 100)):
+        p = plan(M, N, K, "f16", "streamk", bm=bm, bn=bm, grid=g, wg_per_cu=2)
+        for w in range(p.info["launch_grid"]):
+            split = [s for s in p.segments(w) if s[3] != gsk.ROLE_FULL]
+            assert len(split) <= 2
+            if len(split) == 2:
+                assert split[0][3] == gsk.ROLE_CONTRIB and split[1][3] == gsk.ROLE_OWNER
