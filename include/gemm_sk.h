@@ -84,7 +84,12 @@ enum {
      * Both add the pieces of every element in ascending k order, so they give
      * identical bits. */
     GEMM_FLAG_FIXUP_HEAD = 1u << 3,
-    GEMM_FLAG_FIXUP_SPLIT = 1u << 4
+    GEMM_FLAG_FIXUP_SPLIT = 1u << 4,
+    /* fp16/bf16: use the ring kernel that copies A in whole 128-byte rows,
+     * two MAC iterations at a time (kernel_kind 2), instead of one
+     * iteration's 64-byte row halves (kernel_kind 1, the default).  Fewer,
+     * fuller cache-line requests; pays off on long-K Stream-K shapes. */
+    GEMM_FLAG_A_ROW_PAIRS = 1u << 5
 };
 
 /* Tile and schedule knobs.  Every field 0 means "default". */
@@ -169,7 +174,8 @@ typedef struct {
     int32_t bm, bn, bk, group_m;
     uint32_t flags;
     int32_t wave_m, wave_n;
-    int32_t kernel_kind;  /* 0 register-staged, 1 direct-to-LDS ring */
+    int32_t kernel_kind;  /* 0 register-staged, 1 direct-to-LDS ring (A in row
+                             halves), 2 direct-to-LDS ring (A in whole rows) */
     int32_t stages;
     int32_t split_fixup;  /* 1 when the Stream-K fixup is split (see flags) */
     int32_t max_pieces;   /* most workgroups sharing one Stream-K tile */

@@ -57,13 +57,14 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // each dtype's preferred kernel for a tile first.
 const Variant *find_variant(int dtype, const gemm_tiles &t)
 {
-    // fp16/bf16 prefer the direct-to-LDS ring kernel and fall back to the
-    // register-staged one for tiles it does not cover (unless staged loads were
-    // asked for explicitly).
+    // fp16/bf16 prefer the direct-to-LDS ring kernel (the whole-row A variant
+    // when asked for) and fall back to the register-staged one for tiles it
+    // does not cover (unless staged loads were asked for explicitly).
     const bool staged_only = (t.flags & GEMM_FLAG_REGISTER_STAGED) || dtype == GEMM_F32;
+    const bool row_pairs = (t.flags & GEMM_FLAG_A_ROW_PAIRS) != 0;
     int n = 0;
     const Variant *v = variants(&n);
-    for (int kind = staged_only ? 0 : 1; kind >= 0; --kind)
+    for (int kind = staged_only ? 0 : row_pairs ? 2 : 1; kind >= 0; --kind)
         for (int i = 0; i < n; ++i)
             if (v[i].dtype == dtype && v[i].bm == t.bm && v[i].bn == t.bn && v[i].kind == kind &&
                 (t.wave_m == 0 || v[i].wave_m == t.wave_m) &&
@@ -393,7 +394,7 @@ int gemm_plan_describe(const gemm_plan *p, char *buf, size_t len)
                     "workspace=%zu B",
                     (long long)p->M, (long long)p->N, (long long)p->K, dtype_name(p->dtype),
                     sched_name(p->schedule), p->bm, p->bn, p->bk, p->variant->wave_m,
-                    p->variant->wave_n, p->variant->kind ? "ring" : "staged",
+                    p->variant->wave_n, p->variant->kind == 2 ? "ring/rows" : p->variant->kind ? "ring" : "staged",
                     p->variant->kind ? p->variant->stages : 2, p->group_m, p->P.tiles_m,
                     p->P.tiles_n, p->P.T, p->P.ipt, p->P.T_sk, p->P.T - p->P.T_sk,
                     (long long)p->iters_sk, p->P.g, p->P.q, p->P.r, p->P.grid,

@@ -578,6 +578,7 @@ struct DmaTile {
                   "stage copies must split evenly over the waves");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0 && BN >= 128, "tile shape");
     static_assert(S >= 3 && LPI * (S - 2) <= 63, "ring depth");
+    static_assert(MT * NT >= LPI, "one copy per MFMA of a slab");
     static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
@@ -643,14 +644,39 @@ __device__ __forceinline__ uint32_t lds_address(const uint8_t *p)
     return (uint32_t)(uintptr_t)GSK_LDS(const uint8_t, p);
 }
 
+template <int V>
+struct IC {
+    static constexpr int value = V;
+};
+
+// f(IC<B>{}), f(IC<B+1>{}), ..., f(IC<E-1>{}): a loop whose index is a
+// compile-time constant in the body.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    if constexpr (B < E) {
+        f(IC<B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 template <int DT, int BM, int BN, int WM, int WN, int S>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel_dma(KernelArgs args)
 {
     using Cfg = DmaTile<DT, BM, BN, WM, WN, S>;
-    constexpr int NW = Cfg::NW, MT = Cfg::MT, NT = Cfg::NT, LPI = Cfg::LPI;
+    constexpr int NW = Cfg::NW, MT = Cfg::MT, NT = Cfg::NT, LPI = Cfg::LPI, BK = Cfg::BK;
     constexpr int A_INSTR = Cfg::A_INSTR, B_INSTR = Cfg::B_INSTR;
-    constexpr int A_STAGE = Cfg::A_STAGE, STAGE = Cfg::STAGE, B_ROW = Cfg::B_ROW;
-    constexpr int NMFMA = MT * NT;  // MFMAs per slab
+    constexpr int A_STAGE = Cfg::A_STAGE, B_STAGE = Cfg::B_STAGE, B_ROW = Cfg::B_ROW;
+    constexpr int A_BASE = S * B_STAGE;  // LDS: the S B stages, then the S A stages
+    constexpr int NMFMA = MT * NT;       // MFMAs per slab
+    constexpr int NREAD = MT + NT;       // fragment reads per slab
+    static_assert(2 * NMFMA >= NREAD, "two fragment reads per MFMA");
 
     __shared__ __attribute__((aligned(1024))) uint8_t lds[Cfg::LDS];
 
@@ -661,10 +687,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel_dma(KernelArgs ar
     const int wy = wave / WN, wx = wave - (wave / WN) * WN;
     const int half = lane >> 5, l32 = lane & 31;
     const int p = logical_wg((int32_t)blockIdx.x, P.grid, P.xcds);
-    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_address(lds));
+    // LDS address of this wave's first 1 KiB copy block (wave-uniform)
+    const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(lds_address(lds) + wave * 1024);
 
     // Copy geometry of this lane (fixed for the kernel).  Copy j of this wave
-    // fills the 1 KiB block j * NW + wave of the stage's A (or B) region; the
+    // fills the 1 KiB block j * NW + wave of a stage's A (or B) region; the
     // lane writes bytes [16 * lane, 16 * lane + 16) of it.
     int a_row[A_INSTR], a_chunk[A_INSTR];
 #pragma unroll
@@ -681,32 +708,53 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel_dma(KernelArgs ar
         b_chunk[j] = ((o % B_ROW) >> 4) ^ swz_b(o / B_ROW);
     }
 
-    // Fragment read offsets within a stage (slab st = 0, 1 of 16 k each).
-    uint32_t a_rd[2][MT];
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const int row = wy * Cfg::WTM + mt * 32 + l32;
-            a_rd[st][mt] = row * 64 + (((2 * st + half) ^ swz_a(row)) << 4);
-        }
-    uint32_t b_rd[2][NT][2];
+    // Fragment read addresses (stage 0).  A: the lane's row r0 at chunk
+    // 2*st + half; block mt is 32 rows (2 KiB) on with the same swizzle.  B:
+    // the lane's transposing-read address for k-rows 8*(g/2) + si/4 of block
+    // nt; the other three reads of the block (4 and 16 k-rows on) keep the
+    // swizzle, which depends on the k-row mod 4 only.  Stage s adds s times
+    // the stage size, so every read is a base register plus a constant.
+    uint32_t a_rd[2];
     {
-        const int g = lane >> 4, si = lane & 15;
+        const int r0 = wy * Cfg::WTM + l32;
 #pragma unroll
         for (int st = 0; st < 2; ++st)
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const int krow = 16 * st + 8 * (g >> 1) + 4 * t + (si >> 2);
-                    const int n = wx * Cfg::WTN + nt * 32 + 16 * (g & 1) + 4 * (si & 3);
-                    b_rd[st][nt][t] = A_STAGE + krow * B_ROW +
-                                      (((n >> 3) ^ swz_b(krow)) << 4) + (n & 7) * 2;
-                }
+            a_rd[st] = A_BASE + r0 * 64 + (((2 * st + half) ^ swz_a(r0)) << 4);
     }
+    uint32_t b_rd[NT];
+    {
+        const int g = lane >> 4, si = lane & 15;
+        const int krow = 8 * (g >> 1) + (si >> 2);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const int n = wx * Cfg::WTN + nt * 32 + 16 * (g & 1) + 4 * (si & 3);
+            b_rd[nt] = krow * B_ROW + (((n >> 3) ^ swz_b(krow)) << 4) + (n & 7) * 2;
+        }
+    }
+    auto read_a = [&](int s, int st, int mt) {
+        return *(const u32x4 *)(lds + a_rd[st] + s * A_STAGE + mt * 32 * 64);
+    };
+    auto read_b = [&](int s, int st, int nt) {
+        const uint8_t *base = lds + b_rd[nt] + s * B_STAGE + st * 16 * B_ROW;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(GSK_LDS(i16x4, base));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(GSK_LDS(i16x4, base + 4 * B_ROW));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        return u32x4{l2[0], l2[1], h2[0], h2[1]};
+    };
+    // Fragment read r of slab st, in the order a slab's MFMAs (block
+    // (j / NT, j % NT) for j = 0, 1, ...) first need them: A block 0, B
+    // blocks 0 .. NT-1, then A blocks 1 .. MT-1.
+    auto read_frag = [&](int s, int st, int r, u32x4 (&fa)[MT], u32x4 (&fb)[NT]) {
+        if (r == 0)
+            fa[0] = read_a(s, st, 0);
+        else if (r <= NT)
+            fb[r - 1] = read_b(s, st, r - 1);
+        else
+            fa[r - NT] = read_a(s, st, r - NT);
+    };
 
     f32x16 acc[MT][NT];
+    u32x4 fa0[MT], fb0[NT], fa1[MT], fb1[NT];
 
     WorkCursor cur = work_begin(P, p);
     WorkItem w;
@@ -714,6 +762,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel_dma(KernelArgs ar
         int tm, tn;
         tile_coords(P, w.tile, &tm, &tn);
         const int m0 = tm * BM, n0 = tn * BN;
+        const int kb = w.kb, n = w.ke - w.kb;  // MAC iterations of this item (>= 1)
+        const int k_hi = w.ke * BK < args.K ? w.ke * BK : args.K;
 
         uint32_t a_off[A_INSTR];
 #pragma unroll
@@ -727,33 +777,38 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel_dma(KernelArgs ar
             b_off[j] = n0 + b_chunk[j] * 8 < args.N
                            ? (uint32_t)(b_krow[j] * args.ldb * 2 + b_chunk[j] * 16)
                            : kOutOfRange;
+        // Source of the next iteration to be copied: its first k and the A
+        // and B slabs it starts at.  The slab pointers stop at the item's last
+        // iteration, so that a copy past the end (below) never has a base
+        // outside the matrix.
+        int k_cp = kb * BK;
+        const uint8_t *a_cp = args.A + ((int64_t)m0 * args.lda + k_cp) * 2;
+        const uint8_t *b_cp = args.B + ((int64_t)k_cp * args.ldb + n0) * 2;
+        const int64_t b_step = (int64_t)BK * args.ldb * 2;
 
-        // The j-th copy (A copies first, then B) of MAC iteration kk into stage s.
-        auto copy_one = [&](int kk, int s, int j) {
-            const int k0 = kk * Cfg::BK;
-            const int k_left = args.K - k0;
+        // The j-th copy (A copies first, then B) of the next iteration into
+        // stage s.  Every iteration from kb on is copied, also past the end
+        // of the item: there k >= k_hi, every lane reads out of range, and
+        // the stage (one nobody reads again) is filled with zeros.  So every
+        // iteration issues exactly LPI copies and all the waits below have
+        // constant counts.
+        auto copy_one = [&](int s, int j) {
+            const bool whole = k_cp + BK <= k_hi;
             if (j < A_INSTR) {
-                const i32x4 ra = rsrc_words(args.A + ((int64_t)m0 * args.lda + k0) * 2);
-                copy16(ra, a_chunk[j] * 8 < k_left ? a_off[j] : kOutOfRange,
-                       lds0 + s * STAGE + (j * NW + wave) * 1024);
+                const uint32_t off = whole || a_chunk[j] * 8 < k_hi - k_cp ? a_off[j] : kOutOfRange;
+                copy16(rsrc_words(a_cp), off, lds_wave + A_BASE + s * A_STAGE + j * NW * 1024);
             } else {
                 const int jb = j - A_INSTR;
-                const i32x4 rb = rsrc_words(args.B + ((int64_t)k0 * args.ldb + n0) * 2);
-                copy16(rb, b_krow[jb] < k_left ? b_off[jb] : kOutOfRange,
-                       lds0 + s * STAGE + A_STAGE + (jb * NW + wave) * 1024);
+                const uint32_t off = whole || b_krow[jb] < k_hi - k_cp ? b_off[jb] : kOutOfRange;
+                copy16(rsrc_words(b_cp), off, lds_wave + s * B_STAGE + jb * NW * 1024);
             }
         };
-        auto read_a = [&](int s, int st, int mt) {
-            return *(const u32x4 *)(lds + s * STAGE + a_rd[st][mt]);
-        };
-        auto read_b = [&](int s, int st, int nt) {
-            const uint8_t *base = lds + s * STAGE;
-            const i16x4 lo =
-                __builtin_amdgcn_ds_read_tr16_b64_v4i16(GSK_LDS(i16x4, base + b_rd[st][nt][0]));
-            const i16x4 hi =
-                __builtin_amdgcn_ds_read_tr16_b64_v4i16(GSK_LDS(i16x4, base + b_rd[st][nt][1]));
-            const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-            return u32x4{l2[0], l2[1], h2[0], h2[1]};
+        auto next_copy = [&]() {
+            if (k_cp + BK < k_hi) {
+                a_cp += BK * 2;
+                b_cp += b_step;
+            }
+            k_cp += BK;
         };
 
 #pragma unroll
@@ -762,66 +817,355 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel_dma(KernelArgs ar
             for (int nt = 0; nt < NT; ++nt)
                 acc[mt][nt] = f32x16{};
 
-        const int n = w.ke - w.kb;  // MAC iterations of this item (>= 1)
         // All waves are done with the previous item's stages before refilling.
         barrier_only();
+        static_for<0, S - 1>([&](auto u) {
 #pragma unroll
-        for (int j = 0; j < S - 1; ++j)
-            if (j < n)
-#pragma unroll
-                for (int c = 0; c < LPI; ++c)
-                    copy_one(w.kb + j, j, c);
-        wait_copies<LPI>(n - 1 < S - 2 ? n - 1 : S - 2);
+            for (int c = 0; c < LPI; ++c)
+                copy_one(u.value, c);
+            next_copy();
+        });
+        wait_vmcnt<(S - 2) * LPI>();  // iteration kb's copies have landed
         barrier_only();
-
-        u32x4 fa0[MT], fb0[NT], fa1[MT], fb1[NT];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-            fa0[mt] = read_a(0, 0, mt);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-            fb0[nt] = read_b(0, 0, nt);
+        for (int r = 0; r < NREAD; ++r)
+            read_frag(0, 0, r, fa0, fb0);
 
-        int s = 0;
-        for (int i = 0; i < n; ++i) {
-            const int s_next = s + 1 == S ? 0 : s + 1;
+        // MAC iteration i (stage s = i mod S, a compile-time constant here);
+        // `surely_more` says at compile time that another iteration follows.
+        auto step = [&](int i, auto s_c, auto surely_more) {
+            constexpr int s = decltype(s_c)::value;
+            constexpr int s_next = (s + 1) % S, s_fill = (s + S - 1) % S;
             // (a) first slab's MFMAs, with the second slab's fragment reads
-            //     issued one per MFMA while the MFMAs run
+            //     issued two per MFMA in the order the MFMAs consume them
 #pragma unroll
             for (int j = 0; j < NMFMA; ++j) {
                 mfma_step<DT>(acc[j / NT][j % NT], fb0[j % NT], fa0[j / NT]);
-                if (j < MT)
-                    fa1[j] = read_a(s, 1, j);
-                else if (j < MT + NT)
-                    fb1[j - MT] = read_b(s, 1, j - MT);
+#pragma unroll
+                for (int r = 2 * j; r < 2 * j + 2 && r < NREAD; ++r)
+                    read_frag(s, 1, r, fa1, fb1);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            const bool more = i + 1 < n;
+            const bool more = decltype(surely_more)::value || i + 1 < n;
             if (more) {
-                // (b) next stage complete in every wave; everyone is past the
-                //     stage the next copy will overwrite
-                const int after = n - 2 - i < S - 3 ? n - 2 - i : S - 3;
-                wait_copies<LPI>(after);
+                // (b) iteration i + 1's copies are complete in every wave (the
+                //     S - 3 later iterations' may still be in flight), and
+                //     every wave is past iteration i - 1's stage
+                wait_vmcnt<(S - 3) * LPI>();
                 barrier_only();
             }
-            // (c) second slab's MFMAs, with the copies S - 1 iterations ahead
-            //     and the next stage's first-slab reads in between
-            const bool copy = i + S - 1 < n;
-            const int s_fill = s == 0 ? S - 1 : s - 1;  // stage of iteration i - 1
+            // (c) second slab's MFMAs, with the next iteration's first-slab
+            //     reads (unconditional: on the last iteration they are
+            //     harmless, and a fixed count lets the compiler wait for just
+            //     the fragments each MFMA needs) and the copies S - 1
+            //     iterations ahead into the stage of iteration i - 1.  The
+            //     last iteration copies nothing: without the barrier above
+            //     other waves may still be reading.
 #pragma unroll
             for (int j = 0; j < NMFMA; ++j) {
                 mfma_step<DT>(acc[j / NT][j % NT], fb1[j % NT], fa1[j / NT]);
-                if (j < LPI && copy)
-                    copy_one(w.kb + i + S - 1, s_fill, j);
-                if (more) {
-                    if (j < MT)
-                        fa0[j] = read_a(s_next, 0, j);
-                    else if (j < MT + NT)
-                        fb0[j - MT] = read_b(s_next, 0, j - MT);
+#pragma unroll
+                for (int r = 2 * j; r < 2 * j + 2 && r < NREAD; ++r)
+                    read_frag(s_next, 0, r, fa0, fb0);
+                if (more && j >= NMFMA - LPI)
+                    copy_one(s_fill, j - (NMFMA - LPI));
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (more)
+                next_copy();
+        };
+        int i = 0;
+        for (; i + S <= n; i += S)
+            static_for<0, S>([&](auto u) { step(i + u.value, u, IC<(u.value < S - 1)>{}); });
+        static_for<0, S - 1>([&](auto u) {
+            if (i + u.value < n)
+                step(i + u.value, u, IC<0>{});
+        });
+
+        finish_tile<BM, BN, MT, NT>(acc, args, w, p, m0, n0, wave, lane, wy * Cfg::WTM,
+                                    wx * Cfg::WTN);
+    }
+    if (args.split_fixup)
+        reduce_split_tiles<BM, BN, WM, WN>(args, p, wave, lane);
+}
+
+// ---------------------------------------------------------------------------
+// fp16/bf16 kernel with direct global -> LDS loads, A copied in whole rows.
+//
+// The MAC iteration (BK = 32), the B ring and the MFMA / fragment-read
+// pattern are those of gemm_kernel_dma.  A is copied differently: one copy
+// brings k [64Q, 64Q + 64) of a row, 128 bytes, the A operand of iterations
+// 2Q and 2Q + 1 ("pair" Q).  Every A row is then fetched as whole 128-byte
+// cache lines; copying the two 64-byte halves an iteration apart fetches each
+// line twice through the vector L1 and made the pure load phase of a 4096^3
+// product ~15% slower on MI355X.
+//
+// LDS: three A pair slots (BM rows x 128 bytes, 16-byte chunk c of row r at
+// position c ^ ((r ^ r >> 3) & 7)) followed by four B stages (32 k-rows x BN
+// values, swizzled as in gemm_kernel_dma).
+//
+// Copy schedule in global iteration numbers kk: iteration kk issues the B slab
+// of kk + 3 and half (kk & 1) of A pair (kk >> 1) + 2 (half 0 = rows
+// [0, BM/2), half 1 = rows [BM/2, BM)), so every copy lands at least three
+// iterations before its first use.  Pair (kk >> 1) + 2 goes into the slot of
+// pair (kk >> 1) - 1, whose last iteration is kk - 1, and B slab kk + 3 into
+// the stage of kk - 1: both are free once every wave has passed the barrier
+// in the middle of iteration kk.  A segment [kb, ke) starts with the copies
+// that the virtual iterations (kb & ~1) - 4 .. kb - 1 would have issued.
+template <int DT, int BM, int BN, int WM, int WN>
+struct PairTile {
+    static constexpr int NW = WM * WN, NTH = 64 * NW;
+    static constexpr int BK = 32;
+    static constexpr int SA = 3, SB = 4;                   // A pair slots, B stages
+    static constexpr int B_ROW = BN * 2;                   // bytes per B k-row
+    static constexpr int A_PAIR = BM * 128, B_STAGE = BK * BN * 2;
+    static constexpr int B_BASE = SA * A_PAIR;
+    static constexpr int LDS = SA * A_PAIR + SB * B_STAGE;
+    static constexpr int A_INSTR = A_PAIR / 2 / 1024 / NW; // 1 KiB copies per wave and half pair
+    static constexpr int B_INSTR = B_STAGE / 1024 / NW;
+    static constexpr int LPI = A_INSTR + B_INSTR;          // copies per wave and iteration
+    static constexpr int WTM = BM / WM, WTN = BN / WN, MT = WTM / 32, NT = WTN / 32;
+    static_assert(DT == 1 || DT == 2, "fp16 / bf16 only");
+    static_assert(A_INSTR >= 1 && A_INSTR * 2 * 1024 * NW == A_PAIR &&
+                      B_INSTR >= 1 && B_INSTR * 1024 * NW == B_STAGE,
+                  "copies must split evenly over the waves");
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0 && BN >= 128, "tile shape");
+    static_assert(2 * LPI <= 23, "wait counts");
+    static_assert(MT * NT >= LPI, "one copy per MFMA of a slab");
+    static_assert(LDS <= 160 * 1024, "LDS budget");
+};
+
+// s_waitcnt vmcnt(n) for a runtime, wave-uniform n in [0, 23]; a larger n
+// waits for vmcnt(23), which is stricter and therefore still correct.
+__device__ __forceinline__ void wait_vm(int n)
+{
+#define GSK_VM(c)                                              \
+    case c:                                                    \
+        asm volatile("s_waitcnt vmcnt(" #c ")" ::: "memory"); \
+        break;
+    switch (n) {
+        GSK_VM(0) GSK_VM(1) GSK_VM(2) GSK_VM(3) GSK_VM(4) GSK_VM(5) GSK_VM(6) GSK_VM(7)
+        GSK_VM(8) GSK_VM(9) GSK_VM(10) GSK_VM(11) GSK_VM(12) GSK_VM(13) GSK_VM(14) GSK_VM(15)
+        GSK_VM(16) GSK_VM(17) GSK_VM(18) GSK_VM(19) GSK_VM(20) GSK_VM(21) GSK_VM(22)
+    default:
+        asm volatile("s_waitcnt vmcnt(23)" ::: "memory");
+    }
+#undef GSK_VM
+}
+
+__device__ __forceinline__ uint32_t swz_row128(int row) { return (uint32_t)(row ^ (row >> 3)) & 7; }
+
+template <int DT, int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel_pair(KernelArgs args)
+{
+    using Cfg = PairTile<DT, BM, BN, WM, WN>;
+    constexpr int NW = Cfg::NW, MT = Cfg::MT, NT = Cfg::NT;
+    constexpr int A_INSTR = Cfg::A_INSTR, B_INSTR = Cfg::B_INSTR, LPI = Cfg::LPI;
+    constexpr int A_PAIR = Cfg::A_PAIR, B_STAGE = Cfg::B_STAGE, B_BASE = Cfg::B_BASE;
+    constexpr int B_ROW = Cfg::B_ROW;
+    constexpr int NMFMA = MT * NT;  // MFMAs per slab
+    constexpr int NREAD = MT + NT;  // fragment reads per slab
+    static_assert(2 * NMFMA >= NREAD, "two fragment reads per MFMA");
+
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[Cfg::LDS];
+
+    const Partition &P = args.P;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wy = wave / WN, wx = wave - (wave / WN) * WN;
+    const int half = lane >> 5, l32 = lane & 31;
+    const int p = logical_wg((int32_t)blockIdx.x, P.grid, P.xcds);
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_address(lds));
+
+    // A copy j (0 .. 2*A_INSTR-1; half h issues j in [h*A_INSTR, (h+1)*A_INSTR))
+    // fills 1 KiB block j*NW + wave of a pair slot: 8 rows of 128 bytes, the
+    // lane writing position lane & 7 of row 8*block + lane/8.
+    auto a_copy_row = [&](int j) { return (j * NW + wave) * 8 + (lane >> 3); };
+    int b_krow[B_INSTR], b_chunk[B_INSTR];
+#pragma unroll
+    for (int j = 0; j < B_INSTR; ++j) {
+        const int o = (j * NW + wave) * 1024 + lane * 16;
+        b_krow[j] = o / B_ROW;
+        b_chunk[j] = ((o % B_ROW) >> 4) ^ swz_b(o / B_ROW);
+    }
+
+    // Fragment read addresses.  A: the lane's row r0 = wy*WTM + l32 at chunk
+    // `half` (slab 0 of the first iteration of a pair).  Slab 1 is chunk + 2,
+    // the pair's second iteration chunk + 4 and block mt + 1 is 32 rows on,
+    // which flips bit 2 of the row's swizzle: bits 5 and 6 of the byte offset
+    // (XOR) and 4 KiB steps (add).
+    const int r0 = wy * Cfg::WTM + l32;
+    const uint32_t a_lane = (uint32_t)(r0 * 128) + ((half ^ swz_row128(r0)) << 4);
+    // B: the lane's transposing-read address for slab 0, k-rows 8*(g/2) +
+    // (si/4) of each 16.  The swizzle depends on the k-row mod 4 only, so the
+    // other three reads of a block (4 and 16 k-rows on) are constant offsets.
+    uint32_t b_lane[NT];
+    {
+        const int g = lane >> 4, si = lane & 15;
+        const int krow = 8 * (g >> 1) + (si >> 2);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const int n = wx * Cfg::WTN + nt * 32 + 16 * (g & 1) + 4 * (si & 3);
+            b_lane[nt] = B_BASE + krow * B_ROW + (((n >> 3) ^ swz_b(krow)) << 4) + (n & 7) * 2;
+        }
+    }
+
+    f32x16 acc[MT][NT];
+
+    WorkCursor cur = work_begin(P, p);
+    WorkItem w;
+    while (work_next(P, p, cur, w)) {
+        int tm, tn;
+        tile_coords(P, w.tile, &tm, &tn);
+        const int m0 = tm * BM, n0 = tn * BN;
+        const int kb = w.kb, ke = w.ke;
+        // k range of this segment: copies outside it read nothing (zeros).
+        const int k_lo = kb * Cfg::BK;
+        const int k_hi = ke * Cfg::BK < args.K ? ke * Cfg::BK : args.K;
+
+        uint32_t b_off[B_INSTR];
+#pragma unroll
+        for (int j = 0; j < B_INSTR; ++j)
+            b_off[j] = n0 + b_chunk[j] * 8 < args.N
+                           ? (uint32_t)(b_krow[j] * args.ldb * 2 + b_chunk[j] * 16)
+                           : kOutOfRange;
+
+        // The copies of (virtual) iteration v: half (v & 1) of A pair
+        // (v >> 1) + 2 into pair slot sa_fill, and the B slab of v + 3 into
+        // stage sb_fill.  Every iteration issues all LPI of them, so the wait
+        // counts below are constants; a copy whose k lies outside [k_lo, k_hi)
+        // reads nothing and fills its (unused) slot or stage with zeros.
+        auto copy_a = [&](int v, int sa_fill, int j) {
+            const int q = (v >> 1) + 2;
+            const int jj = (v & 1) * A_INSTR + j;
+            const int k0 = 64 * q;
+            const int live = k0 < k_hi;
+            const int row = a_copy_row(jj);
+            const int chunk = (lane & 7) ^ (int)swz_row128(row);
+            const i32x4 ra =
+                rsrc_words(args.A + ((int64_t)m0 * args.lda + (live ? k0 : 0)) * 2);
+            copy16(ra,
+                   live && m0 + row < args.M && chunk * 8 < k_hi - k0
+                       ? (uint32_t)(row * args.lda * 2 + chunk * 16)
+                       : kOutOfRange,
+                   lds0 + sa_fill * A_PAIR + (jj * NW + wave) * 1024);
+        };
+        auto copy_b = [&](int v, int sb_fill, int j) {
+            const int k0 = (v + 3) * Cfg::BK;
+            const int live = k0 >= k_lo && k0 < k_hi;
+            const i32x4 rb =
+                rsrc_words(args.B + ((int64_t)(live ? k0 : 0) * args.ldb + n0) * 2);
+            copy16(rb, live && b_krow[j] < k_hi - k0 ? b_off[j] : kOutOfRange,
+                   lds0 + B_BASE + sb_fill * B_STAGE + (j * NW + wave) * 1024);
+        };
+        auto read_a = [&](int slot, int odd, int st, int mt) {
+            const uint32_t x = (uint32_t)((st << 5) | ((odd ^ (mt & 1)) << 6));
+            return *(const u32x4 *)(lds + slot * A_PAIR + mt * 4096 + (a_lane ^ x));
+        };
+        auto read_b = [&](int s, int st, int nt) {
+            const uint8_t *base = lds + s * B_STAGE + b_lane[nt] + st * 16 * B_ROW;
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(GSK_LDS(i16x4, base));
+            const i16x4 hi =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16(GSK_LDS(i16x4, base + 4 * B_ROW));
+            const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+            return u32x4{l2[0], l2[1], h2[0], h2[1]};
+        };
+        // Fragment read r of slab st, in the order the slab's MFMAs first
+        // need them: A block 0, B blocks 0 .. NT-1, A blocks 1 .. MT-1.
+        auto read_frag = [&](int slot, int odd, int s, int st, int r, u32x4 (&fa)[MT],
+                             u32x4 (&fb)[NT]) {
+            if (r == 0)
+                fa[0] = read_a(slot, odd, st, 0);
+            else if (r <= NT)
+                fb[r - 1] = read_b(s, st, r - 1);
+            else
+                fa[r - NT] = read_a(slot, odd, st, r - NT);
+        };
+
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                acc[mt][nt] = f32x16{};
+
+        // Slots and stages are numbered from the segment's first pair and
+        // iteration.  Pair q = (kb >> 1) + d sits in slot d % 3; B slab kk in
+        // stage (kk - kb) % 4.
+        // All waves are done with the previous item's slots before refilling.
+        barrier_only();
+        {
+            const int vb = (kb & ~1) - 4;  // pairs (kb >> 1) and on
+            for (int v = vb; v < kb; ++v) {
+                const int sa_fill = ((v - vb) >> 1) % Cfg::SA;
+                const int sb_fill = (v + 3 - kb) & (Cfg::SB - 1);
+#pragma unroll
+                for (int j = 0; j < A_INSTR; ++j)
+                    copy_a(v, sa_fill, j);
+#pragma unroll
+                for (int j = 0; j < B_INSTR; ++j)
+                    copy_b(v, sb_fill, j);
+            }
+        }
+        // Iteration kb's copies were issued by virtual iterations <= kb - 3.
+        wait_copies<LPI>(2);
+        barrier_only();
+
+        int sa = 0;                   // pair slot of the current iteration
+        int sb = 0;                   // B stage of the current iteration
+        int odd = kb & 1;             // the current iteration is the second of its pair
+        int sa_fill = 2;              // slot of pair (kk >> 1) + 2
+        u32x4 fa0[MT], fb0[NT], fa1[MT], fb1[NT];
+#pragma unroll
+        for (int r = 0; r < NREAD; ++r)
+            read_frag(sa, odd, sb, 0, r, fa0, fb0);
+
+        for (int kk = kb; kk < ke; ++kk) {
+            const int sa_next = odd ? (sa + 1 == Cfg::SA ? 0 : sa + 1) : sa;
+            const int sb_next = (sb + 1) & (Cfg::SB - 1);
+            const int sb_fill = (sb + 3) & (Cfg::SB - 1);  // stage of kk - 1 = stage of kk + 3
+            // (a) first slab's MFMAs, the second slab's fragment reads between
+#pragma unroll
+            for (int j = 0; j < NMFMA; ++j) {
+                mfma_step<DT>(acc[j / NT][j % NT], fb0[j % NT], fa0[j / NT]);
+#pragma unroll
+                for (int r = 2 * j; r < 2 * j + 2 && r < NREAD; ++r)
+                    read_frag(sa, odd, sb, 1, r, fa1, fb1);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            const bool more = kk + 1 < ke;
+            if (more) {
+                // (b) iteration kk + 1's copies are complete in every wave (only
+                //     those of iteration kk - 1 may still be in flight), and
+                //     every wave is past iteration kk - 1's slot and stage
+                wait_copies<LPI>(1);
+                barrier_only();
+            }
+            // (c) second slab's MFMAs, with the next iteration's first-slab
+            //     reads (unconditional: on the last iteration they are
+            //     harmless, and a fixed count lets the compiler wait for just
+            //     the fragments each MFMA needs) and this iteration's copies.
+            //     The last iteration issues no copies: without the barrier
+            //     above other waves may still be reading.
+#pragma unroll
+            for (int j = 0; j < NMFMA; ++j) {
+                mfma_step<DT>(acc[j / NT][j % NT], fb1[j % NT], fa1[j / NT]);
+#pragma unroll
+                for (int r = 2 * j; r < 2 * j + 2 && r < NREAD; ++r)
+                    read_frag(sa_next, odd ^ 1, sb_next, 0, r, fa0, fb0);
+                if (more && j >= NMFMA - LPI) {
+                    if (j - (NMFMA - LPI) < A_INSTR)
+                        copy_a(kk, sa_fill, j - (NMFMA - LPI));
+                    else
+                        copy_b(kk, sb_fill, j - (NMFMA - LPI) - A_INSTR);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
-            s = s_next;
+            if (odd)
+                sa_fill = sa_fill + 1 == Cfg::SA ? 0 : sa_fill + 1;
+            sa = sa_next;
+            sb = sb_next;
+            odd ^= 1;
         }
 
         finish_tile<BM, BN, MT, NT>(acc, args, w, p, m0, n0, wave, lane, wy * Cfg::WTM,
@@ -847,6 +1191,14 @@ static int launch_gemm_dma(const KernelArgs &args, int grid, hipStream_t stream)
     return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
+template <int DT, int BM, int BN, int WM, int WN>
+static int launch_gemm_pair(const KernelArgs &args, int grid, hipStream_t stream)
+{
+    hipLaunchKernelGGL((gemm_kernel_pair<DT, BM, BN, WM, WN>), dim3(grid),
+                       dim3(PairTile<DT, BM, BN, WM, WN>::NTH), 0, stream, args);
+    return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
 // Register-staged kernel (fp32, and fp16/bf16 for comparison)
 #define GSK_STAGED(DT, BM, BN, WM, WN)                                                           \
     Variant{DT, BM, BN, Tile<DT, BM, BN, WM, WN>::BK, WM, WN, Tile<DT, BM, BN, WM, WN>::NTH,     \
@@ -859,9 +1211,22 @@ static int launch_gemm_dma(const KernelArgs &args, int grid, hipStream_t stream)
             &launch_gemm_dma<DT, BM, BN, WM, WN, S>,                                             \
             (const void *)&gemm_kernel_dma<DT, BM, BN, WM, WN, S>}
 
+// Direct-to-LDS ring kernel with whole-row A copies (fp16/bf16)
+#define GSK_PAIR(DT, BM, BN, WM, WN)                                                             \
+    Variant{DT, BM, BN, 32, WM, WN, PairTile<DT, BM, BN, WM, WN>::NTH,                           \
+            (size_t)PairTile<DT, BM, BN, WM, WN>::LDS, 2, PairTile<DT, BM, BN, WM, WN>::SB,       \
+            &launch_gemm_pair<DT, BM, BN, WM, WN>,                                               \
+            (const void *)&gemm_kernel_pair<DT, BM, BN, WM, WN>}
+
 // The first entry matching a request wins, so each dtype's preferred kernel
 // for a tile comes first.
 static const Variant kVariants[] = {
+    GSK_PAIR(1, 256, 256, 4, 2), GSK_PAIR(1, 256, 256, 2, 4), GSK_PAIR(1, 256, 256, 2, 2),
+    GSK_PAIR(1, 256, 128, 4, 2), GSK_PAIR(1, 256, 128, 2, 2), GSK_PAIR(1, 128, 256, 2, 4),
+    GSK_PAIR(1, 128, 256, 2, 2), GSK_PAIR(1, 128, 128, 2, 2),
+    GSK_PAIR(2, 256, 256, 4, 2), GSK_PAIR(2, 256, 256, 2, 4), GSK_PAIR(2, 256, 256, 2, 2),
+    GSK_PAIR(2, 256, 128, 4, 2), GSK_PAIR(2, 256, 128, 2, 2), GSK_PAIR(2, 128, 256, 2, 4),
+    GSK_PAIR(2, 128, 256, 2, 2), GSK_PAIR(2, 128, 128, 2, 2),
     GSK_DMA(1, 256, 256, 4, 2, 4), GSK_DMA(1, 256, 256, 4, 2, 5), GSK_DMA(1, 256, 256, 2, 4, 4),
     GSK_DMA(1, 256, 256, 2, 2, 4), GSK_DMA(1, 256, 256, 2, 2, 5), GSK_DMA(1, 256, 128, 2, 2, 4),
     GSK_DMA(1, 256, 128, 4, 2, 4), GSK_DMA(1, 128, 256, 2, 2, 4), GSK_DMA(1, 128, 256, 2, 4, 4),

@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 from gpu_util import compare, run_gemm, to_device
-from persistent_stream_tiling_amd import inputs, tuning
+from persistent_stream_tiling_amd import FLAG_A_ROW_PAIRS, inputs, tuning
 
 pytestmark = pytest.mark.gpu
 
@@ -27,9 +27,12 @@ SMALL = [
     (300, 200, 704),   # ragged M and N; K a multiple of 8 (no repack)
     (257, 203, 701),   # ragged everything; rows not 16-byte multiples (repacked)
 ]
+ROWS = FLAG_A_ROW_PAIRS  # the ring kernel that copies A in whole rows
 TILES = {"f16": [dict(bm=64, bn=64), dict(bm=128, bn=128), dict(bm=256, bn=128),
-                 dict(bm=128, bn=256), dict(bm=256, bn=256)],
-         "bf16": [dict(bm=64, bn=64), dict(bm=128, bn=128), dict(bm=256, bn=256)],
+                 dict(bm=128, bn=256), dict(bm=256, bn=256), dict(bm=128, bn=128, flags=ROWS),
+                 dict(bm=256, bn=128, flags=ROWS), dict(bm=256, bn=256, flags=ROWS)],
+         "bf16": [dict(bm=64, bn=64), dict(bm=128, bn=128), dict(bm=256, bn=256),
+                  dict(bm=256, bn=128, wave_m=4, wave_n=2, flags=ROWS)],
          "f32": [dict(bm=64, bn=64), dict(bm=128, bn=128)]}
 
 
@@ -86,17 +89,20 @@ def test_stream_k_long_k_integer_exact():
     ref, _ = oracle.gemm_sampled(a, b, "bf16", rows, cols)
     da, db = to_device(a, "bf16"), to_device(b, "bf16")
     import persistent_stream_tiling_amd as gsk
-    for tiles in (dict(bm=128, bn=128), dict(bm=64, bn=64), dict(bm=256, bn=256)):
+    for tiles in (dict(bm=128, bn=128), dict(bm=64, bn=64), dict(bm=256, bn=256),
+                  dict(bm=256, bn=128, flags=ROWS)):
         for g in (256, 100, 3):
             for flag in (gsk.FLAG_FIXUP_HEAD, gsk.FLAG_FIXUP_SPLIT):
-                plan, _, c = run_gemm(da, db, M, N, K, "bf16", "streamk", grid=g, flags=flag,
-                                      **tiles)
+                t = dict(tiles)
+                t["flags"] = t.get("flags", 0) | flag
+                plan, _, c = run_gemm(da, db, M, N, K, "bf16", "streamk", grid=g, **t)
                 got = c.cpu().numpy()[rows, cols]
                 compare(got, ref, None, "bf16", exact=True, what=plan.describe())
 
 
-@pytest.mark.parametrize("tiles", [dict(bm=128, bn=128), dict(bm=256, bn=256), dict(bm=64, bn=64)],
-                         ids=lambda t: f"{t['bm']}x{t['bn']}")
+@pytest.mark.parametrize("tiles", [dict(bm=128, bn=128), dict(bm=256, bn=256), dict(bm=64, bn=64),
+                                   dict(bm=256, bn=128, flags=ROWS)],
+                         ids=lambda t: f"{t['bm']}x{t['bn']}" + ("-rows" if t.get("flags") else ""))
 def test_split_and_head_fixups_agree_bitwise(tiles):
     # both fixups add every element's pieces in ascending k order
     M, N, K = 512, 384, 16384
@@ -105,7 +111,9 @@ def test_split_and_head_fixups_agree_bitwise(tiles):
     import persistent_stream_tiling_amd as gsk
     outs = {}
     for name, flag in (("head", gsk.FLAG_FIXUP_HEAD), ("split", gsk.FLAG_FIXUP_SPLIT)):
-        plan, ws, c = run_gemm(da, db, M, N, K, "bf16", "streamk", flags=flag, **tiles)
+        t = dict(tiles)
+        t["flags"] = t.get("flags", 0) | flag
+        plan, ws, c = run_gemm(da, db, M, N, K, "bf16", "streamk", **t)
         assert plan.info["max_pieces"] >= 2
         assert plan.workspace_status(ws) == 0
         # flags and counters are left zero for the next run
