@@ -85,20 +85,21 @@ enum {
      * identical bits. */
     GEMM_FLAG_FIXUP_HEAD = 1u << 3,
     GEMM_FLAG_FIXUP_SPLIT = 1u << 4,
-    /* fp16/bf16: use the ring kernel that copies A in whole 128-byte rows,
-     * two MAC iterations at a time (kernel_kind 2), instead of one
-     * iteration's 64-byte row halves (kernel_kind 1, the default).  Fewer,
-     * fuller cache-line requests; pays off on long-K Stream-K shapes. */
-    GEMM_FLAG_A_ROW_PAIRS = 1u << 5
+    /* fp16/bf16: use the ring kernel with 32-deep MAC iterations, which
+     * copies A in 64-byte row halves (kernel_kind 1), instead of the default
+     * one with 64-deep iterations and whole 128-byte A rows (kernel_kind 2).
+     * Kept for comparison: half-line A copies fetch every A line twice. */
+    GEMM_FLAG_A_HALF_ROWS = 1u << 5
 };
 
 /* Tile and schedule knobs.  Every field 0 means "default". */
 typedef struct {
     int32_t bm, bn;   /* output tile (multiples of 32 from the supported set;
                          default per dtype and shape) */
-    int32_t bk;       /* k-depth of one MAC iteration, fixed per kernel: 32
-                         for the fp16/bf16 ring kernel, 64 for the fp16/bf16
-                         register-staged one, 32 for fp32; 0 = any */
+    int32_t bk;       /* k-depth of one MAC iteration, fixed per kernel: 64
+                         for the fp16/bf16 ring kernels (32 with
+                         GEMM_FLAG_A_HALF_ROWS) and the register-staged one,
+                         32 for fp32; 0 = any */
     int32_t grid;     /* g: workgroups of the persistent / Stream-K launch;
                          0 = number of CUs (issue #1393 uses the SM count) */
     int32_t group_m;  /* tile-order group height (issue #1393 GROUP_M);

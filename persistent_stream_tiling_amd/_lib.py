@@ -12,7 +12,7 @@ FLAG_NO_XCD_REMAP = 1 << 1
 FLAG_REGISTER_STAGED = 1 << 2
 FLAG_FIXUP_HEAD = 1 << 3
 FLAG_FIXUP_SPLIT = 1 << 4
-FLAG_A_ROW_PAIRS = 1 << 5
+FLAG_A_HALF_ROWS = 1 << 5
 ROLE_FULL, ROLE_CONTRIB, ROLE_OWNER = 0, 1, 2
 
 SCHEDULES = {"dp": DP, "persistent": PERSISTENT, "streamk": STREAMK, "hybrid": HYBRID}

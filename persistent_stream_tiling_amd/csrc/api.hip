@@ -57,16 +57,18 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // each dtype's preferred kernel for a tile first.
 const Variant *find_variant(int dtype, const gemm_tiles &t)
 {
-    // fp16/bf16 prefer the direct-to-LDS ring kernel (the whole-row A variant
-    // when asked for) and fall back to the register-staged one for tiles it
-    // does not cover (unless staged loads were asked for explicitly).
+    // fp16/bf16 prefer the direct-to-LDS ring kernel with whole-row A copies,
+    // then the one with half-row A copies (or only that one when asked for),
+    // and fall back to the register-staged one for tiles neither covers
+    // (unless staged loads were asked for explicitly).
     const bool staged_only = (t.flags & GEMM_FLAG_REGISTER_STAGED) || dtype == GEMM_F32;
-    const bool row_pairs = (t.flags & GEMM_FLAG_A_ROW_PAIRS) != 0;
+    const bool half_rows = (t.flags & GEMM_FLAG_A_HALF_ROWS) != 0;
     int n = 0;
     const Variant *v = variants(&n);
-    for (int kind = staged_only ? 0 : row_pairs ? 2 : 1; kind >= 0; --kind)
+    for (int kind = staged_only ? 0 : 2; kind >= 0; --kind)
         for (int i = 0; i < n; ++i)
             if (v[i].dtype == dtype && v[i].bm == t.bm && v[i].bn == t.bn && v[i].kind == kind &&
+                !(kind == 2 && half_rows) &&
                 (t.wave_m == 0 || v[i].wave_m == t.wave_m) &&
                 (t.wave_n == 0 || v[i].wave_n == t.wave_n) && (t.bk == 0 || v[i].bk == t.bk) &&
                 (t.stages == 0 || v[i].stages == t.stages))

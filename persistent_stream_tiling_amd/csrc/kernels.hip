@@ -892,66 +892,50 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel_dma(KernelArgs ar
 // ---------------------------------------------------------------------------
 // fp16/bf16 kernel with direct global -> LDS loads, A copied in whole rows.
 //
-// The MAC iteration (BK = 32), the B ring and the MFMA / fragment-read
-// pattern are those of gemm_kernel_dma.  A is copied differently: one copy
-// brings k [64Q, 64Q + 64) of a row, 128 bytes, the A operand of iterations
-// 2Q and 2Q + 1 ("pair" Q).  Every A row is then fetched as whole 128-byte
-// cache lines; copying the two 64-byte halves an iteration apart fetches each
-// line twice through the vector L1 and made the pure load phase of a 4096^3
-// product ~15% slower on MI355X.
+// Here a MAC iteration is 64 deep (BK = 64): its A slab is BM rows of 128
+// bytes, whole cache lines, and it is multiplied as two 32-deep halves with
+// the MFMA / fragment-read pattern of gemm_kernel_dma.  (gemm_kernel_dma's
+// 64-byte row halves, copied an iteration apart, fetch every A line twice
+// through the vector L1; on a 4096^3 product that made its pure load phase
+// ~20% slower.)
 //
-// LDS: three A pair slots (BM rows x 128 bytes, 16-byte chunk c of row r at
-// position c ^ ((r ^ r >> 3) & 7)) followed by four B stages (32 k-rows x BN
-// values, swizzled as in gemm_kernel_dma).
+// LDS: four B stages (one per half-iteration: 32 k-rows x BN values,
+// swizzled as in gemm_kernel_dma) followed by three A slots (one per
+// iteration: BM rows x 128 bytes, 16-byte chunk c of row r at position
+// c ^ ((r ^ r >> 3) & 7)).
 //
-// Copy schedule in global iteration numbers kk: iteration kk issues the B slab
-// of kk + 3 and half (kk & 1) of A pair (kk >> 1) + 2 (half 0 = rows
-// [0, BM/2), half 1 = rows [BM/2, BM)), so every copy lands at least three
-// iterations before its first use.  Pair (kk >> 1) + 2 goes into the slot of
-// pair (kk >> 1) - 1, whose last iteration is kk - 1, and B slab kk + 3 into
-// the stage of kk - 1: both are free once every wave has passed the barrier
-// in the middle of iteration kk.  A segment [kb, ke) starts with the copies
-// that the virtual iterations (kb & ~1) - 4 .. kb - 1 would have issued.
+// Copy schedule in half-iterations t of the segment: half-iteration t issues
+// the B slab of t + 3 and half (t & 1) of the A slab of iteration (t >> 1) + 2
+// (half 0 = rows [0, BM/2), half 1 = rows [BM/2, BM)), so every copy lands at
+// least three half-iterations before its first use.  The A slab goes into
+// the slot of iteration (t >> 1) - 1, whose last half is t - 1, and B slab
+// t + 3 into the stage of t - 1: both are free once every wave has passed the
+// barrier in the middle of half-iteration t.  The segment starts with the
+// copies that half-iterations -4 .. -1 would have issued.  As in
+// gemm_kernel_dma, copies past the end of the segment read nothing and fill
+// a free slot or stage with zeros, so every wait count is a constant.
 template <int DT, int BM, int BN, int WM, int WN>
 struct PairTile {
     static constexpr int NW = WM * WN, NTH = 64 * NW;
-    static constexpr int BK = 32;
-    static constexpr int SA = 3, SB = 4;                   // A pair slots, B stages
+    static constexpr int BK = 64, HK = 32;                 // iteration and half depth
+    static constexpr int SA = 3, SB = 4;                   // A slots, B stages
     static constexpr int B_ROW = BN * 2;                   // bytes per B k-row
-    static constexpr int A_PAIR = BM * 128, B_STAGE = BK * BN * 2;
-    static constexpr int B_BASE = SA * A_PAIR;
-    static constexpr int LDS = SA * A_PAIR + SB * B_STAGE;
-    static constexpr int A_INSTR = A_PAIR / 2 / 1024 / NW; // 1 KiB copies per wave and half pair
+    static constexpr int A_SLOT = BM * 128, B_STAGE = HK * BN * 2;
+    static constexpr int A_BASE = SB * B_STAGE;
+    static constexpr int LDS = SB * B_STAGE + SA * A_SLOT;
+    static constexpr int A_INSTR = A_SLOT / 2 / 1024 / NW; // 1 KiB copies per wave and half slab
     static constexpr int B_INSTR = B_STAGE / 1024 / NW;
-    static constexpr int LPI = A_INSTR + B_INSTR;          // copies per wave and iteration
+    static constexpr int LPI = A_INSTR + B_INSTR;          // copies per wave and half-iteration
     static constexpr int WTM = BM / WM, WTN = BN / WN, MT = WTM / 32, NT = WTN / 32;
     static_assert(DT == 1 || DT == 2, "fp16 / bf16 only");
-    static_assert(A_INSTR >= 1 && A_INSTR * 2 * 1024 * NW == A_PAIR &&
+    static_assert(A_INSTR >= 1 && A_INSTR * 2 * 1024 * NW == A_SLOT &&
                       B_INSTR >= 1 && B_INSTR * 1024 * NW == B_STAGE,
                   "copies must split evenly over the waves");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0 && BN >= 128, "tile shape");
-    static_assert(2 * LPI <= 23, "wait counts");
+    static_assert(2 * LPI <= 63, "wait counts");
     static_assert(MT * NT >= LPI, "one copy per MFMA of a slab");
     static_assert(LDS <= 160 * 1024, "LDS budget");
 };
-
-// s_waitcnt vmcnt(n) for a runtime, wave-uniform n in [0, 23]; a larger n
-// waits for vmcnt(23), which is stricter and therefore still correct.
-__device__ __forceinline__ void wait_vm(int n)
-{
-#define GSK_VM(c)                                              \
-    case c:                                                    \
-        asm volatile("s_waitcnt vmcnt(" #c ")" ::: "memory"); \
-        break;
-    switch (n) {
-        GSK_VM(0) GSK_VM(1) GSK_VM(2) GSK_VM(3) GSK_VM(4) GSK_VM(5) GSK_VM(6) GSK_VM(7)
-        GSK_VM(8) GSK_VM(9) GSK_VM(10) GSK_VM(11) GSK_VM(12) GSK_VM(13) GSK_VM(14) GSK_VM(15)
-        GSK_VM(16) GSK_VM(17) GSK_VM(18) GSK_VM(19) GSK_VM(20) GSK_VM(21) GSK_VM(22)
-    default:
-        asm volatile("s_waitcnt vmcnt(23)" ::: "memory");
-    }
-#undef GSK_VM
-}
 
 __device__ __forceinline__ uint32_t swz_row128(int row) { return (uint32_t)(row ^ (row >> 3)) & 7; }
 
@@ -959,10 +943,10 @@ template <int DT, int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel_pair(KernelArgs args)
 {
     using Cfg = PairTile<DT, BM, BN, WM, WN>;
-    constexpr int NW = Cfg::NW, MT = Cfg::MT, NT = Cfg::NT;
+    constexpr int NW = Cfg::NW, MT = Cfg::MT, NT = Cfg::NT, HK = Cfg::HK;
     constexpr int A_INSTR = Cfg::A_INSTR, B_INSTR = Cfg::B_INSTR, LPI = Cfg::LPI;
-    constexpr int A_PAIR = Cfg::A_PAIR, B_STAGE = Cfg::B_STAGE, B_BASE = Cfg::B_BASE;
-    constexpr int B_ROW = Cfg::B_ROW;
+    constexpr int A_SLOT = Cfg::A_SLOT, B_STAGE = Cfg::B_STAGE, A_BASE = Cfg::A_BASE;
+    constexpr int B_ROW = Cfg::B_ROW, SA = Cfg::SA, SB = Cfg::SB;
     constexpr int NMFMA = MT * NT;  // MFMAs per slab
     constexpr int NREAD = MT + NT;  // fragment reads per slab
     static_assert(2 * NMFMA >= NREAD, "two fragment reads per MFMA");
@@ -976,12 +960,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel_pair(KernelArgs a
     const int wy = wave / WN, wx = wave - (wave / WN) * WN;
     const int half = lane >> 5, l32 = lane & 31;
     const int p = logical_wg((int32_t)blockIdx.x, P.grid, P.xcds);
-    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_address(lds));
+    const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(lds_address(lds) + wave * 1024);
 
-    // A copy j (0 .. 2*A_INSTR-1; half h issues j in [h*A_INSTR, (h+1)*A_INSTR))
-    // fills 1 KiB block j*NW + wave of a pair slot: 8 rows of 128 bytes, the
-    // lane writing position lane & 7 of row 8*block + lane/8.
-    auto a_copy_row = [&](int j) { return (j * NW + wave) * 8 + (lane >> 3); };
+    // A copy jj (0 .. 2*A_INSTR-1; half h issues jj in [h*A_INSTR, (h+1)*A_INSTR))
+    // fills 1 KiB block jj*NW + wave of a slot: 8 rows of 128 bytes, the lane
+    // writing position lane & 7 of row 8*block + lane/8.
+    auto a_copy_row = [&](int jj) { return (jj * NW + wave) * 8 + (lane >> 3); };
     int b_krow[B_INSTR], b_chunk[B_INSTR];
 #pragma unroll
     for (int j = 0; j < B_INSTR; ++j) {
@@ -991,27 +975,47 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel_pair(KernelArgs a
     }
 
     // Fragment read addresses.  A: the lane's row r0 = wy*WTM + l32 at chunk
-    // `half` (slab 0 of the first iteration of a pair).  Slab 1 is chunk + 2,
-    // the pair's second iteration chunk + 4 and block mt + 1 is 32 rows on,
-    // which flips bit 2 of the row's swizzle: bits 5 and 6 of the byte offset
-    // (XOR) and 4 KiB steps (add).
+    // `half` (slab 0 of the first half-iteration).  Slab 1 is chunk + 2, the
+    // second half-iteration chunk + 4, and block mt + 1 is 32 rows on, which
+    // flips bit 2 of the row's swizzle: bits 5 and 6 of the byte offset (XOR)
+    // and 4 KiB steps (add).  B: as in gemm_kernel_dma.
     const int r0 = wy * Cfg::WTM + l32;
-    const uint32_t a_lane = (uint32_t)(r0 * 128) + ((half ^ swz_row128(r0)) << 4);
-    // B: the lane's transposing-read address for slab 0, k-rows 8*(g/2) +
-    // (si/4) of each 16.  The swizzle depends on the k-row mod 4 only, so the
-    // other three reads of a block (4 and 16 k-rows on) are constant offsets.
-    uint32_t b_lane[NT];
+    const uint32_t a_lane = A_BASE + (uint32_t)(r0 * 128) + ((half ^ swz_row128(r0)) << 4);
+    uint32_t b_rd[NT];
     {
         const int g = lane >> 4, si = lane & 15;
         const int krow = 8 * (g >> 1) + (si >> 2);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             const int n = wx * Cfg::WTN + nt * 32 + 16 * (g & 1) + 4 * (si & 3);
-            b_lane[nt] = B_BASE + krow * B_ROW + (((n >> 3) ^ swz_b(krow)) << 4) + (n & 7) * 2;
+            b_rd[nt] = krow * B_ROW + (((n >> 3) ^ swz_b(krow)) << 4) + (n & 7) * 2;
         }
     }
+    // slot_off: A slot byte offset (runtime); odd, st, s: compile-time
+    auto read_a = [&](uint32_t slot_off, int odd, int st, int mt) {
+        const uint32_t x = (uint32_t)((st << 5) | ((odd ^ (mt & 1)) << 6));
+        return *(const u32x4 *)(lds + slot_off + mt * 4096 + (a_lane ^ x));
+    };
+    auto read_b = [&](int s, int st, int nt) {
+        const uint8_t *base = lds + b_rd[nt] + s * B_STAGE + st * 16 * B_ROW;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(GSK_LDS(i16x4, base));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(GSK_LDS(i16x4, base + 4 * B_ROW));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        return u32x4{l2[0], l2[1], h2[0], h2[1]};
+    };
+    // Fragment read r of a slab in the order its MFMAs first need them.
+    auto read_frag = [&](uint32_t slot_off, int odd, int s, int st, int r, u32x4 (&fa)[MT],
+                         u32x4 (&fb)[NT]) {
+        if (r == 0)
+            fa[0] = read_a(slot_off, odd, st, 0);
+        else if (r <= NT)
+            fb[r - 1] = read_b(s, st, r - 1);
+        else
+            fa[r - NT] = read_a(slot_off, odd, st, r - NT);
+    };
 
     f32x16 acc[MT][NT];
+    u32x4 fa0[MT], fb0[NT], fa1[MT], fb1[NT];
 
     WorkCursor cur = work_begin(P, p);
     WorkItem w;
@@ -1019,11 +1023,19 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel_pair(KernelArgs a
         int tm, tn;
         tile_coords(P, w.tile, &tm, &tn);
         const int m0 = tm * BM, n0 = tn * BN;
-        const int kb = w.kb, ke = w.ke;
-        // k range of this segment: copies outside it read nothing (zeros).
-        const int k_lo = kb * Cfg::BK;
-        const int k_hi = ke * Cfg::BK < args.K ? ke * Cfg::BK : args.K;
+        const int k_lo = w.kb * Cfg::BK;
+        const int k_hi = w.ke * Cfg::BK < args.K ? w.ke * Cfg::BK : args.K;
+        const int n = (k_hi - k_lo + HK - 1) / HK;  // half-iterations of this item (>= 1)
 
+        uint32_t a_off[2 * A_INSTR];
+#pragma unroll
+        for (int jj = 0; jj < 2 * A_INSTR; ++jj) {
+            const int row = a_copy_row(jj);
+            a_off[jj] = m0 + row < args.M
+                            ? (uint32_t)(row * args.lda * 2 +
+                                         (((lane & 7) ^ (int)swz_row128(row)) << 4))
+                            : kOutOfRange;
+        }
         uint32_t b_off[B_INSTR];
 #pragma unroll
         for (int j = 0; j < B_INSTR; ++j)
@@ -1031,56 +1043,37 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel_pair(KernelArgs a
                            ? (uint32_t)(b_krow[j] * args.ldb * 2 + b_chunk[j] * 16)
                            : kOutOfRange;
 
-        // The copies of (virtual) iteration v: half (v & 1) of A pair
-        // (v >> 1) + 2 into pair slot sa_fill, and the B slab of v + 3 into
-        // stage sb_fill.  Every iteration issues all LPI of them, so the wait
-        // counts below are constants; a copy whose k lies outside [k_lo, k_hi)
-        // reads nothing and fills its (unused) slot or stage with zeros.
-        auto copy_a = [&](int v, int sa_fill, int j) {
-            const int q = (v >> 1) + 2;
-            const int jj = (v & 1) * A_INSTR + j;
-            const int k0 = 64 * q;
-            const int live = k0 < k_hi;
-            const int row = a_copy_row(jj);
-            const int chunk = (lane & 7) ^ (int)swz_row128(row);
-            const i32x4 ra =
-                rsrc_words(args.A + ((int64_t)m0 * args.lda + (live ? k0 : 0)) * 2);
-            copy16(ra,
-                   live && m0 + row < args.M && chunk * 8 < k_hi - k0
-                       ? (uint32_t)(row * args.lda * 2 + chunk * 16)
-                       : kOutOfRange,
-                   lds0 + sa_fill * A_PAIR + (jj * NW + wave) * 1024);
+        // Next A slab to copy (its k and source; the pointer stops at the
+        // item's last slab) and next B half-slab (likewise).
+        int ka = k_lo;
+        const uint8_t *a_cp = args.A + ((int64_t)m0 * args.lda + k_lo) * 2;
+        int kbh = k_lo;
+        const uint8_t *b_cp = args.B + ((int64_t)k_lo * args.ldb + n0) * 2;
+        const int64_t b_step = (int64_t)HK * args.ldb * 2;
+
+        // Copies of one half-iteration: half h of the next A slab into slot
+        // `a_slot`, then the next B half-slab into stage s_fill.
+        auto copy_a = [&](int h, uint32_t a_slot_off, int j) {
+            const int jj = h * A_INSTR + j;
+            const bool whole = ka + Cfg::BK <= k_hi;
+            const int chunk = (lane & 7) ^ (int)swz_row128(a_copy_row(jj));
+            const uint32_t off = whole || chunk * 8 < k_hi - ka ? a_off[jj] : kOutOfRange;
+            copy16(rsrc_words(a_cp), off, lds_wave + A_BASE + a_slot_off + jj * NW * 1024);
         };
-        auto copy_b = [&](int v, int sb_fill, int j) {
-            const int k0 = (v + 3) * Cfg::BK;
-            const int live = k0 >= k_lo && k0 < k_hi;
-            const i32x4 rb =
-                rsrc_words(args.B + ((int64_t)(live ? k0 : 0) * args.ldb + n0) * 2);
-            copy16(rb, live && b_krow[j] < k_hi - k0 ? b_off[j] : kOutOfRange,
-                   lds0 + B_BASE + sb_fill * B_STAGE + (j * NW + wave) * 1024);
+        auto next_a = [&]() {
+            if (ka + Cfg::BK < k_hi)
+                a_cp += Cfg::BK * 2;
+            ka += Cfg::BK;
         };
-        auto read_a = [&](int slot, int odd, int st, int mt) {
-            const uint32_t x = (uint32_t)((st << 5) | ((odd ^ (mt & 1)) << 6));
-            return *(const u32x4 *)(lds + slot * A_PAIR + mt * 4096 + (a_lane ^ x));
+        auto copy_b = [&](int s_fill, int j) {
+            const bool whole = kbh + HK <= k_hi;
+            const uint32_t off = whole || b_krow[j] < k_hi - kbh ? b_off[j] : kOutOfRange;
+            copy16(rsrc_words(b_cp), off, lds_wave + s_fill * B_STAGE + j * NW * 1024);
         };
-        auto read_b = [&](int s, int st, int nt) {
-            const uint8_t *base = lds + s * B_STAGE + b_lane[nt] + st * 16 * B_ROW;
-            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(GSK_LDS(i16x4, base));
-            const i16x4 hi =
-                __builtin_amdgcn_ds_read_tr16_b64_v4i16(GSK_LDS(i16x4, base + 4 * B_ROW));
-            const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-            return u32x4{l2[0], l2[1], h2[0], h2[1]};
-        };
-        // Fragment read r of slab st, in the order the slab's MFMAs first
-        // need them: A block 0, B blocks 0 .. NT-1, A blocks 1 .. MT-1.
-        auto read_frag = [&](int slot, int odd, int s, int st, int r, u32x4 (&fa)[MT],
-                             u32x4 (&fb)[NT]) {
-            if (r == 0)
-                fa[0] = read_a(slot, odd, st, 0);
-            else if (r <= NT)
-                fb[r - 1] = read_b(s, st, r - 1);
-            else
-                fa[r - NT] = read_a(slot, odd, st, r - NT);
+        auto next_b = [&]() {
+            if (kbh + HK < k_hi)
+                b_cp += b_step;
+            kbh += HK;
         };
 
 #pragma unroll
@@ -1089,84 +1082,99 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel_pair(KernelArgs a
             for (int nt = 0; nt < NT; ++nt)
                 acc[mt][nt] = f32x16{};
 
-        // Slots and stages are numbered from the segment's first pair and
-        // iteration.  Pair q = (kb >> 1) + d sits in slot d % 3; B slab kk in
-        // stage (kk - kb) % 4.
         // All waves are done with the previous item's slots before refilling.
         barrier_only();
-        {
-            const int vb = (kb & ~1) - 4;  // pairs (kb >> 1) and on
-            for (int v = vb; v < kb; ++v) {
-                const int sa_fill = ((v - vb) >> 1) % Cfg::SA;
-                const int sb_fill = (v + 3 - kb) & (Cfg::SB - 1);
+        // half-iterations -4 .. -1: A slabs 0 and 1 into slots 0 and 1, B
+        // half-slabs -1 (nothing to read) .. 2 into stages 3, 0, 1, 2
+        static_for<0, 4>([&](auto u) {
+            constexpr int h = u.value & 1;
 #pragma unroll
-                for (int j = 0; j < A_INSTR; ++j)
-                    copy_a(v, sa_fill, j);
+            for (int j = 0; j < A_INSTR; ++j)
+                copy_a(h, (u.value >> 1) * A_SLOT, j);
+            if (h)
+                next_a();
+            if constexpr (u.value == 0) {
+                // half-slab -1: nothing to read, a zero fill keeps the count
 #pragma unroll
                 for (int j = 0; j < B_INSTR; ++j)
-                    copy_b(v, sb_fill, j);
+                    copy16(rsrc_words(b_cp), kOutOfRange,
+                           lds_wave + (SB - 1) * B_STAGE + j * NW * 1024);
+            } else {
+#pragma unroll
+                for (int j = 0; j < B_INSTR; ++j)
+                    copy_b(u.value - 1, j);
+                next_b();
             }
-        }
-        // Iteration kb's copies were issued by virtual iterations <= kb - 3.
-        wait_copies<LPI>(2);
+        });
+        wait_vmcnt<2 * LPI>();  // half-iteration 0's copies have landed
         barrier_only();
 
-        int sa = 0;                   // pair slot of the current iteration
-        int sb = 0;                   // B stage of the current iteration
-        int odd = kb & 1;             // the current iteration is the second of its pair
-        int sa_fill = 2;              // slot of pair (kk >> 1) + 2
-        u32x4 fa0[MT], fb0[NT], fa1[MT], fb1[NT];
+        uint32_t sa_off = 0;             // slot of the current A slab
+        uint32_t fill_off = 2 * A_SLOT;  // slot of the slab two ahead
 #pragma unroll
         for (int r = 0; r < NREAD; ++r)
-            read_frag(sa, odd, sb, 0, r, fa0, fb0);
+            read_frag(sa_off, 0, 0, 0, r, fa0, fb0);
 
-        for (int kk = kb; kk < ke; ++kk) {
-            const int sa_next = odd ? (sa + 1 == Cfg::SA ? 0 : sa + 1) : sa;
-            const int sb_next = (sb + 1) & (Cfg::SB - 1);
-            const int sb_fill = (sb + 3) & (Cfg::SB - 1);  // stage of kk - 1 = stage of kk + 3
-            // (a) first slab's MFMAs, the second slab's fragment reads between
+        // Half-iteration t (B stage t mod 4 and parity t mod 2 are
+        // compile-time constants here); `surely_more` says at compile time
+        // that another half-iteration follows.
+        auto step = [&](int t, auto u_c, auto surely_more) {
+            constexpr int u = decltype(u_c)::value;
+            constexpr int odd = u & 1, s = u & (SB - 1);
+            constexpr int s_next = (s + 1) & (SB - 1), s_fill = (s + SB - 1) & (SB - 1);
+            const uint32_t sa_next = odd ? (sa_off + A_SLOT == SA * A_SLOT ? 0 : sa_off + A_SLOT)
+                                         : sa_off;
+            // (a) first slab's MFMAs, the second slab's reads between
 #pragma unroll
             for (int j = 0; j < NMFMA; ++j) {
                 mfma_step<DT>(acc[j / NT][j % NT], fb0[j % NT], fa0[j / NT]);
 #pragma unroll
                 for (int r = 2 * j; r < 2 * j + 2 && r < NREAD; ++r)
-                    read_frag(sa, odd, sb, 1, r, fa1, fb1);
+                    read_frag(sa_off, odd, s, 1, r, fa1, fb1);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            const bool more = kk + 1 < ke;
+            const bool more = decltype(surely_more)::value || t + 1 < n;
             if (more) {
-                // (b) iteration kk + 1's copies are complete in every wave (only
-                //     those of iteration kk - 1 may still be in flight), and
-                //     every wave is past iteration kk - 1's slot and stage
-                wait_copies<LPI>(1);
+                // (b) half-iteration t + 1's copies are complete in every wave
+                //     (only those of t - 1 may be in flight), and every wave
+                //     is past t - 1's slot and stage
+                wait_vmcnt<LPI>();
                 barrier_only();
             }
-            // (c) second slab's MFMAs, with the next iteration's first-slab
-            //     reads (unconditional: on the last iteration they are
-            //     harmless, and a fixed count lets the compiler wait for just
-            //     the fragments each MFMA needs) and this iteration's copies.
-            //     The last iteration issues no copies: without the barrier
-            //     above other waves may still be reading.
+            // (c) second slab's MFMAs, with the next half-iteration's
+            //     first-slab reads and this half-iteration's copies (none on
+            //     the last one: without the barrier others may still read)
 #pragma unroll
             for (int j = 0; j < NMFMA; ++j) {
                 mfma_step<DT>(acc[j / NT][j % NT], fb1[j % NT], fa1[j / NT]);
 #pragma unroll
                 for (int r = 2 * j; r < 2 * j + 2 && r < NREAD; ++r)
-                    read_frag(sa_next, odd ^ 1, sb_next, 0, r, fa0, fb0);
+                    read_frag(sa_next, odd ^ 1, s_next, 0, r, fa0, fb0);
                 if (more && j >= NMFMA - LPI) {
-                    if (j - (NMFMA - LPI) < A_INSTR)
-                        copy_a(kk, sa_fill, j - (NMFMA - LPI));
+                    const int c = j - (NMFMA - LPI);
+                    if (c < A_INSTR)
+                        copy_a(odd, fill_off, c);
                     else
-                        copy_b(kk, sb_fill, j - (NMFMA - LPI) - A_INSTR);
+                        copy_b(s_fill, c - A_INSTR);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
-            if (odd)
-                sa_fill = sa_fill + 1 == Cfg::SA ? 0 : sa_fill + 1;
-            sa = sa_next;
-            sb = sb_next;
-            odd ^= 1;
-        }
+            if (more) {
+                if (odd) {
+                    next_a();
+                    fill_off = fill_off + A_SLOT == SA * A_SLOT ? 0 : fill_off + A_SLOT;
+                }
+                next_b();
+            }
+            sa_off = sa_next;
+        };
+        int t = 0;
+        for (; t + SB <= n; t += SB)
+            static_for<0, SB>([&](auto u) { step(t + u.value, u, IC<(u.value < SB - 1)>{}); });
+        static_for<0, SB - 1>([&](auto u) {
+            if (t + u.value < n)
+                step(t + u.value, u, IC<0>{});
+        });
 
         finish_tile<BM, BN, MT, NT>(acc, args, w, p, m0, n0, wave, lane, wy * Cfg::WTM,
                                     wx * Cfg::WTN);
@@ -1213,7 +1221,7 @@ static int launch_gemm_pair(const KernelArgs &args, int grid, hipStream_t stream
 
 // Direct-to-LDS ring kernel with whole-row A copies (fp16/bf16)
 #define GSK_PAIR(DT, BM, BN, WM, WN)                                                             \
-    Variant{DT, BM, BN, 32, WM, WN, PairTile<DT, BM, BN, WM, WN>::NTH,                           \
+    Variant{DT, BM, BN, 64, WM, WN, PairTile<DT, BM, BN, WM, WN>::NTH,                           \
             (size_t)PairTile<DT, BM, BN, WM, WN>::LDS, 2, PairTile<DT, BM, BN, WM, WN>::SB,       \
             &launch_gemm_pair<DT, BM, BN, WM, WN>,                                               \
             (const void *)&gemm_kernel_pair<DT, BM, BN, WM, WN>}

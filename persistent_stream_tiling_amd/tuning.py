@@ -3,7 +3,7 @@
 The benchmark times exactly these, and the full-size GPU parity tests run
 exactly these, so what is measured is what is checked.
 """
-from ._lib import FLAG_A_ROW_PAIRS
+from ._lib import FLAG_NO_XCD_REMAP
 
 SCHEDULES = ("dp", "persistent", "streamk", "hybrid")
 
@@ -19,19 +19,21 @@ _DEFAULTS = {
 BENCH_TILES = {
     # 16 tiles of 64x64 (the configuration names this tile)
     "fp32_256": {s: dict(bm=64, bn=64) for s in SCHEDULES},
-    # 256 tiles of 256x256: exactly one tile per CU
-    "fp16_4096": {s: dict(bm=256, bn=256, stages=5) for s in SCHEDULES},
+    # 256 tiles of 256x256: exactly one tile per CU; 4-row tile bands, hardware
+    # workgroup order across the dies
+    "fp16_4096": {s: dict(bm=256, bn=256, group_m=4, flags=FLAG_NO_XCD_REMAP) for s in SCHEDULES},
     # Tile-per-workgroup schedules: 144 tiles of 128x128 on 256 CUs.  Stream-K
     # and hybrid: 36 tiles of 256x256, each split over ~7 workgroups.
     "fp16_1536x1536x8192": dict(dp=dict(bm=128, bn=128), persistent=dict(bm=128, bn=128),
                                 streamk=dict(bm=256, bn=256), hybrid=dict(bm=256, bn=256)),
     # 64 tiles of 64x64 for the tile-per-workgroup schedules; Stream-K and
-    # hybrid: 8 tiles of 256x128, each split over 32 workgroups, A copied in
-    # whole rows.
+    # hybrid: 8 tiles of 256x128, each split over 32 workgroups.
     "bf16_512x512x65536": dict(dp=dict(bm=64, bn=64), persistent=dict(bm=64, bn=64),
-                               streamk=dict(bm=256, bn=128, wave_m=4, wave_n=2, flags=FLAG_A_ROW_PAIRS),
-                               hybrid=dict(bm=256, bn=128, wave_m=4, wave_n=2, flags=FLAG_A_ROW_PAIRS)),
-    "bf16_8192x28672x8192": {s: dict(bm=256, bn=256, stages=5) for s in SCHEDULES},
+                               streamk=dict(bm=256, bn=128, wave_m=4, wave_n=2),
+                               hybrid=dict(bm=256, bn=128, wave_m=4, wave_n=2)),
+    # 3584 tiles of 256x256 (14 per CU)
+    "bf16_8192x28672x8192": dict(dp=dict(bm=256, bn=256), persistent=dict(bm=256, bn=256, group_m=4),
+                                 streamk=dict(bm=256, bn=256), hybrid=dict(bm=256, bn=256)),
 }
 
 

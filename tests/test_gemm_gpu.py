@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 from gpu_util import compare, run_gemm, to_device
-from persistent_stream_tiling_amd import FLAG_A_ROW_PAIRS, inputs, tuning
+from persistent_stream_tiling_amd import FLAG_A_HALF_ROWS, inputs, tuning
 
 pytestmark = pytest.mark.gpu
 
@@ -27,12 +27,12 @@ SMALL = [
     (300, 200, 704),   # ragged M and N; K a multiple of 8 (no repack)
     (257, 203, 701),   # ragged everything; rows not 16-byte multiples (repacked)
 ]
-ROWS = FLAG_A_ROW_PAIRS  # the ring kernel that copies A in whole rows
+HALF = FLAG_A_HALF_ROWS  # the 32-deep ring kernel that copies A in row halves
 TILES = {"f16": [dict(bm=64, bn=64), dict(bm=128, bn=128), dict(bm=256, bn=128),
-                 dict(bm=128, bn=256), dict(bm=256, bn=256), dict(bm=128, bn=128, flags=ROWS),
-                 dict(bm=256, bn=128, flags=ROWS), dict(bm=256, bn=256, flags=ROWS)],
+                 dict(bm=128, bn=256), dict(bm=256, bn=256), dict(bm=128, bn=128, flags=HALF),
+                 dict(bm=256, bn=128, flags=HALF), dict(bm=256, bn=256, flags=HALF)],
          "bf16": [dict(bm=64, bn=64), dict(bm=128, bn=128), dict(bm=256, bn=256),
-                  dict(bm=256, bn=128, wave_m=4, wave_n=2, flags=ROWS)],
+                  dict(bm=256, bn=128, wave_m=4, wave_n=2, flags=HALF)],
          "f32": [dict(bm=64, bn=64), dict(bm=128, bn=128)]}
 
 
@@ -90,7 +90,7 @@ def test_stream_k_long_k_integer_exact():
     da, db = to_device(a, "bf16"), to_device(b, "bf16")
     import persistent_stream_tiling_amd as gsk
     for tiles in (dict(bm=128, bn=128), dict(bm=64, bn=64), dict(bm=256, bn=256),
-                  dict(bm=256, bn=128, flags=ROWS)):
+                  dict(bm=256, bn=128, flags=HALF)):
         for g in (256, 100, 3):
             for flag in (gsk.FLAG_FIXUP_HEAD, gsk.FLAG_FIXUP_SPLIT):
                 t = dict(tiles)
@@ -101,8 +101,8 @@ def test_stream_k_long_k_integer_exact():
 
 
 @pytest.mark.parametrize("tiles", [dict(bm=128, bn=128), dict(bm=256, bn=256), dict(bm=64, bn=64),
-                                   dict(bm=256, bn=128, flags=ROWS)],
-                         ids=lambda t: f"{t['bm']}x{t['bn']}" + ("-rows" if t.get("flags") else ""))
+                                   dict(bm=256, bn=128, flags=HALF)],
+                         ids=lambda t: f"{t['bm']}x{t['bn']}" + ("-half" if t.get("flags") else ""))
 def test_split_and_head_fixups_agree_bitwise(tiles):
     # both fixups add every element's pieces in ascending k order
     M, N, K = 512, 384, 16384
