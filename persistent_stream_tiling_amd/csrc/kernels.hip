@@ -161,44 +161,66 @@ __device__ __forceinline__ void lds_store_words(uint8_t *p, const uint32_t *w)
 // 32*nt.. of the tile) to C through a buffer descriptor based at the tile's
 // first row; an element outside C gets an out-of-range offset so its write is
 // dropped: no branches around the stores.
+__device__ __forceinline__ void store_quad(const f32x4 &v, const KernelArgs &args,
+                                           __amdgpu_buffer_rsrc_t c_rsrc, int m0, int n0, int row,
+                                           int col, int half, int g)
+{
+    const bool row_ok = m0 + row < args.M;
+    const int n = n0 + col + 8 * g + 4 * half;
+    const uint32_t off = (uint32_t)((row * args.ldc + n) * 4);
+    const u32x4 u = u32x4{bits_of(v[0]), bits_of(v[1]), bits_of(v[2]), bits_of(v[3])};
+    if (args.c_vec) {
+        // N % 4 == 0: a vector is either wholly inside C or wholly outside
+        __builtin_amdgcn_raw_buffer_store_b128(u, c_rsrc,
+                                               (int)(row_ok && n < args.N ? off : kOutOfRange),
+                                               0, 0);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            __builtin_amdgcn_raw_buffer_store_b32(
+                u[e], c_rsrc, (int)(row_ok && n + e < args.N ? off + 4 * e : kOutOfRange), 0, 0);
+    }
+}
+
 __device__ __forceinline__ void store_block(const f32x16 &blk, const KernelArgs &args,
                                             __amdgpu_buffer_rsrc_t c_rsrc, int m0, int n0,
                                             int row, int col, int half)
 {
-    const bool row_ok = m0 + row < args.M;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        const int n = n0 + col + 8 * g + 4 * half;
-        const uint32_t off = (uint32_t)((row * args.ldc + n) * 4);
-        const u32x4 u = u32x4{bits_of(blk[4 * g]),
-                              bits_of(blk[4 * g + 1]),
-                              bits_of(blk[4 * g + 2]),
-                              bits_of(blk[4 * g + 3])};
-        if (args.c_vec) {
-            // N % 4 == 0: a vector is either wholly inside C or wholly outside
-            __builtin_amdgcn_raw_buffer_store_b128(u, c_rsrc,
-                                                   (int)(row_ok && n < args.N ? off : kOutOfRange),
-                                                   0, 0);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                __builtin_amdgcn_raw_buffer_store_b32(
-                    u[e], c_rsrc, (int)(row_ok && n + e < args.N ? off + 4 * e : kOutOfRange), 0,
-                    0);
-        }
-    }
+    for (int g = 0; g < 4; ++g)
+        store_quad(f32x4{blk[4 * g], blk[4 * g + 1], blk[4 * g + 2], blk[4 * g + 3]}, args,
+                   c_rsrc, m0, n0, row, col, half, g);
 }
 
-// Wait (thread 0) until flags[slot] is set; bounded, see spin_limit.
-__device__ __forceinline__ void wait_flag(const KernelArgs &args, int32_t slot)
+// Wave 0 waits until the flags of workgroups q_first .. q_last are all set;
+// slot_of(q) gives a workgroup's flag slot.  The lanes poll up to 64 flags at
+// once, so many pieces cost one memory round trip, not one each.  With
+// `clear`, each consumed flag is reset for the next run.  Bounded: after
+// spin_limit rounds the status word is set and the wait gives up.
+template <typename SlotOf>
+__device__ __forceinline__ void wait_flags(const KernelArgs &args, int32_t q_first,
+                                           int32_t q_last, SlotOf slot_of, bool clear)
 {
-    int spins = 0;
-    while (__hip_atomic_load(args.flags + slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
-        if (++spins > args.spin_limit) {
-            __hip_atomic_store(args.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            break;
+    const int lane = threadIdx.x & 63;
+    for (int32_t q0 = q_first; q0 <= q_last; q0 += 64) {
+        const int32_t q = q0 + lane;
+        const bool mine = q <= q_last;
+        int32_t *flag = args.flags + (mine ? slot_of(q) : 0);
+        int spins = 0;
+        for (;;) {
+            const bool ready =
+                !mine || __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+            if (__builtin_amdgcn_ballot_w64(!ready) == 0)
+                break;
+            if (++spins > args.spin_limit) {
+                if (lane == 0)
+                    __hip_atomic_store(args.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
         }
-        __builtin_amdgcn_s_sleep(2);
+        if (clear && mine)
+            __hip_atomic_store(flag, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -256,13 +278,9 @@ __device__ __forceinline__ void finish_tile(f32x16 (&acc)[MT][NT], const KernelA
     if (w.role == ROLE_OWNER) {
         // Head of a split tile: wait for every later workgroup on the tile,
         // then add their partials in ascending workgroup (= ascending k) order.
-        if (tid == 0) {
-            for (int q = p + 1; q <= w.peer_last; ++q) {
-                wait_flag(args, q);
-                // Consumed: leave the flag clear for the next run.
-                __hip_atomic_store(args.flags + q, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-        }
+        // (consumed flags are cleared for the next run)
+        if (wave == 0)
+            wait_flags(args, p + 1, w.peer_last, [](int32_t q) { return q; }, true);
         // the partials are read below with agent-coherent loads issued after
         // the flags were seen
         __syncthreads();
@@ -324,9 +342,8 @@ __device__ __forceinline__ void reduce_split_tiles(const KernelArgs &args, int p
         const int32_t parts = pl - pf + 1;
         int32_t b0, b1;
         split_share(p - pf, parts, NBLK, &b0, &b1);
-        if (tid == 0)
-            for (int32_t q = pf; q <= pl; ++q)
-                wait_flag(args, split_slot(q, q == pf));
+        if (wave == 0)
+            wait_flags(args, pf, pl, [pf](int32_t q) { return split_slot(q, q == pf); }, false);
         __syncthreads();
         int tm, tn;
         tile_coords(P, t, &tm, &tn);
@@ -334,32 +351,34 @@ __device__ __forceinline__ void reduce_split_tiles(const KernelArgs &args, int p
         const __amdgpu_buffer_rsrc_t c_rsrc = make_rsrc(args.C + (int64_t)m0 * args.ldc);
         const __amdgpu_buffer_rsrc_t slots = make_rsrc(args.partials);
         const uint32_t slot_bytes = (uint32_t)(BM * BN * 4);
-        for (int b = b0 + wave; b < b1; b += NW) {
+        // Work units: quarter blocks (4 floats per lane, 1 KiB per piece),
+        // dealt to the waves.  A unit's pieces are loaded QB at a time, all in
+        // flight together, then added in ascending order.
+        constexpr int QB = 16;
+        const int units = (b1 - b0) * 4;
+        for (int u = wave; u < units; u += NW) {
+            const int b = b0 + (u >> 2), g = u & 3;
             const int ww = b / (MT * NT), mt = (b / NT) % MT, nt = b % NT;
-            const uint32_t frag_off = (uint32_t)(b * 4 * 64 + lane) * 16;
-            f32x16 blk;
-            for (int32_t q = pf; q <= pl; ++q) {
-                const uint32_t off = (uint32_t)split_slot(q, q == pf) * slot_bytes + frag_off;
+            const uint32_t frag_off = (uint32_t)(b * 4 * 64 + lane) * 16 + g * 1024;
+            f32x4 sum = f32x4{};
+            for (int32_t q0 = pf; q0 <= pl; q0 += QB) {
+                f32x4 v[QB];
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const f32x4 v = __builtin_bit_cast(
-                        f32x4, __builtin_amdgcn_raw_buffer_load_b128(slots, (int)off, g * 1024,
-                                                                     kAgentCoherent));
-                    if (q == pf) {
-                        blk[4 * g] = v[0];
-                        blk[4 * g + 1] = v[1];
-                        blk[4 * g + 2] = v[2];
-                        blk[4 * g + 3] = v[3];
-                    } else {
-                        blk[4 * g] += v[0];
-                        blk[4 * g + 1] += v[1];
-                        blk[4 * g + 2] += v[2];
-                        blk[4 * g + 3] += v[3];
-                    }
-                }
+                for (int i = 0; i < QB; ++i)
+                    if (q0 + i <= pl)
+                        v[i] = __builtin_bit_cast(
+                            f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                       slots,
+                                       (int)((uint32_t)split_slot(q0 + i, q0 + i == pf) *
+                                                 slot_bytes + frag_off),
+                                       0, kAgentCoherent));
+#pragma unroll
+                for (int i = 0; i < QB; ++i)
+                    if (q0 + i <= pl)
+                        sum = q0 + i == pf ? v[i] : sum + v[i];
             }
-            store_block(blk, args, c_rsrc, m0, n0, (ww / WN) * WTM + mt * 32 + l32,
-                        (ww % WN) * WTN + nt * 32, half);
+            store_quad(sum, args, c_rsrc, m0, n0, (ww / WN) * WTM + mt * 32 + l32,
+                       (ww % WN) * WTN + nt * 32, half, g);
         }
         // this workgroup's reads of the tile's slots are complete (their values
         // are already summed) before it counts itself done
