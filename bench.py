@@ -60,12 +60,15 @@ def algorithmic_bytes(M, N, K, dtype, plan_info):
 
 
 def partial_bytes(plan):
-    """Bytes of Stream-K partial tiles written (and read back) by one run."""
+    """Bytes of Stream-K partial tiles written (and read back) by one run: every
+    piece that does not start at k = 0, plus, with the split fixup, the head
+    pieces of split tiles (which are parked too)."""
     info = plan.info
+    parked = (1, 2) if info["split_fixup"] else (1,)
     n = 0
     for w in range(info["launch_grid"] if info["tiles_sk"] else 0):
         for (_, _, _, role, _) in plan.segments(w):
-            if role == 1:
+            if role in parked:
                 n += 1
     return n * info["bm"] * info["bn"] * 4
 
