@@ -115,6 +115,57 @@ def cpu_baseline(a_bits, b_bits, M, N, K, dtype, seed, target_s):
         (rows, cols, ref, scale)
 
 
+def schedule_table(args, out):
+    """Median time of every schedule (tuned tiles, default grid) per workload, the
+    schedules interleaved round by round so that clock drift hits all alike."""
+    import torch
+    import persistent_stream_tiling_amd as gsk
+    from persistent_stream_tiling_amd import inputs, tuning
+    table = workload_table()
+    names = sorted(inputs.irregular_workloads()) if args.workload == "irregular" \
+        else args.workload.split(",")
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    rounds, per = 4, max(1, args.steps // 4)
+    lines = [f"# Schedules per workload: `python bench.py --workload {args.workload} "
+             f"--steps {args.steps} --table <file>`", "",
+             f"Kernel source hash: {kernel_source_hash()}.  Median of {rounds * per} timed runs per "
+             "schedule (rounds interleaved, 512 MiB cache flush before each run), tuned tiles, "
+             "default grid (one workgroup per CU).", "",
+             "| workload | M x N x K | tiles T | dp us | persistent us | Stream-K us | hybrid us "
+             "| best | best TFLOP/s | Stream-K / DP | hybrid / DP |",
+             "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for name in names:
+        wl = table[name]
+        M, N, K, dt = wl["M"], wl["N"], wl["K"], wl["dtype"]
+        log(f"[table] {name}: {M}x{N}x{K} {dt}")
+        a_bits, b_bits = inputs.operands(M, N, K, dt, wl["dist"], wl["seed"], wl["scale"])
+        a, b = to_device(a_bits, dt), to_device(b_bits, dt)
+        c = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        runs = {}
+        for sched in SCHEDULES:
+            plan = gsk.GemmPlan(M, N, K, dt, sched, **tuning.bench_tiles(name, sched, dt))
+            ws = plan.new_workspace()
+            plan.run(a, b, c, ws)
+            runs[sched] = (plan, ws, [])
+        torch.cuda.synchronize()
+        for _ in range(rounds):
+            for sched, (plan, ws, times) in runs.items():
+                ms, _ = time_schedule(plan, a, b, c, ws, per, 1, flush)
+                times.extend(ms.tolist())
+        med = {s: float(np.median(v[2])) * 1e3 for s, v in runs.items()}
+        best = min(med, key=med.get)
+        T = runs["dp"][0].info["tiles"]
+        lines.append(f"| {name} | {M} x {N} x {K} | {T} | " +
+                     " | ".join(f"{med[s]:.1f}" for s in SCHEDULES) +
+                     f" | {best} | {2.0 * M * N * K / (med[best] * 1e-6) / 1e12:.0f} | "
+                     f"{med['dp'] / med['streamk']:.2f} | {med['dp'] / med['hybrid']:.2f} |")
+        del a, b, c, runs
+        torch.cuda.empty_cache()
+    text = "\n".join(lines) + "\n"
+    open(out, "w").write(text)
+    log(text)
+
+
 def load_traffic(workload, schedule):
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
@@ -139,6 +190,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--report", default=None, help="also append per-schedule records here")
+    ap.add_argument("--table", default=None, metavar="FILE",
+                    help="no JSON line: time the four schedules on each of the workloads named by "
+                         "--workload (comma-separated, or 'irregular' for the seeded irregular "
+                         "shapes) and write a markdown table to FILE")
     ap.add_argument("--traffic-run", default=None, metavar="SCHEDULE",
                     help="no timing: run a 256 MiB device copy, then this schedule's GEMM, "
                          "three times each (for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)")
@@ -157,6 +212,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+    if args.table:
+        schedule_table(args, args.table)
+        return
     wl = workload_table()[args.workload]
     M, N, K, dt = wl["M"], wl["N"], wl["K"], wl["dtype"]
     log(f"[bench] {args.workload}: {M}x{N}x{K} {dt} {wl['dist']} seed {wl['seed']}")

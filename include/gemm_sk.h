@@ -75,12 +75,14 @@ enum {
     /* fp16/bf16: use the kernel that stages A and B through registers (bk 64)
      * instead of the direct-to-LDS ring kernel (bk 32). */
     GEMM_FLAG_REGISTER_STAGED = 1u << 2,
-    /* Stream-K fixup mode (default: split when some tile is cut into three or
-     * more pieces, else head-adds):
+    /* Stream-K fixup mode (default: split whenever some tile is cut):
      *  HEAD  the workgroup holding a split tile's k = 0 adds the other pieces
      *        one by one and stores the tile;
      *  SPLIT every piece is parked in the workspace; after their MAC work the
      *        tile's workgroups each add up and store a share of its blocks.
+     *        A workgroup then walks its range as whole tiles, head piece, tail
+     *        piece, so that workgroups running side by side read the same k
+     *        range of A and B at the same time.
      * Both add the pieces of every element in ascending k order, so they give
      * identical bits. */
     GEMM_FLAG_FIXUP_HEAD = 1u << 3,

@@ -227,7 +227,8 @@ gemm_plan *create(int64_t M, int64_t N, int64_t K, gemm_dtype dtype, gemm_schedu
             delete p;
             return nullptr;
         }
-        // Fixup mode: split when some tile is cut into three or more pieces.
+        // Fixup mode: split (with the k-aligned walk) whenever some tile is cut;
+        // head mode only when asked for.
         p->max_pieces = 1;
         for (int32_t t = 0; t < P.T_sk; ++t) {
             int32_t f, l;
@@ -240,7 +241,8 @@ gemm_plan *create(int64_t M, int64_t N, int64_t K, gemm_dtype dtype, gemm_schedu
         else if (t.flags & GEMM_FLAG_FIXUP_HEAD)
             p->split_fixup = 0;
         else
-            p->split_fixup = p->max_pieces >= 3;
+            p->split_fixup = p->max_pieces >= 2;
+        P.k_aligned = p->split_fixup;
         const int64_t slots = p->split_fixup ? 2 * (int64_t)g : g;
         if (slots * var->bm * var->bn * 4 >= ((int64_t)1 << 31)) {
             set_error("Stream-K grid %d too large for the partial-tile workspace indexing", g);
@@ -251,6 +253,7 @@ gemm_plan *create(int64_t M, int64_t N, int64_t K, gemm_dtype dtype, gemm_schedu
         P.q = P.r = 0;
         p->max_pieces = 1;
         p->split_fixup = 0;
+        P.k_aligned = 0;
     }
 
     // Workspace: [status word | flags | per-tile counters (split fixup) |

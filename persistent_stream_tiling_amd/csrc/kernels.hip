@@ -1,24 +1,18 @@
-// gfx950 (CDNA4) GEMM kernels: C = A.B with fp32 accumulation, one kernel
-// body for every schedule (data-parallel, persistent, Stream-K, hybrid).
+// gfx950 (CDNA4) GEMM kernels: C = A.B with fp32 accumulation.  Every kernel
+// runs every schedule (data-parallel, persistent, Stream-K, hybrid) in one
+// launch: a workgroup walks the work items the schedule gives it (schedule.h)
+// and finishes each with a store to C or a Stream-K fixup.
 //
-// A workgroup of 4 waves computes a BM x BN output tile; each wave owns a
-// (BM/2) x (BN/2) sub-tile built from 32x32 MFMA blocks.  One MAC iteration
-// consumes a BK-deep slab of A (BM x BK) and B (BK x BN), where BK is 128
-// bytes of input per row (64 fp16/bf16 or 32 fp32 values).  Slabs are staged
-// global -> registers -> LDS with two LDS buffers, so the loads of slab k+1
-// are in flight while slab k is multiplied, and one barrier per iteration
-// separates the two ("double-buffering" in the persistent matmul post on the
-// Hugging Face activity feed page).
+//   gemm_kernel_pair  fp16/bf16 default: 64-deep MAC iterations, operands
+//                     copied straight from global memory into LDS (A in whole
+//                     128-byte rows), an unrolled ring of B stages and A slots.
+//   gemm_kernel_dma   fp16/bf16 with 32-deep iterations and A in 64-byte row
+//                     halves (kept for comparison).
+//   gemm_kernel       fp32, and a register-staged fp16/bf16 variant: loads go
+//                     global -> registers -> LDS, two LDS buffers.
 //
-// Both operands sit in LDS as rows of 128 bytes with the reduction index k
-// contiguous (A: one row per output row m; B transposed on its way in: one
-// row per output column n), so every MFMA operand is one 16-byte LDS read.
-// The 16-byte chunks of a row are XOR-swizzled with (row ^ row >> 3) & 7:
-// the 32 rows one fragment read touches, and the rows eight apart that one
-// B write touches, land in distinct bank groups.
-//
-// The MFMA is issued with the operands swapped (B^T as the "A" operand), so
-// the 32x32 accumulator block holds C^T: each lane then owns four consecutive
+// All use the 32x32 MFMA with the operands swapped (B^T as the "A" operand),
+// so the accumulator block holds C^T: each lane then owns four consecutive
 // columns of one row of C and the epilogue writes 16-byte stores.
 //
 // Out-of-range rows, columns and k-chunks read as zero through the buffer
@@ -398,6 +392,17 @@ __device__ __forceinline__ void reduce_split_tiles(const KernelArgs &args, int p
     }
 }
 
+// ---------------------------------------------------------------------------
+// Register-staged kernel (fp32; fp16/bf16 for comparison).
+//
+// One MAC iteration consumes a BK-deep slab of A (BM x BK) and B (BK x BN),
+// BK being 128 bytes of input per row (32 fp32 or 64 fp16/bf16 values).  Slabs
+// go global -> registers -> LDS with two LDS buffers, so the loads of slab
+// k + 1 are in flight while slab k is multiplied, with one barrier per
+// iteration ("double-buffering" in the persistent matmul post on the Hugging
+// Face activity feed page).  Both operands sit in LDS as 128-byte rows with k
+// contiguous (B is transposed in registers on its way in), chunk-swizzled with
+// (row ^ row >> 3) & 7, so every MFMA operand is one 16-byte LDS read.
 template <int DT, int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(KernelArgs args)
 {
@@ -573,8 +578,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(KernelArgs args)
 // Swizzles (16-byte chunk index XOR a function of the row):
 //   A: chunk ^ (((row >> 1) ^ (row >> 3)) & 3)   64-byte rows
 //   B: chunk ^ kB[k & 3], kB = {0, 6, 10, 12}    BN * 2-byte rows
-// A fragment reads (32 consecutive rows, one chunk) and B transposing reads
-// (4 consecutive k-rows x 32 bytes per 16-lane group) then hit distinct banks.
+// B transposing reads (4 consecutive k-rows x 32 bytes per 16-lane group) hit
+// distinct banks; the 64-byte A rows still conflict on about a quarter of the
+// LDS cycles (measured), one reason gemm_kernel_pair is preferred.
 //
 // Per iteration and wave: wait for the next stage's copies, barrier, launch
 // the copy S - 1 iterations ahead into the stage everybody has finished with,
@@ -606,20 +612,6 @@ __device__ __forceinline__ uint32_t swz_a(int row) { return ((row >> 1) ^ (row >
 __device__ __forceinline__ uint32_t swz_b(int krow)
 {
     return (0xCA60u >> ((krow & 3) * 4)) & 0xF;  // {0, 6, 10, 12}[krow & 3]
-}
-
-// s_waitcnt vmcnt(n * LPI) for a runtime n in [0, 3]
-template <int LPI>
-__device__ __forceinline__ void wait_copies(int n)
-{
-    if (n <= 0)
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    else if (n == 1)
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPI) : "memory");
-    else if (n == 2)
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LPI) : "memory");
-    else
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * LPI) : "memory");
 }
 
 __device__ __forceinline__ void barrier_only()

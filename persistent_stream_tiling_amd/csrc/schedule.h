@@ -35,6 +35,8 @@ struct Partition {
     int32_t grid;     // launched workgroups (also the data-parallel tile stride)
     int32_t group_m;  // tile-order group height; <= 0 means row-major order
     int32_t xcds;     // dies that hardware workgroup ids are dealt to in turn
+    int32_t k_aligned; // walk a Stream-K range as whole tiles, head piece, tail
+                       // piece (see work_next); only with the split fixup
 };
 
 GSK_HD int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
@@ -105,7 +107,10 @@ struct WorkItem {
 };
 
 struct WorkCursor {
-    int64_t it, end;    // Stream-K iterations still to walk
+    int64_t it, end;    // Stream-K iterations still to walk (in order mode)
+    int64_t b, e;       // the workgroup's whole Stream-K range (k-aligned mode)
+    int32_t full;       // next whole tile of the range (k-aligned mode)
+    int32_t phase;      // k-aligned mode: 0 whole tiles, 1 head piece, 2 tail piece, 3 done
     int32_t dp_tile;    // next data-parallel tile
 };
 
@@ -118,8 +123,22 @@ GSK_HD WorkCursor work_begin(const Partition &P, int32_t p)
     } else {
         c.it = c.end = 0;
     }
+    c.b = c.it;
+    c.e = c.end;
+    c.full = (int32_t)((c.b + P.ipt - 1) / (P.ipt > 0 ? P.ipt : 1));
+    c.phase = 0;
     c.dp_tile = P.T_sk + p;
     return c;
+}
+
+GSK_HD void set_owner(const Partition &P, int32_t p, int32_t tile, int32_t ke, WorkItem &w)
+{
+    w.tile = tile;
+    w.kb = 0;
+    w.ke = ke;
+    w.role = ROLE_OWNER;
+    w.peer_last = sk_wg_of_iter(P, (int64_t)tile * P.ipt + P.ipt - 1);
+    (void)p;
 }
 
 // Next unit of work of workgroup p.  The Stream-K range is cut at tile
@@ -127,9 +146,59 @@ GSK_HD WorkCursor work_begin(const Partition &P, int32_t p)
 // [start_iter, last_iter)); then the data-parallel tiles T_sk + p,
 // T_sk + p + grid, ... follow.  Only the first Stream-K segment can start
 // inside a tile (CONTRIB) and only the last can stop inside one (OWNER).
+//
+// k-aligned mode (with the split fixup, where every piece is parked and the
+// order of a workgroup's segments does not matter): the same segments, but
+// whole tiles first, then the head piece (k = 0 up), then the tail piece.
+// All workgroups then start their head pieces at k = 0 together and their
+// tail pieces at the same offset from their start, so the workgroups running
+// side by side read the same k range of A and B at the same time, as in a
+// data-parallel wave, and share it in L2.  (In order mode the tail pieces
+// start at k offsets that differ from workgroup to workgroup.)
 GSK_HD bool work_next(const Partition &P, int32_t p, WorkCursor &c, WorkItem &w)
 {
-    if (c.it < c.end) {
+    if (P.k_aligned) {
+        const int64_t b = c.b, e = c.e;
+        if (b >= e) {
+            c.phase = 3;
+        } else if (c.phase < 3) {
+            if (c.phase == 0) {
+                if (((int64_t)c.full + 1) * P.ipt <= e) {
+                    w.tile = c.full;
+                    w.kb = 0;
+                    w.ke = P.ipt;
+                    w.role = ROLE_FULL;
+                    w.peer_last = p;
+                    ++c.full;
+                    return true;
+                }
+                c.phase = 1;
+            }
+            if (c.phase == 1) {
+                c.phase = 2;
+                const int32_t t = (int32_t)(e / P.ipt);
+                const int32_t ke = (int32_t)(e - (int64_t)t * P.ipt);
+                if (ke > 0 && (int64_t)t * P.ipt >= b) {
+                    set_owner(P, p, t, ke, w);
+                    return true;
+                }
+            }
+            if (c.phase == 2) {
+                c.phase = 3;
+                const int32_t t = (int32_t)(b / P.ipt);
+                const int32_t kb = (int32_t)(b - (int64_t)t * P.ipt);
+                if (kb > 0) {
+                    const int64_t tile_end = (int64_t)(t + 1) * P.ipt;
+                    w.tile = t;
+                    w.kb = kb;
+                    w.ke = (int32_t)((e < tile_end ? e : tile_end) - (int64_t)t * P.ipt);
+                    w.role = ROLE_CONTRIB;
+                    w.peer_last = p;
+                    return true;
+                }
+            }
+        }
+    } else if (c.it < c.end) {
         int32_t tile = (int32_t)(c.it / P.ipt);
         int32_t kb = (int32_t)(c.it - (int64_t)tile * P.ipt);
         int64_t left = c.end - c.it;
@@ -143,8 +212,7 @@ GSK_HD bool work_next(const Partition &P, int32_t p, WorkCursor &c, WorkItem &w)
         } else if (ke == P.ipt) {
             w.role = ROLE_FULL;
         } else {
-            w.role = ROLE_OWNER;
-            w.peer_last = sk_wg_of_iter(P, (int64_t)tile * P.ipt + P.ipt - 1);
+            set_owner(P, p, tile, ke, w);
         }
         c.it += ke - kb;
         return true;

@@ -7,9 +7,11 @@ these checks cover exactly what the GPU executes:
 * Stream-K ranges are contiguous, ascending and balanced to within one
   iteration (issue #1393, the first-wave kernel's per-program range),
 * the hybrid split follows the final revision's host formula,
-* each split tile has exactly one owner (the workgroup holding k = 0), which
-  waits only on later workgroups whose contribution is their first segment,
-  so the waits cannot form a cycle,
+* each split tile has exactly one owner (the workgroup holding k = 0); with
+  the head fixup it waits only on later workgroups whose contribution is
+  their first segment, so the waits cannot form a cycle; with the split
+  fixup (where nobody waits before its MAC work is done) the walk is
+  k-aligned: whole tiles, then the head piece, then the tail piece,
 * the tile order and the die remap are bijections.
 """
 import random
@@ -35,20 +37,29 @@ def check_plan(p):
     info = p.info
     T, ipt, g = info["tiles"], info["iters_per_tile"], info["g"]
     T_sk, q, r = info["tiles_sk"], info["q"], info["r"]
+    split = info["split_fixup"]
     segs = all_segments(p)
     cover = np.zeros((max(T, 1), max(ipt, 1)), dtype=np.int32)
     tile_workers = {}
     for w, ss in enumerate(segs):
+        n_sk = len([s for s in ss if s[0] < T_sk])
         for i, (tile, kb, ke, role, peer_last) in enumerate(ss):
             assert 0 <= tile < T and 0 <= kb < ke <= ipt
             cover[tile, kb:ke] += 1
             tile_workers.setdefault(tile, []).append((w, kb, ke, role, peer_last, i))
             if role == gsk.ROLE_CONTRIB:
-                assert i == 0 and kb > 0, "only a first segment may start inside a tile"
+                assert kb > 0
+                if split:  # k-aligned walk: whole tiles, head piece, then the tail piece
+                    assert i == n_sk - 1, "the tail piece is the last Stream-K segment"
+                else:
+                    assert i == 0, "only a first segment may start inside a tile"
             if role == gsk.ROLE_OWNER:
                 assert kb == 0 and ke < ipt
-                assert i == len([s for s in ss if s[0] < T_sk]) - 1, \
-                    "an owner segment is the last Stream-K segment"
+                if split:
+                    assert all(s[3] == gsk.ROLE_FULL for s in ss[:i]), \
+                        "the head piece follows the whole tiles"
+                else:
+                    assert i == n_sk - 1, "an owner segment is the last Stream-K segment"
             if role == gsk.ROLE_FULL:
                 assert kb == 0 and ke == ipt
     if T and ipt:
@@ -62,7 +73,10 @@ def check_plan(p):
             its = [t * ipt + k for (t, kb, ke, _, _) in segs[w] if t < T_sk for k in range(kb, ke)]
             begin = w * q + min(w, r)
             end = (w + 1) * q + min(w + 1, r)
-            assert its == list(range(begin, end))
+            # the walk may reorder whole segments (k-aligned mode), never iterations
+            assert sorted(its) == list(range(begin, end))
+            if not split:
+                assert its == list(range(begin, end))
             assert begin == prev_end
             prev_end = end
             assert end - begin in (q, q + 1)
@@ -80,7 +94,9 @@ def check_plan(p):
         assert contribs == list(range(ow + 1, peer_last + 1))
         for x in ws:
             if x[3] == gsk.ROLE_CONTRIB:
-                assert x[5] == 0 and x[0] > ow  # signalled before the worker ever waits
+                assert x[0] > ow
+                if not split:
+                    assert x[5] == 0  # head mode: signalled before the worker ever waits
     return segs
 
 
@@ -268,6 +284,9 @@ def test_fixup_mode_choice_and_workspace():
     # second revision's demo: 13 or 12 iterations of 32-iteration tiles -> at most 4 pieces
     p = plan(256, 512, 2048, "f16", "streamk", bm=64, bn=64, grid=82)
     assert p.info["max_pieces"] == 4 and p.info["split_fixup"] == 1
+    # two pieces per tile are split too
+    p = plan(2372, 5997, 6089, "bf16", "streamk")
+    assert p.info["max_pieces"] == 2 and p.info["split_fixup"] == 1
     # whole tiles only: nothing to fix up
     p = plan(4096, 4096, 4096, "f16", "streamk")
     assert p.info["max_pieces"] == 1 and p.info["split_fixup"] == 0
@@ -282,7 +301,10 @@ def test_split_tiles_per_workgroup_at_most_two():
                              (300, 200, 704, 64, 37), (1000, 1000, 333, 128, 100)):
         p = plan(M, N, K, "f16", "streamk", bm=bm, bn=bm, grid=g, wg_per_cu=2)
         for w in range(p.info["launch_grid"]):
-            split = [s for s in p.segments(w) if s[3] != gsk.ROLE_FULL]
-            assert len(split) <= 2
-            if len(split) == 2:
-                assert split[0][3] == gsk.ROLE_CONTRIB and split[1][3] == gsk.ROLE_OWNER
+            pieces = [s for s in p.segments(w) if s[3] != gsk.ROLE_FULL]
+            assert len(pieces) <= 2
+            if len(pieces) == 2:
+                if p.info["split_fixup"]:  # k-aligned walk: head piece, then tail piece
+                    assert pieces[0][3] == gsk.ROLE_OWNER and pieces[1][3] == gsk.ROLE_CONTRIB
+                else:
+                    assert pieces[0][3] == gsk.ROLE_CONTRIB and pieces[1][3] == gsk.ROLE_OWNER
