@@ -1240,10 +1240,10 @@ static int launch_gemm_pair(const KernelArgs &args, int grid, hipStream_t stream
 // The first entry matching a request wins, so each dtype's preferred kernel
 // for a tile comes first.
 static const Variant kVariants[] = {
-    GSK_PAIR(1, 256, 256, 4, 2), GSK_PAIR(1, 256, 256, 2, 4), GSK_PAIR(1, 256, 256, 2, 2),
+    GSK_PAIR(1, 256, 256, 2, 4), GSK_PAIR(1, 256, 256, 4, 2), GSK_PAIR(1, 256, 256, 2, 2),
     GSK_PAIR(1, 256, 128, 4, 2), GSK_PAIR(1, 256, 128, 2, 2), GSK_PAIR(1, 128, 256, 2, 4),
     GSK_PAIR(1, 128, 256, 2, 2), GSK_PAIR(1, 128, 128, 2, 2),
-    GSK_PAIR(2, 256, 256, 4, 2), GSK_PAIR(2, 256, 256, 2, 4), GSK_PAIR(2, 256, 256, 2, 2),
+    GSK_PAIR(2, 256, 256, 2, 4), GSK_PAIR(2, 256, 256, 4, 2), GSK_PAIR(2, 256, 256, 2, 2),
     GSK_PAIR(2, 256, 128, 4, 2), GSK_PAIR(2, 256, 128, 2, 2), GSK_PAIR(2, 128, 256, 2, 4),
     GSK_PAIR(2, 128, 256, 2, 2), GSK_PAIR(2, 128, 128, 2, 2),
     GSK_DMA(1, 256, 256, 4, 2, 4), GSK_DMA(1, 256, 256, 4, 2, 5), GSK_DMA(1, 256, 256, 2, 4, 4),
