@@ -115,26 +115,46 @@ def cpu_baseline(a_bits, b_bits, M, N, K, dtype, seed, target_s):
         (rows, cols, ref, scale)
 
 
+TABLE_ROUNDS = 4
+
+
 def schedule_table(args, out):
-    """Median time of every schedule (tuned tiles, default grid) per workload, the
-    schedules interleaved round by round so that clock drift hits all alike."""
-    import torch
-    import persistent_stream_tiling_amd as gsk
-    from persistent_stream_tiling_amd import inputs, tuning
-    table = workload_table()
+    """Median time of every schedule (tuned tiles, default grid) per workload.
+    Each workload runs in a child process of its own (a workload's timing was
+    seen to depend on what ran before it in the same process), its schedules
+    interleaved round by round so that clock drift hits all alike."""
+    import subprocess
+    from persistent_stream_tiling_amd import inputs
     names = sorted(inputs.irregular_workloads()) if args.workload == "irregular" \
         else args.workload.split(",")
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-    rounds, per = 4, max(1, args.steps // 4)
+    per = max(1, args.steps // TABLE_ROUNDS)
     lines = [f"# Schedules per workload: `python bench.py --workload {args.workload} "
              f"--steps {args.steps} --table <file>`", "",
-             f"Kernel source hash: {kernel_source_hash()}.  Median of {rounds * per} timed runs per "
-             "schedule (rounds interleaved, 512 MiB cache flush before each run), tuned tiles, "
-             "default grid (one workgroup per CU).", "",
+             f"Kernel source hash: {kernel_source_hash()}.  Median of {TABLE_ROUNDS * per} timed "
+             "runs per schedule (rounds interleaved, 512 MiB cache flush before each run), tuned "
+             "tiles, default grid (one workgroup per CU); one process per workload.", "",
              "| workload | M x N x K | tiles T | dp us | persistent us | Stream-K us | hybrid us "
              "| best | best TFLOP/s | Stream-K / DP | hybrid / DP |",
              "|---|---|---|---|---|---|---|---|---|---|---|"]
     for name in names:
+        r = subprocess.run([sys.executable, os.path.abspath(__file__), "--workload", name,
+                            "--steps", str(args.steps), "--table-row"],
+                           stdout=subprocess.PIPE, check=True, text=True)
+        lines.append(r.stdout.strip().splitlines()[-1])
+    text = "\n".join(lines) + "\n"
+    open(out, "w").write(text)
+    log(text)
+
+
+def schedule_table_row(args):
+    """One row of the schedule table, for one workload, on stdout."""
+    import torch
+    import persistent_stream_tiling_amd as gsk
+    from persistent_stream_tiling_amd import inputs, tuning
+    table = workload_table()
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    rounds, per = TABLE_ROUNDS, max(1, args.steps // TABLE_ROUNDS)
+    for name in [args.workload]:
         wl = table[name]
         M, N, K, dt = wl["M"], wl["N"], wl["K"], wl["dtype"]
         log(f"[table] {name}: {M}x{N}x{K} {dt}")
@@ -155,15 +175,10 @@ def schedule_table(args, out):
         med = {s: float(np.median(v[2])) * 1e3 for s, v in runs.items()}
         best = min(med, key=med.get)
         T = runs["dp"][0].info["tiles"]
-        lines.append(f"| {name} | {M} x {N} x {K} | {T} | " +
-                     " | ".join(f"{med[s]:.1f}" for s in SCHEDULES) +
-                     f" | {best} | {2.0 * M * N * K / (med[best] * 1e-6) / 1e12:.0f} | "
-                     f"{med['dp'] / med['streamk']:.2f} | {med['dp'] / med['hybrid']:.2f} |")
-        del a, b, c, runs
-        torch.cuda.empty_cache()
-    text = "\n".join(lines) + "\n"
-    open(out, "w").write(text)
-    log(text)
+        print(f"| {name} | {M} x {N} x {K} | {T} | " +
+              " | ".join(f"{med[s]:.1f}" for s in SCHEDULES) +
+              f" | {best} | {2.0 * M * N * K / (med[best] * 1e-6) / 1e12:.0f} | "
+              f"{med['dp'] / med['streamk']:.2f} | {med['dp'] / med['hybrid']:.2f} |", flush=True)
 
 
 def load_traffic(workload, schedule):
@@ -194,6 +209,7 @@ def main():
                     help="no JSON line: time the four schedules on each of the workloads named by "
                          "--workload (comma-separated, or 'irregular' for the seeded irregular "
                          "shapes) and write a markdown table to FILE")
+    ap.add_argument("--table-row", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--traffic-run", default=None, metavar="SCHEDULE",
                     help="no timing: run a 256 MiB device copy, then this schedule's GEMM, "
                          "three times each (for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)")
@@ -204,6 +220,10 @@ def main():
               "(this build has no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
 
+    if args.table:
+        schedule_table(args, args.table)  # children do the GPU work
+        return
+
     import torch
     import persistent_stream_tiling_amd as gsk
     from persistent_stream_tiling_amd import inputs, tuning
@@ -212,8 +232,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
-    if args.table:
-        schedule_table(args, args.table)
+    if args.table_row:
+        schedule_table_row(args)
         return
     wl = workload_table()[args.workload]
     M, N, K, dt = wl["M"], wl["N"], wl["K"], wl["dtype"]
