@@ -4,6 +4,8 @@ under profiles/ (kernel-time table, HBM traffic per launch).
   python -m persistent_stream_tiling_amd.profiling trace  --csv DIR --out FILE --cmd "..."
   python -m persistent_stream_tiling_amd.profiling traffic --fetch DIR --write DIR \
         --workload NAME --schedule NAME --out profiles/traffic.json --cmd "..."
+  python -m persistent_stream_tiling_amd.profiling counters --csv DIR --workload NAME \
+        --out profiles/FILE.md --cmd "..."
 
 `trace` reads a --kernel-trace --stats run of `bench.py` and reports, per
 schedule, the mean duration of the GEMM kernel over the timed steps (the
@@ -11,7 +13,11 @@ bench runs the schedules one after the other: warm-up launches, then the
 timed ones).  `traffic` reads two --pmc runs of `bench.py --traffic-run`
 (FETCH_SIZE, then WRITE_SIZE), calibrates each counter against the plain
 device copy of known size that run performs first, and stores the GEMM
-kernel's HBM bytes per launch.
+kernel's HBM bytes per launch.  `counters` reads one --pmc run of
+`bench.py --no-cpu-baseline` with COUNTERS and reports, per schedule, the
+MFMA utilisation (MFMA-busy SIMD cycles over SIMDs x active GPU cycles), the
+active clock (GPU-active cycles of one die over the dispatch's duration), LDS
+bank-conflict and LDS-active fractions, and wait cycles on LDS results.
 """
 import argparse
 import csv
@@ -101,6 +107,89 @@ def traffic(fetch_dir, write_dir):
     return res
 
 
+# One --pmc pass: 6 SQ counters and one GRBM counter (within one pass's limits).
+COUNTERS = ("GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA", "SQ_LDS_BANK_CONFLICT",
+            "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_LDS", "SQ_WAIT_INST_LDS")
+XCDS, CUS, SIMDS = 8, 256, 1024
+SHORT_US = 50.0
+
+
+def counters_summary(csv_dir, workload, schedules, warmup, steps, flops):
+    """Per schedule: mean over the timed dispatches of each derived figure.
+    GRBM_GUI_ACTIVE is summed over the dies by rocprofv3; all dies are busy
+    for the whole dispatch, so one die's count is the sum over XCDS."""
+    rows = list(csv.DictReader(open(_find(csv_dir, "counter_collection.csv"))))
+    disp = {}
+    for r in rows:
+        if not _is_gemm(r["Kernel_Name"]):
+            continue
+        d = disp.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"],
+                                                    "us": (int(r["End_Timestamp"]) -
+                                                           int(r["Start_Timestamp"])) / 1e3})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    order = [disp[k] for k in sorted(disp)]
+    per = warmup + steps
+    out = []
+    for i, s in enumerate(schedules):
+        timed = order[i * per:(i + 1) * per][warmup:]
+        if not timed:
+            break
+        def mean(f):
+            return statistics.mean(f(d) for d in timed)
+        gui = lambda d: d["GRBM_GUI_ACTIVE"] / XCDS  # noqa: E731
+        out.append({
+            "workload": workload, "schedule": s,
+            "kernel": timed[0]["name"].split("(")[0].replace("void ", ""),
+            "us": mean(lambda d: d["us"]),
+            "tflops": mean(lambda d: flops / (d["us"] * 1e-6) / 1e12),
+            "clock_ghz": mean(lambda d: gui(d) / (d["us"] * 1e3)),
+            "mfma_util": mean(lambda d: d["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui(d) * SIMDS)),
+            "lds_bank_conflict": mean(lambda d: d["SQ_LDS_BANK_CONFLICT"] / (gui(d) * CUS)),
+            "lds_active": mean(lambda d: d["SQ_LDS_IDX_ACTIVE"] / (gui(d) * CUS)),
+            "lds_conflict_per_lds_instr": mean(
+                lambda d: d["SQ_LDS_BANK_CONFLICT"] / max(d["SQ_INSTS_LDS"], 1.0)),
+            "mfma_instrs": mean(lambda d: d["SQ_INSTS_MFMA"]),
+            "lds_wait_per_lds_instr": mean(
+                lambda d: d["SQ_WAIT_INST_LDS"] / max(d["SQ_INSTS_LDS"], 1.0)),
+        })
+    return out
+
+
+def counters_table(records, cmd):
+    lines = [f"# rocprofv3 counters per workload and schedule", "",
+             f"Command per workload: `{cmd}`", "",
+             f"Kernel source hash: {source_hash()}.  Means over the timed dispatches "
+             "(counter collection serialises dispatches, so times are a little longer "
+             "than in the bench).", "",
+             "- MFMA util = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE of one die) "
+             "(rocprofv3's MfmaUtil);",
+             "- clock = GRBM_GUI_ACTIVE of one die / dispatch duration;",
+             "- peak at clock = 256 CUs x 4096 FLOP/clk x clock (fp16/bf16);",
+             "- LDS bank conflict = SQ_LDS_BANK_CONFLICT / (256 CUs x GRBM_GUI_ACTIVE) "
+             "(rocprofv3's LdsBankConflict), LDS active = SQ_LDS_IDX_ACTIVE / (256 x "
+             "GRBM_GUI_ACTIVE) (LdsUtil).", "",
+             "| workload | schedule | kernel | us | TFLOP/s | clock GHz | MFMA util | "
+             "LDS bank conflict | LDS conflict cycles / LDS instr | LDS active |",
+             "|---|---|---|---|---|---|---|---|---|---|"]
+    short = False
+    for r in records:
+        # GRBM_GUI_ACTIVE also counts the dispatch's own set-up: on a kernel of a
+        # few microseconds it swamps the kernel, so clock and MFMA util are void
+        if r["us"] < SHORT_US:
+            short = True
+            clock, util = "n/a*", "n/a*"
+        else:
+            clock, util = f"{r['clock_ghz']:.2f}", f"{100 * r['mfma_util']:.1f}%"
+        lines.append(f"| {r['workload']} | {r['schedule']} | `{r['kernel']}` | {r['us']:.1f} | "
+                     f"{r['tflops']:.0f} | {clock} | {util} | "
+                     f"{100 * r['lds_bank_conflict']:.2f}% | "
+                     f"{r['lds_conflict_per_lds_instr']:.3f} | {100 * r['lds_active']:.1f}% |")
+    if short:
+        lines += ["", f"\\* dispatches under {SHORT_US} us: the GPU-active count includes the "
+                  "dispatch's set-up, so clock and MFMA util are not meaningful there."]
+    return "\n".join(lines) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd_name", required=True)
@@ -119,8 +208,27 @@ def main():
     f.add_argument("--algorithmic-bytes", type=float, required=True)
     f.add_argument("--out", required=True)
     f.add_argument("--cmd", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("--csv", required=True, nargs="+", help="one run directory per workload")
+    c.add_argument("--workload", required=True, nargs="+")
+    c.add_argument("--schedules", default="dp,persistent,streamk,hybrid")
+    c.add_argument("--warmup", type=int, default=1)
+    c.add_argument("--steps", type=int, default=3)
+    c.add_argument("--out", required=True)
+    c.add_argument("--cmd", required=True)
     a = ap.parse_args()
-    if a.cmd_name == "trace":
+    if a.cmd_name == "counters":
+        from . import inputs
+        table = dict(inputs.WORKLOADS, **inputs.irregular_workloads())
+        recs = []
+        for d, w in zip(a.csv, a.workload):
+            wl = table[w]
+            recs += counters_summary(d, w, a.schedules.split(","), a.warmup, a.steps,
+                                     2.0 * wl["M"] * wl["N"] * wl["K"])
+        text = counters_table(recs, a.cmd)
+        open(a.out, "w").write(text)
+        print(text)
+    elif a.cmd_name == "trace":
         text, _ = trace_summary(a.csv, a.schedules.split(","), a.warmup, a.steps, a.cmd)
         open(a.out, "w").write(text)
         print(text)
