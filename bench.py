@@ -181,6 +181,88 @@ def schedule_table_row(args):
               f"{med['dp'] / med['streamk']:.2f} | {med['dp'] / med['hybrid']:.2f} |", flush=True)
 
 
+SWEEP_VARIANTS = (("streamk", 0), ("hybrid", 0), ("hybrid", "one_tile"))
+
+
+def sweep_grids(name, T):
+    """Stream-K grid sizes tried per workload: one workgroup per CU (the
+    default), one per tile, 128, 64, and a seeded random even size."""
+    import random
+    rnd = random.Random(sum(map(ord, name)) + 20261202).randrange(2, 257, 2)
+    out = []
+    for g in (256, T, 128, 64, rnd):
+        if g not in out:
+            out.append(g)
+    return out
+
+
+def grid_sweep(args, out):
+    """Stream-K and hybrid (two-tile and one-tile) over several grid sizes g,
+    against data-parallel, per workload; one child process per workload."""
+    import subprocess
+    from persistent_stream_tiling_amd import inputs
+    names = sorted(inputs.irregular_workloads()) if args.workload == "irregular" \
+        else args.workload.split(",")
+    lines = [f"# Stream-K grid sweep: `python bench.py --workload {args.workload} "
+             f"--steps {args.steps} --grid-sweep <file>`", "",
+             f"Kernel source hash: {kernel_source_hash()}.  Median of {args.steps} timed runs per "
+             "line (512 MiB cache flush before each), tuned tiles per schedule.  g = 256 is one "
+             "workgroup per CU; g = T is one per tile; with g = s*T and s dividing the "
+             "iterations per tile, Stream-K is a fixed split-K with s pieces per tile.  Grids "
+             "above 256 are refused (the fixup needs every workgroup resident).  `one_tile` is "
+             "the hybrid without two_tiles (Stream-K over T mod g tiles only).", "",
+             "| workload | tiles T | schedule | g | us | TFLOP/s | DP us | DP / this |",
+             "|---|---|---|---|---|---|---|---|"]
+    for name in names:
+        r = subprocess.run([sys.executable, os.path.abspath(__file__), "--workload", name,
+                            "--steps", str(args.steps), "--grid-sweep-rows"],
+                           stdout=subprocess.PIPE, check=True, text=True)
+        lines += [ln for ln in r.stdout.splitlines() if ln.startswith("| ")]
+    text = "\n".join(lines) + "\n"
+    open(out, "w").write(text)
+    log(text)
+
+
+def grid_sweep_rows(args):
+    import torch
+    import persistent_stream_tiling_amd as gsk
+    from persistent_stream_tiling_amd import FLAG_ONE_TILE, inputs, tuning
+    wl = workload_table()[args.workload]
+    M, N, K, dt = wl["M"], wl["N"], wl["K"], wl["dtype"]
+    log(f"[sweep] {args.workload}: {M}x{N}x{K} {dt}")
+    a_bits, b_bits = inputs.operands(M, N, K, dt, wl["dist"], wl["seed"], wl["scale"])
+    a, b = to_device(a_bits, dt), to_device(b_bits, dt)
+    c = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    flops = 2.0 * M * N * K
+
+    def med(plan, ws):
+        ms, _ = time_schedule(plan, a, b, c, ws, args.steps, 2, flush)
+        if ws is not None and plan.workspace_status(ws) != 0:
+            raise RuntimeError("a Stream-K fixup wait gave up")
+        return float(np.median(ms)) * 1e3
+
+    dp = gsk.GemmPlan(M, N, K, dt, "dp", **tuning.bench_tiles(args.workload, "dp", dt))
+    dp_us = med(dp, dp.new_workspace())
+    for sched, variant in SWEEP_VARIANTS:
+        tiles = tuning.bench_tiles(args.workload, sched, dt)
+        if variant == "one_tile":
+            tiles["flags"] = tiles.get("flags", 0) | FLAG_ONE_TILE
+        T = gsk.GemmPlan(M, N, K, dt, sched, **tiles).info["tiles"]
+        label = sched + (" one_tile" if variant else "")
+        for g in sweep_grids(args.workload, T):
+            try:
+                plan = gsk.GemmPlan(M, N, K, dt, sched, grid=g, **tiles)
+            except ValueError as e:
+                print(f"| {args.workload} | {T} | {label} | {g} | refused: {str(e)[:60]} "
+                      "| | | |", flush=True)
+                continue
+            us = med(plan, plan.new_workspace())
+            print(f"| {args.workload} | {T} | {label} | {g} | {us:.1f} | "
+                  f"{flops / (us * 1e-6) / 1e12:.0f} | {dp_us:.1f} | {dp_us / us:.2f} |",
+                  flush=True)
+
+
 def load_traffic(workload, schedule):
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
@@ -210,6 +292,11 @@ def main():
                          "--workload (comma-separated, or 'irregular' for the seeded irregular "
                          "shapes) and write a markdown table to FILE")
     ap.add_argument("--table-row", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--grid-sweep", default=None, metavar="FILE",
+                    help="time Stream-K and hybrid over several grid sizes against DP for "
+                         "each workload in --workload (comma list, or 'irregular'); write "
+                         "a markdown table to FILE")
+    ap.add_argument("--grid-sweep-rows", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--traffic-run", default=None, metavar="SCHEDULE",
                     help="no timing: run a 256 MiB device copy, then this schedule's GEMM, "
                          "three times each (for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)")
@@ -223,6 +310,9 @@ def main():
     if args.table:
         schedule_table(args, args.table)  # children do the GPU work
         return
+    if args.grid_sweep:
+        grid_sweep(args, args.grid_sweep)
+        return
 
     import torch
     import persistent_stream_tiling_amd as gsk
@@ -234,6 +324,9 @@ def main():
     torch.cuda.set_device(0)
     if args.table_row:
         schedule_table_row(args)
+        return
+    if args.grid_sweep_rows:
+        grid_sweep_rows(args)
         return
     wl = workload_table()[args.workload]
     M, N, K, dt = wl["M"], wl["N"], wl["K"], wl["dtype"]

@@ -23,14 +23,21 @@ BENCH_TILES = {
     # workgroup order across the dies
     "fp16_4096": {s: dict(bm=256, bn=256, group_m=4, flags=FLAG_NO_XCD_REMAP) for s in SCHEDULES},
     # Tile-per-workgroup schedules: 144 tiles of 128x128 on 256 CUs.  Stream-K
-    # and hybrid: 36 tiles of 256x256, each split over ~7 workgroups.
+    # and hybrid: 72 tiles of 256x128, each split over 3-4 workgroups, in the
+    # hardware workgroup order (the pieces of one k range spread over the dies)
     "fp16_1536x1536x8192": dict(dp=dict(bm=128, bn=128), persistent=dict(bm=128, bn=128),
-                                streamk=dict(bm=256, bn=256), hybrid=dict(bm=256, bn=256)),
+                                streamk=dict(bm=256, bn=128, wave_m=4, wave_n=2,
+                                             flags=FLAG_NO_XCD_REMAP),
+                                hybrid=dict(bm=256, bn=128, wave_m=4, wave_n=2,
+                                            flags=FLAG_NO_XCD_REMAP)),
     # 64 tiles of 64x64 for the tile-per-workgroup schedules; Stream-K and
-    # hybrid: 8 tiles of 256x128, each split over 32 workgroups.
+    # hybrid: 8 tiles of 256x128, each split over 32 workgroups; hardware
+    # workgroup order, so each die holds one k range of all 8 tiles
     "bf16_512x512x65536": dict(dp=dict(bm=64, bn=64), persistent=dict(bm=64, bn=64),
-                               streamk=dict(bm=256, bn=128, wave_m=4, wave_n=2),
-                               hybrid=dict(bm=256, bn=128, wave_m=4, wave_n=2)),
+                               streamk=dict(bm=256, bn=128, wave_m=4, wave_n=2,
+                                            flags=FLAG_NO_XCD_REMAP),
+                               hybrid=dict(bm=256, bn=128, wave_m=4, wave_n=2,
+                                           flags=FLAG_NO_XCD_REMAP)),
     # 3584 tiles of 256x256 (14 per CU)
     "bf16_8192x28672x8192": dict(dp=dict(bm=256, bn=256), persistent=dict(bm=256, bn=256, group_m=4),
                                  streamk=dict(bm=256, bn=256), hybrid=dict(bm=256, bn=256)),
