@@ -53,10 +53,13 @@ def to_device(bits, dtype):
 
 
 def algorithmic_bytes(M, N, K, dtype, plan_info):
-    """A and B read once, C written once, Stream-K partials written and read once."""
+    """A and B read once, C written once (fp32, or the input dtype when the
+    plan stores C in it); the callers add the Stream-K partials written and
+    read once."""
+    from persistent_stream_tiling_amd import FLAG_C_INPUT_DTYPE
     e = 4 if dtype == "f32" else 2
-    base = (M * K + K * N) * e + M * N * 4
-    return base
+    ce = e if plan_info["flags"] & FLAG_C_INPUT_DTYPE else 4
+    return (M * K + K * N) * e + M * N * ce
 
 
 def partial_bytes(plan):
@@ -285,6 +288,9 @@ def main():
     ap.add_argument("--workload", default="fp16_4096")
     ap.add_argument("--schedules", default=",".join(SCHEDULES))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--c-dtype", choices=("f32", "input"), default="f32",
+                    help="C as fp32 (the workloads' output type, the default) or in the input "
+                         "dtype (the pages' fp16 output; fp16/bf16 workloads only)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--report", default=None, help="also append per-schedule records here")
     ap.add_argument("--table", default=None, metavar="FILE",
@@ -333,16 +339,23 @@ def main():
     log(f"[bench] {args.workload}: {M}x{N}x{K} {dt} {wl['dist']} seed {wl['seed']}")
     a_bits, b_bits = inputs.operands(M, N, K, dt, wl["dist"], wl["seed"], wl["scale"])
     a, b = to_device(a_bits, dt), to_device(b_bits, dt)
-    c = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    c_half = args.c_dtype == "input" and dt != "f32"
+    c = torch.empty((M, N), dtype=a.dtype if c_half else torch.float32, device="cuda")
     flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
     flops = 2.0 * M * N * K
     bound = "hbm" if args.workload == "bf16_512x512x65536" else "mfma"
+
+    def tiles_for(sched):
+        t = tuning.bench_tiles(args.workload, sched, dt)
+        if c_half:
+            t["flags"] = t.get("flags", 0) | gsk.FLAG_C_INPUT_DTYPE
+        return t
 
     if args.traffic_run:
         from persistent_stream_tiling_amd.profiling import COPY_BYTES
         src = torch.ones(COPY_BYTES, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
-        tiles = tuning.bench_tiles(args.workload, args.traffic_run, dt)
+        tiles = tiles_for(args.traffic_run)
         plan = gsk.GemmPlan(M, N, K, dt, args.traffic_run, **tiles)
         ws = plan.new_workspace()
         for _ in range(3):
@@ -359,7 +372,7 @@ def main():
 
     results = {}
     for sched in args.schedules.split(","):
-        tiles = tuning.bench_tiles(args.workload, sched, dt)
+        tiles = tiles_for(sched)
         plan = gsk.GemmPlan(M, N, K, dt, sched, **tiles)
         ws = plan.new_workspace()
         log(f"[bench] {sched}: {plan.describe()}")
@@ -391,7 +404,7 @@ def main():
                                                      args.cpu_seconds)
         plan.run(a, b, c, ws)
         torch.cuda.synchronize()
-        got = c[torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()].cpu().numpy()
+        got = c[torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()].float().cpu().numpy()
         rel = np.abs(got.astype(np.float64) - ref) / np.maximum(scale, 1e-300)
         check = {"samples": int(rows.size), "max_err_over_S": float(rel.max()),
                  "tolerance": 1e-5 if dt == "f32" else 4e-3}
@@ -419,7 +432,8 @@ def main():
         "dtype": dt,
         "data": "synthetic",
         "config": {"workload": args.workload, "M": M, "N": N, "K": K,
-                   "distribution": wl["dist"], "schedule": best, "tiles": rec["tiles"],
+                   "distribution": wl["dist"], "c_dtype": dt if c_half else "f32",
+                   "schedule": best, "tiles": rec["tiles"],
                    "grid": rec["grid"]},
         "schedules": {s: r[0] for s, r in results.items()},
         "roofline": roof,

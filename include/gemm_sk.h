@@ -9,7 +9,8 @@
  * time as a sum-reduction across K).  A and B are fp32, fp16 or bf16; the
  * products are accumulated in fp32 (Triton issue #1393 "Stream-k matmul
  * implementation very slow...", final revision, where the accumulator type is
- * fp32 for fp16/bf16/fp32 inputs) and C is written as fp32.
+ * fp32 for fp16/bf16/fp32 inputs) and C is written as fp32 (or, with
+ * GEMM_FLAG_C_INPUT_DTYPE, in the input dtype, as on that page).
  *
  * The schedules (same two pages):
  *   GEMM_DP          one workgroup per output tile; the hardware hands CUs new
@@ -37,8 +38,9 @@
  * run.  Different schedules may differ in the last bits.
  *
  * Layout.  A is M x K row-major (leading dimension K), B is K x N row-major
- * (leading dimension N), C is M x N fp32 row-major (leading dimension N).  A, B
- * and C are device pointers; A and B must be 16-byte aligned.  C is fully
+ * (leading dimension N), C is M x N row-major (leading dimension N), fp32 or,
+ * with GEMM_FLAG_C_INPUT_DTYPE, fp16/bf16.  A, B and C are device pointers; A
+ * and B must be 16-byte aligned, C aligned to its element size.  C is fully
  * overwritten (no zero fill needed).  Rows whose byte length is not a multiple
  * of 16 are repacked into the workspace before the multiply.
  *
@@ -91,7 +93,16 @@ enum {
      * copies A in 64-byte row halves (kernel_kind 1), instead of the default
      * one with 64-deep iterations and whole 128-byte A rows (kernel_kind 2).
      * Kept for comparison: half-line A copies fetch every A line twice. */
-    GEMM_FLAG_A_HALF_ROWS = 1u << 5
+    GEMM_FLAG_A_HALF_ROWS = 1u << 5,
+    /* C is written in the input dtype instead of fp32: each fp32 sum is
+     * rounded to the nearest fp16 / bf16 value (ties to even) as it is
+     * stored.  This is the pages' output type: issue #1393's final revision
+     * allocates C in A's dtype and casts the fp32 accumulator to it when it
+     * stores a tile.  Stream-K partial tiles stay fp32 in the workspace and
+     * only the finished sum is rounded, so the half-precision C of a plan is
+     * exactly the rounding of the fp32 C of the same plan without this flag.
+     * A no-op for fp32 inputs. */
+    GEMM_FLAG_C_INPUT_DTYPE = 1u << 6
 };
 
 /* Tile and schedule knobs.  Every field 0 means "default". */
@@ -150,10 +161,12 @@ gemm_plan *gemm_plan_create_for_device(int64_t M, int64_t N, int64_t K, gemm_dty
  * when allocated; it may be NULL when that size is 0.  A run leaves the
  * workspace's flags zero again, so it can be reused by later runs without
  * clearing.  Two runs that overlap in time must not share a workspace.
+ * C points to M x N fp32 values, or to fp16/bf16 values when the plan was
+ * made with GEMM_FLAG_C_INPUT_DTYPE.
  * Returns 0, or -1 invalid argument (NULL or misaligned pointer), -2 workspace
  * missing, -3 HIP launch error, -5 plan made for another device.
  */
-int gemm_run(const gemm_plan *plan, const void *A, const void *B, float *C, void *workspace,
+int gemm_run(const gemm_plan *plan, const void *A, const void *B, void *C, void *workspace,
              void *stream);
 
 /* Free a plan (NULL is ignored). */

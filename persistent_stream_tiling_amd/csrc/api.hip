@@ -393,11 +393,12 @@ int gemm_plan_describe(const gemm_plan *p, char *buf, size_t len)
         return -1;
     }
     return snprintf(buf, buf ? len : 0,
-                    "M,N,K=%lld,%lld,%lld %s %s tile=%dx%dx%d waves=%dx%d %s%d group_m=%d | tiles %dx%d=%d "
+                    "M,N,K=%lld,%lld,%lld %s C=%s %s tile=%dx%dx%d waves=%dx%d %s%d group_m=%d | tiles %dx%d=%d "
                     "ipt=%d | T_sk=%d T_dp=%d I_sk=%lld g=%d q=%d r=%d | grid=%d x %d threads, "
                     "lds=%zu B, capacity=%d wg, xcds=%d | fixup=%s pieces<=%d | pack A=%d B=%d | "
                     "workspace=%zu B",
                     (long long)p->M, (long long)p->N, (long long)p->K, dtype_name(p->dtype),
+                    dtype_name((p->flags & GEMM_FLAG_C_INPUT_DTYPE) ? p->dtype : GEMM_F32),
                     sched_name(p->schedule), p->bm, p->bn, p->bk, p->variant->wave_m,
                     p->variant->wave_n, p->variant->kind == 2 ? "ring/rows" : p->variant->kind ? "ring" : "staged",
                     p->variant->kind ? p->variant->stages : 2, p->group_m, p->P.tiles_m,
@@ -446,7 +447,7 @@ int32_t gemm_plan_logical_wg(const gemm_plan *p, int32_t hw)
     return logical_wg(hw, p->P.grid, p->P.xcds);
 }
 
-int gemm_run(const gemm_plan *p, const void *A, const void *B, float *C, void *workspace,
+int gemm_run(const gemm_plan *p, const void *A, const void *B, void *C, void *workspace,
              void *stream_v)
 {
     if (!p) {
@@ -469,8 +470,15 @@ int gemm_run(const gemm_plan *p, const void *A, const void *B, float *C, void *w
         set_error("plan was made for device %d, current device is %d", p->device, cur);
         return -5;
     }
+    // C holds fp32, or the input dtype with GEMM_FLAG_C_INPUT_DTYPE
+    const int c_dtype = (p->flags & GEMM_FLAG_C_INPUT_DTYPE) ? p->dtype : GEMM_F32;
+    const int CE = elem_size(c_dtype);
+    if ((uintptr_t)C & (CE - 1)) {
+        set_error("C must be %d-byte aligned", CE);
+        return -1;
+    }
     if (p->K == 0) {
-        if (launch_zero(C, p->M * p->N, stream)) {
+        if (launch_zero(C, p->M * p->N, CE, stream)) {
             set_error("zero-fill launch failed: %s", hipGetErrorString(hipGetLastError()));
             return -3;
         }
@@ -484,9 +492,8 @@ int gemm_run(const gemm_plan *p, const void *A, const void *B, float *C, void *w
         set_error("this plan needs %zu bytes of workspace", p->ws_size);
         return -2;
     }
-    if (((uintptr_t)A & 15) || ((uintptr_t)B & 15) || ((uintptr_t)C & 3) ||
-        ((uintptr_t)workspace & 255)) {
-        set_error("A and B must be 16-byte aligned, C 4-byte aligned, workspace 256-byte aligned");
+    if (((uintptr_t)A & 15) || ((uintptr_t)B & 15) || ((uintptr_t)workspace & 255)) {
+        set_error("A and B must be 16-byte aligned, workspace 256-byte aligned");
         return -1;
     }
     const int E = elem_size(p->dtype);
@@ -510,7 +517,8 @@ int gemm_run(const gemm_plan *p, const void *A, const void *B, float *C, void *w
     KernelArgs args;
     args.A = a;
     args.B = b;
-    args.C = C;
+    args.C = (uint8_t *)C;
+    args.c_dtype = c_dtype;
     args.status = p->P.T_sk > 0 ? (int32_t *)ws : nullptr;
     args.flags = p->P.T_sk > 0 ? (int32_t *)(ws + p->off_flags) : nullptr;
     args.partials = p->P.T_sk > 0 ? (float *)(ws + p->off_partials) : nullptr;
@@ -522,7 +530,9 @@ int gemm_run(const gemm_plan *p, const void *A, const void *B, float *C, void *w
     args.lda = (int32_t)p->lda;
     args.ldb = (int32_t)p->ldb;
     args.ldc = (int32_t)p->N;
-    args.c_vec = (p->N % 4 == 0) && (((uintptr_t)C & 15) == 0);
+    // a lane stores 4 consecutive elements of a row: one 16-byte (fp32) or
+    // 8-byte (fp16/bf16) store when rows and C keep that alignment
+    args.c_vec = (p->N % 4 == 0) && (((uintptr_t)C & (4 * CE - 1)) == 0);
     args.spin_limit = p->spin_limit;
     args.P = p->P;
     if (p->variant->launch(args, p->P.grid, stream)) {

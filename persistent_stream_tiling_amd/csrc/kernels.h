@@ -14,7 +14,8 @@ namespace gsk {
 struct KernelArgs {
     const uint8_t *A;      // M x lda elements, row-major, 16-byte aligned rows
     const uint8_t *B;      // K x ldb elements, row-major, 16-byte aligned rows
-    float *C;              // M x ldc floats
+    uint8_t *C;            // M x ldc elements of c_dtype
+    int32_t c_dtype;       // 0: fp32 C; 1: fp16 C; 2: bf16 C (rounded to nearest even)
     float *partials;       // Stream-K partial tiles: bm*bn floats per slot
     int32_t *flags;        // one "partial ready" flag per slot (0 between runs)
     int32_t *counters;     // split fixup: readers done per split tile (0 between runs)
@@ -24,7 +25,7 @@ struct KernelArgs {
                            //    each reduce a share of its blocks
     int32_t M, N, K;
     int32_t lda, ldb, ldc; // leading dimensions in elements
-    int32_t c_vec;         // 1: C rows allow 16-byte stores
+    int32_t c_vec;         // 1: C rows allow whole 4-element vector stores
     int32_t spin_limit;    // polls before a fixup wait gives up
     Partition P;
 };
@@ -51,7 +52,7 @@ const Variant *variants(int *count);
 int launch_pack(const void *src, void *dst, int64_t rows, int64_t cols, int64_t ld_src,
                 int64_t ld_dst, int elem_size, hipStream_t stream);
 
-// C[0 .. count) = 0 (the K = 0 product).
-int launch_zero(float *C, int64_t count, hipStream_t stream);
+// C[0 .. count) = 0 for elements of elem_size bytes (the K = 0 product).
+int launch_zero(void *C, int64_t count, int elem_size, hipStream_t stream);
 
 }  // namespace gsk

@@ -151,16 +151,46 @@ __device__ __forceinline__ void lds_store_words(uint8_t *p, const uint32_t *w)
     }
 }
 
+// fp32 -> fp16 / bf16 bits, rounded to nearest even (by value: see bits_of).
+__device__ __forceinline__ uint32_t f16_bits(float x)
+{
+    return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+__device__ __forceinline__ uint32_t bf16_bits(float x)
+{
+    return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
 // Store one 32x32 accumulator block (rows row0 + 32*mt.., columns col0 +
 // 32*nt.. of the tile) to C through a buffer descriptor based at the tile's
 // first row; an element outside C gets an out-of-range offset so its write is
-// dropped: no branches around the stores.
+// dropped: no branches around the stores.  C is fp32, or fp16 / bf16 rounded
+// to nearest even from the fp32 sums (args.c_dtype, uniform per launch).
 __device__ __forceinline__ void store_quad(const f32x4 &v, const KernelArgs &args,
                                            __amdgpu_buffer_rsrc_t c_rsrc, int m0, int n0, int row,
                                            int col, int half, int g)
 {
     const bool row_ok = m0 + row < args.M;
     const int n = n0 + col + 8 * g + 4 * half;
+    if (args.c_dtype != 0) {
+        const uint32_t off = (uint32_t)((row * args.ldc + n) * 2);
+        uint32_t h[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            h[e] = args.c_dtype == 1 ? f16_bits(v[e]) : bf16_bits(v[e]);
+        if (args.c_vec) {
+            const u32x2 u = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+            __builtin_amdgcn_raw_buffer_store_b64(
+                u, c_rsrc, (int)(row_ok && n < args.N ? off : kOutOfRange), 0, 0);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                __builtin_amdgcn_raw_buffer_store_b16(
+                    (uint16_t)h[e], c_rsrc,
+                    (int)(row_ok && n + e < args.N ? off + 2 * e : kOutOfRange), 0, 0);
+        }
+        return;
+    }
     const uint32_t off = (uint32_t)((row * args.ldc + n) * 4);
     const u32x4 u = u32x4{bits_of(v[0]), bits_of(v[1]), bits_of(v[2]), bits_of(v[3])};
     if (args.c_vec) {
@@ -174,6 +204,12 @@ __device__ __forceinline__ void store_quad(const f32x4 &v, const KernelArgs &arg
             __builtin_amdgcn_raw_buffer_store_b32(
                 u[e], c_rsrc, (int)(row_ok && n + e < args.N ? off + 4 * e : kOutOfRange), 0, 0);
     }
+}
+
+// Descriptor for the C rows of a tile starting at row m0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t c_rows(const KernelArgs &args, int m0)
+{
+    return make_rsrc(args.C + (int64_t)m0 * args.ldc * (args.c_dtype != 0 ? 2 : 4));
 }
 
 __device__ __forceinline__ void store_block(const f32x16 &blk, const KernelArgs &args,
@@ -268,7 +304,7 @@ __device__ __forceinline__ void finish_tile(f32x16 (&acc)[MT][NT], const KernelA
                                __HIP_MEMORY_SCOPE_AGENT);
         return;
     }
-    const __amdgpu_buffer_rsrc_t c_rsrc = make_rsrc(args.C + (int64_t)m0 * args.ldc);
+    const __amdgpu_buffer_rsrc_t c_rsrc = c_rows(args, m0);
     if (w.role == ROLE_OWNER) {
         // Head of a split tile: wait for every later workgroup on the tile,
         // then add their partials in ascending workgroup (= ascending k) order.
@@ -342,7 +378,7 @@ __device__ __forceinline__ void reduce_split_tiles(const KernelArgs &args, int p
         int tm, tn;
         tile_coords(P, t, &tm, &tn);
         const int m0 = tm * BM, n0 = tn * BN;
-        const __amdgpu_buffer_rsrc_t c_rsrc = make_rsrc(args.C + (int64_t)m0 * args.ldc);
+        const __amdgpu_buffer_rsrc_t c_rsrc = c_rows(args, m0);
         const __amdgpu_buffer_rsrc_t slots = make_rsrc(args.partials);
         const uint32_t slot_bytes = (uint32_t)(BM * BN * 4);
         // Work units: quarter blocks (4 floats per lane, 1 KiB per piece),
@@ -1301,21 +1337,27 @@ int launch_pack(const void *src, void *dst, int64_t rows, int64_t cols, int64_t 
     return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
-__global__ void zero_kernel(float *__restrict__ C, int64_t count)
+template <typename T>
+__global__ void zero_kernel(T *__restrict__ C, int64_t count)
 {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count;
          i += (int64_t)gridDim.x * blockDim.x)
-        C[i] = 0.0f;
+        C[i] = T(0);
 }
 
-int launch_zero(float *C, int64_t count, hipStream_t stream)
+int launch_zero(void *C, int64_t count, int elem_size, hipStream_t stream)
 {
     if (count <= 0)
         return 0;
     int64_t blocks = (count + 255) / 256;
     if (blocks > 8192)
         blocks = 8192;
-    hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, C, count);
+    if (elem_size == 2)
+        hipLaunchKernelGGL(zero_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                           (uint16_t *)C, count);
+    else
+        hipLaunchKernelGGL(zero_kernel<uint32_t>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                           (uint32_t *)C, count);
     return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 

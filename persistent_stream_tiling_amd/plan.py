@@ -1,7 +1,8 @@
 """Plan objects and the ``matmul`` convenience call (argument marshalling only)."""
 import ctypes
 
-from ._lib import DTYPES, SCHEDULES, DeviceDesc, PlanInfo, Segment, Tiles, last_error, load
+from ._lib import (DTYPES, FLAG_C_INPUT_DTYPE, SCHEDULES, DeviceDesc, PlanInfo, Segment, Tiles,
+                   last_error, load)
 
 _TORCH_DTYPES = None
 
@@ -144,9 +145,11 @@ def plan_for_device(M, N, K, dtype, schedule, cus=256, xcds=8, wg_per_cu=1, **ti
 _PLANS = {}
 
 
-def matmul(a, b, schedule="hybrid", **tiles):
-    """C = a @ b (fp32) for contiguous CUDA tensors a (M x K) and b (K x N) of
-    float32, float16 or bfloat16, through the library's kernels."""
+def matmul(a, b, schedule="hybrid", out_dtype=None, **tiles):
+    """C = a @ b for contiguous CUDA tensors a (M x K) and b (K x N) of
+    float32, float16 or bfloat16, through the library's kernels.  C is fp32,
+    or a's dtype when ``out_dtype`` is a's dtype (fp32 sums rounded to nearest
+    even as they are stored)."""
     import torch
     if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[0]:
         raise ValueError(f"incompatible shapes {tuple(a.shape)} and {tuple(b.shape)}")
@@ -154,6 +157,10 @@ def matmul(a, b, schedule="hybrid", **tiles):
         raise ValueError(f"unsupported dtypes {a.dtype}, {b.dtype}")
     if not (a.is_cuda and b.is_cuda):
         raise ValueError("a and b must be on the GPU")
+    if out_dtype not in (None, torch.float32, a.dtype):
+        raise ValueError(f"out_dtype must be float32 or {a.dtype}, got {out_dtype}")
+    if out_dtype == a.dtype and a.dtype != torch.float32:
+        tiles["flags"] = tiles.get("flags", 0) | FLAG_C_INPUT_DTYPE
     a, b = a.contiguous(), b.contiguous()
     M, K = a.shape
     N = b.shape[1]
@@ -164,6 +171,7 @@ def matmul(a, b, schedule="hybrid", **tiles):
         entry = (plan, plan.new_workspace(a.device))
         _PLANS[key] = entry
     plan, ws = entry
-    c = torch.empty((M, N), dtype=torch.float32, device=a.device)
+    c_half = tiles.get("flags", 0) & FLAG_C_INPUT_DTYPE
+    c = torch.empty((M, N), dtype=a.dtype if c_half else torch.float32, device=a.device)
     plan.run(a, b, c, ws)
     return c

@@ -72,3 +72,21 @@ def test_destroy_null_and_describe_null_are_safe():
     lib.gemm_plan_destroy(None)
     assert lib.gemm_plan_describe(None, None, 0) == -1
     assert lib.gemm_plan_workspace_size(None) == 0
+
+
+def test_header_flag_values_match_the_binding():
+    # every GEMM_FLAG_* in the header has the same bit in the Python binding
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    flags = dict(re.findall(r"GEMM_FLAG_(\w+)\s*=\s*1u\s*<<\s*(\d+)", text))
+    assert flags
+    for name, bit in flags.items():
+        assert getattr(_lib, "FLAG_" + name) == 1 << int(bit), name
+
+
+def test_plan_describes_its_output_dtype():
+    plan = gsk.plan_for_device(300, 200, 704, "f16", "hybrid", bm=128, bn=128)
+    assert " C=f32 " in plan.describe()
+    plan = gsk.plan_for_device(300, 200, 704, "bf16", "hybrid", bm=128, bn=128,
+                               flags=gsk.FLAG_C_INPUT_DTYPE)
+    assert " C=bf16 " in plan.describe()
+    assert plan.info["flags"] & gsk.FLAG_C_INPUT_DTYPE
