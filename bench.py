@@ -266,6 +266,115 @@ def grid_sweep_rows(args):
                   flush=True)
 
 
+def log_sampled_shapes(n, seed=20261203, lo=256, hi=8192, step=256):
+    """n (M, N, K), each log-uniform in [lo, hi] and rounded to a multiple of
+    step, as the pages' shape benchmark draws them."""
+    import math
+    import random
+    rnd = random.Random(seed)
+
+    def one():
+        v = math.exp(rnd.uniform(math.log(lo), math.log(hi)))
+        return int(min(hi, max(lo, round(v / step) * step)))
+    return [(one(), one(), one()) for _ in range(n)]
+
+
+def log_sampled(args, out):
+    """The pages' shape benchmark: fp16 GEMMs of log-sampled shapes, fp16 C.
+    Per shape: data-parallel, Stream-K and hybrid (library default tiles,
+    g = 256) and, as context only, torch.matmul (hipBLASLt) with the same
+    fp16 output; median of --steps runs each, cache flush before every run."""
+    import torch
+    import persistent_stream_tiling_amd as gsk
+    shapes = log_sampled_shapes(args.log_sampled)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7)
+    rows = []
+
+    def med(fn):
+        ts = []
+        for _ in range(args.steps + 1):
+            flush.zero_()
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            fn()
+            e.record()
+            e.synchronize()
+            ts.append(s.elapsed_time(e) * 1e3)
+        return float(np.median(ts[1:]))
+
+    for i, (M, N, K) in enumerate(shapes):
+        a = torch.randn((M, K), device="cuda", generator=gen).half()
+        b = torch.randn((K, N), device="cuda", generator=gen).half()
+        c = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        us, err = {}, 0.0
+        ref = a[:64].float() @ b.float()
+        sref = a[:64].float().abs() @ b.float().abs()
+        for sched in ("dp", "streamk", "hybrid"):
+            plan = gsk.GemmPlan(M, N, K, "f16", sched, flags=gsk.FLAG_C_INPUT_DTYPE)
+            ws = plan.new_workspace()
+            plan.run(a, b, c, ws)
+            torch.cuda.synchronize()
+            # sanity check on the first rows against an fp32 product (not a parity test:
+            # parity is checked against the oracle by the test suite)
+            err = max(err, float(((c[:64].float() - ref).abs() / sref.clamp_min(1e-30)).max()))
+            us[sched] = med(lambda: plan.run(a, b, c, ws))
+            if ws is not None and plan.workspace_status(ws) != 0:
+                raise RuntimeError(f"{(M, N, K)} {sched}: a fixup wait gave up")
+        T = -(-M // 256) * -(-N // 256)  # 256x256 tiles, for the summary by size
+        us["torch"] = med(lambda: torch.matmul(a, b, out=c))
+        if err > 4e-3 + 2.0 ** -11:
+            raise RuntimeError(f"{(M, N, K)}: max |C - A.B| / S = {err:.2e}")
+        rows.append((M, N, K, T, us))
+        if i % 50 == 0:
+            log(f"[log-sampled] {i}/{len(shapes)} {M}x{N}x{K}: " +
+                " ".join(f"{k} {v:.1f}" for k, v in us.items()))
+        del a, b, c
+
+    def gmean(x):
+        return float(np.exp(np.mean(np.log(x))))
+    best_sk = np.array([min(r[4]["streamk"], r[4]["hybrid"]) for r in rows])
+    dp = np.array([r[4]["dp"] for r in rows])
+    hy = np.array([r[4]["hybrid"] for r in rows])
+    best = np.minimum(best_sk, dp)
+    th = np.array([r[4]["torch"] for r in rows])
+    lines = [f"# Log-sampled fp16 shapes: `python bench.py --log-sampled {args.log_sampled} "
+             f"--steps {args.steps} --log-sampled-out <file>`", "",
+             f"Kernel source hash: {kernel_source_hash()}.  {len(rows)} shapes (M, N, K) drawn "
+             "log-uniformly in [256, 8192] and rounded to multiples of 256 (seeded); fp16 inputs "
+             "N(0,1), fp16 C (fp32 accumulate); library default tiles, g = 256; median of "
+             f"{args.steps} runs per line, 512 MiB cache flush before each; T below counts "
+             "256x256 tiles whatever tile the plan chose.  torch.matmul "
+             "(hipBLASLt, same fp16 output) is context, not a target.", "",
+             "| statistic | value |", "|---|---|",
+             f"| mean DP time / hybrid time (the pages' statistic, over shapes) | "
+             f"{float(np.mean(dp / hy)):.3f} |",
+             f"| geomean DP / hybrid | {gmean(dp / hy):.3f} |",
+             f"| geomean DP / best of Stream-K, hybrid | {gmean(dp / best_sk):.3f} |",
+             f"| shapes where Stream-K or hybrid beats DP | {int((best_sk < dp).sum())} of {len(rows)} |",
+             f"| geomean torch.matmul / best schedule | {gmean(th / best):.3f} |",
+             f"| mean torch.matmul / hybrid | {float(np.mean(th / hy)):.3f} |",
+             f"| shapes where the best schedule beats torch.matmul | {int((best < th).sum())} of {len(rows)} |",
+             "", "By tile count T (256x256 tiles) relative to the 256 CUs:", "",
+             "| T range | shapes | geomean DP / best SK-hybrid | geomean torch / best |",
+             "|---|---|---|---|"]
+    Ts = np.array([r[3] for r in rows])
+    for lo_, hi_ in ((1, 64), (65, 192), (193, 256), (257, 512), (513, 4096)):
+        m = (Ts >= lo_) & (Ts <= hi_)
+        if m.any():
+            lines.append(f"| {lo_}-{hi_} | {int(m.sum())} | {gmean(dp[m] / best_sk[m]):.3f} | "
+                         f"{gmean(th[m] / best[m]):.3f} |")
+    lines += ["", "First 40 shapes (us):", "",
+              "| M | N | K | T | dp | Stream-K | hybrid | torch.matmul |", "|---|---|---|---|---|---|---|---|"]
+    for (M, N, K, T, us) in rows[:40]:
+        lines.append(f"| {M} | {N} | {K} | {T} | {us['dp']:.1f} | {us['streamk']:.1f} | "
+                     f"{us['hybrid']:.1f} | {us['torch']:.1f} |")
+    text = "\n".join(lines) + "\n"
+    open(out, "w").write(text)
+    log(text)
+
+
 def load_traffic(workload, schedule):
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
@@ -303,6 +412,10 @@ def main():
                          "each workload in --workload (comma list, or 'irregular'); write "
                          "a markdown table to FILE")
     ap.add_argument("--grid-sweep-rows", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--log-sampled", type=int, default=0, metavar="N",
+                    help="the pages' shape benchmark: N log-sampled fp16 shapes (multiples of "
+                         "256 in [256, 8192]), DP / Stream-K / hybrid and torch.matmul")
+    ap.add_argument("--log-sampled-out", default="log_sampled.md", metavar="FILE")
     ap.add_argument("--traffic-run", default=None, metavar="SCHEDULE",
                     help="no timing: run a 256 MiB device copy, then this schedule's GEMM, "
                          "three times each (for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)")
@@ -333,6 +446,9 @@ def main():
         return
     if args.grid_sweep_rows:
         grid_sweep_rows(args)
+        return
+    if args.log_sampled:
+        log_sampled(args, args.log_sampled_out)
         return
     wl = workload_table()[args.workload]
     M, N, K, dt = wl["M"], wl["N"], wl["K"], wl["dtype"]

@@ -53,6 +53,52 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Default output tile for fp16/bf16 when the caller names none.
+//
+// Tile-per-workgroup schedules (DP, persistent): a wave-quantisation model.
+// A launch runs ceil(T / CUs) waves of tiles; a tile costs a fixed prologue
+// and epilogue plus ipt MAC iterations (64 deep) at the per-iteration time
+// that tile shape sustains with every CU busy, measured on MI355X with the
+// ring kernel: 1.8 us (256x256), 1.47 / 1.45 us (256x128 / 128x256), 0.78 us
+// (128x128).  The cheapest estimate wins; ties go to the larger tile.  Big
+// tiles win once there are enough of them to fill the CUs (4096^3: 256x256),
+// small ones when the big ones would leave CUs idle (1536x1536x8192: 128x128).
+//
+// Stream-K and hybrid spread the MAC iterations over all workgroups whatever
+// the tile, so the tile decides the efficiency of the MAC loop and the size
+// of the fixup: 256x256 when there are at least CUs/2 such tiles, otherwise
+// 256x128 (measured faster on the wave-quantised and long-K shapes, where
+// most tiles are split).
+struct TileChoice {
+    int bm, bn;
+    double iter_us;
+};
+static const TileChoice kTileModel[] = {
+    {256, 256, 1.8}, {256, 128, 1.47}, {128, 256, 1.45}, {128, 128, 0.78}};
+
+void default_tile(int64_t M, int64_t N, int64_t K, gemm_schedule schedule, int cus, int *bm,
+                  int *bn)
+{
+    const int64_t t256 = cdiv(M, 256) * cdiv(N, 256);
+    if (schedule == GEMM_STREAMK || schedule == GEMM_HYBRID) {
+        *bm = 256;
+        *bn = t256 * 2 >= cus ? 256 : 128;
+        return;
+    }
+    const double t0_us = 4.0;
+    const int64_t ipt = cdiv(K > 0 ? K : 1, 64);
+    double best = 0.0;
+    for (const TileChoice &c : kTileModel) {
+        const int64_t T = cdiv(M, c.bm) * cdiv(N, c.bn);
+        const double est = (double)cdiv(T, cus) * (t0_us + (double)ipt * c.iter_us);
+        if (&c == kTileModel || est < best) {
+            best = est;
+            *bm = c.bm;
+            *bn = c.bn;
+        }
+    }
+}
+
 // The first compiled variant matching the request (0 = any): the table lists
 // each dtype's preferred kernel for a tile first.
 const Variant *find_variant(int dtype, const gemm_tiles &t)
@@ -110,10 +156,14 @@ gemm_plan *create(int64_t M, int64_t N, int64_t K, gemm_dtype dtype, gemm_schedu
         t = *tiles_in;
     const int E = elem_size(dtype);
     if (t.bm == 0 && t.bn == 0) {
-        if (dtype == GEMM_F32) {
+        if (dtype == GEMM_F32)
             t.bm = t.bn = (M * N <= 512 * 512) ? 64 : 128;
-        } else {
-            t.bm = t.bn = 256;
+        else {
+            default_tile(M, N, K, schedule, dev.cus, &t.bm, &t.bn);
+            // a wave layout, ring depth or kernel family asked for may exist
+            // only at the 256x256 tile
+            if (!find_variant(dtype, t))
+                t.bm = t.bn = 256;
         }
     } else if (t.bm == 0 || t.bn == 0) {
         set_error("give both bm and bn, or neither");

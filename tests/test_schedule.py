@@ -308,3 +308,22 @@ def test_split_tiles_per_workgroup_at_most_two():
                     assert pieces[0][3] == gsk.ROLE_OWNER and pieces[1][3] == gsk.ROLE_CONTRIB
                 else:
                     assert pieces[0][3] == gsk.ROLE_CONTRIB and pieces[1][3] == gsk.ROLE_OWNER
+
+
+@pytest.mark.parametrize("shape,schedule,tile", [
+    ((4096, 4096, 4096), "dp", (256, 256)),           # 256 tiles fill the CUs exactly
+    ((8192, 28672, 8192), "persistent", (256, 256)),  # 14 full waves
+    ((1536, 1536, 8192), "dp", (128, 128)),           # 36 big tiles would idle 86% of the CUs
+    ((5376, 256, 512), "dp", (128, 128)),
+    ((1536, 1536, 8192), "streamk", (256, 128)),      # few big tiles: the split tile is 256x128
+    ((512, 512, 65536), "hybrid", (256, 128)),
+    ((4096, 4096, 4096), "streamk", (256, 256)),
+])
+def test_default_tile_follows_the_wave_model(shape, schedule, tile):
+    M, N, K = shape
+    plan = gsk.plan_for_device(M, N, K, "f16", schedule)
+    assert (plan.info["bm"], plan.info["bn"]) == tile
+    # an explicit tile always wins, and a layout only built at 256x256 keeps it
+    assert gsk.plan_for_device(M, N, K, "f16", schedule, bm=64, bn=64).info["bm"] == 64
+    p2 = gsk.plan_for_device(M, N, K, "bf16", schedule, wave_m=2, wave_n=4, stages=0)
+    assert p2.info["wave_m"] == 2 and p2.info["wave_n"] == 4
