@@ -102,7 +102,14 @@ enum {
      * only the finished sum is rounded, so the half-precision C of a plan is
      * exactly the rounding of the fp32 C of the same plan without this flag.
      * A no-op for fp32 inputs. */
-    GEMM_FLAG_C_INPUT_DTYPE = 1u << 6
+    GEMM_FLAG_C_INPUT_DTYPE = 1u << 6,
+    /* Testing the fixup's failure detection only: the highest-numbered
+     * workgroup that parks a Stream-K piece never raises its flag, and every
+     * fixup wait gives up after a few thousand polls (a few milliseconds)
+     * instead of about a second.  A run of such a plan ends normally with
+     * workspace status 1 (see gemm_workspace_status) and an invalid C.
+     * gemm_plan_create refuses it for a plan that splits no tile. */
+    GEMM_FLAG_DEBUG_DROP_SIGNAL = 1u << 7
 };
 
 /* Tile and schedule knobs.  Every field 0 means "default". */

@@ -30,6 +30,7 @@ struct gemm_plan {
     int64_t lda, ldb;          // leading dimensions the kernel reads (packed or not)
     size_t off_flags, off_counters, off_partials, off_pack_a, off_pack_b, ws_size;
     int32_t spin_limit;
+    int32_t drop_wg;           // GEMM_FLAG_DEBUG_DROP_SIGNAL: workgroup that never signals
     int split_fixup, max_pieces;
 };
 
@@ -127,6 +128,8 @@ const Variant *find_variant(int dtype, const gemm_tiles &t)
 // real wait (one workgroup's Stream-K share, milliseconds at most), and it
 // turns a lost signal into an error instead of a hung GPU.
 constexpr int32_t kSpinLimit = 1 << 21;
+// GEMM_FLAG_DEBUG_DROP_SIGNAL plans: a few milliseconds
+constexpr int32_t kDebugSpinLimit = 4096;
 
 constexpr int kDiesPerGfx950 = 8;
 
@@ -211,6 +214,7 @@ gemm_plan *create(int64_t M, int64_t N, int64_t K, gemm_dtype dtype, gemm_schedu
     p->xcds = (t.flags & GEMM_FLAG_NO_XCD_REMAP) ? 1 : dev.xcds;
     p->device = device;
     p->spin_limit = kSpinLimit;
+    p->drop_wg = -1;
 
     int occ = dev.wg_per_cu > 0 ? dev.wg_per_cu : 1;
     if (query_occupancy) {
@@ -293,6 +297,17 @@ gemm_plan *create(int64_t M, int64_t N, int64_t K, gemm_dtype dtype, gemm_schedu
         else
             p->split_fixup = p->max_pieces >= 2;
         P.k_aligned = p->split_fixup;
+        if (t.flags & GEMM_FLAG_DEBUG_DROP_SIGNAL) {
+            // the last workgroup whose work includes a parked piece
+            for (int32_t wg = 0; wg < g; ++wg) {
+                WorkCursor c = work_begin(P, wg);
+                WorkItem w;
+                while (work_next(P, wg, c, w))
+                    if (w.role == ROLE_CONTRIB || (w.role == ROLE_OWNER && p->split_fixup))
+                        p->drop_wg = wg;
+            }
+            p->spin_limit = kDebugSpinLimit;
+        }
         const int64_t slots = p->split_fixup ? 2 * (int64_t)g : g;
         if (slots * var->bm * var->bn * 4 >= ((int64_t)1 << 31)) {
             set_error("Stream-K grid %d too large for the partial-tile workspace indexing", g);
@@ -304,6 +319,11 @@ gemm_plan *create(int64_t M, int64_t N, int64_t K, gemm_dtype dtype, gemm_schedu
         p->max_pieces = 1;
         p->split_fixup = 0;
         P.k_aligned = 0;
+    }
+    if ((t.flags & GEMM_FLAG_DEBUG_DROP_SIGNAL) && p->drop_wg < 0) {
+        set_error("GEMM_FLAG_DEBUG_DROP_SIGNAL needs a plan that splits some tile");
+        delete p;
+        return nullptr;
     }
 
     // Workspace: [status word | flags | per-tile counters (split fixup) |
@@ -584,6 +604,7 @@ int gemm_run(const gemm_plan *p, const void *A, const void *B, void *C, void *wo
     // 8-byte (fp16/bf16) store when rows and C keep that alignment
     args.c_vec = (p->N % 4 == 0) && (((uintptr_t)C & (4 * CE - 1)) == 0);
     args.spin_limit = p->spin_limit;
+    args.drop_signal_wg = p->drop_wg;
     args.P = p->P;
     if (p->variant->launch(args, p->P.grid, stream)) {
         set_error("kernel launch failed: %s", hipGetErrorString(hipGetLastError()));

@@ -299,7 +299,7 @@ __device__ __forceinline__ void finish_tile(f32x16 (&acc)[MT][NT], const KernelA
         // every lane's coherent stores have completed before the flag goes up
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (tid == 0)
+        if (tid == 0 && p != args.drop_signal_wg)
             __hip_atomic_store(args.flags + slot_id, 1, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
         return;

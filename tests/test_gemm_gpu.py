@@ -214,6 +214,34 @@ def test_empty_shapes(schedule):
                  torch.empty((M, N), device="cuda"), plan.new_workspace())
 
 
+@pytest.mark.parametrize("fixup", ["head", "split"])
+def test_lost_signal_is_reported_and_workspace_recovers(fixup):
+    # a piece whose flag never rises (forced from the host): every wait on it
+    # is bounded, the kernel ends, and the workspace status says the run failed;
+    # after a zero fill the same workspace serves a normal plan again
+    import persistent_stream_tiling_amd as gsk
+    flag = gsk.FLAG_FIXUP_HEAD if fixup == "head" else gsk.FLAG_FIXUP_SPLIT
+    M, N, K = 256, 512, 16384
+    a, b = inputs.operands(M, N, K, "bf16", "int4", seed=41)
+    rows, cols = inputs.sample_positions(M, N, 1024, seed=42, tails=True)
+    ref, _ = oracle.gemm_sampled(a, b, "bf16", rows, cols)
+    da, db = to_device(a, "bf16"), to_device(b, "bf16")
+    bad = gsk.GemmPlan(M, N, K, "bf16", "streamk", bm=128, bn=128,
+                       flags=flag | gsk.FLAG_DEBUG_DROP_SIGNAL)
+    good = gsk.GemmPlan(M, N, K, "bf16", "streamk", bm=128, bn=128, flags=flag)
+    assert bad.workspace_bytes == good.workspace_bytes and bad.info["max_pieces"] >= 2
+    ws = good.new_workspace()
+    c = torch.empty((M, N), device="cuda")
+    bad.run(da, db, c, ws)
+    torch.cuda.synchronize()
+    assert bad.workspace_status(ws) == 1
+    ws.zero_()
+    good.run(da, db, c, ws)
+    torch.cuda.synchronize()
+    assert good.workspace_status(ws) == 0
+    compare(c.cpu().numpy()[rows, cols], ref, None, "bf16", exact=True, what=good.describe())
+
+
 def test_side_stream_and_reuse_across_plans():
     M, N, K = 300, 200, 704
     a, b, ref, scale = small_inputs(M, N, K, "f16")

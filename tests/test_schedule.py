@@ -327,3 +327,13 @@ def test_default_tile_follows_the_wave_model(shape, schedule, tile):
     assert gsk.plan_for_device(M, N, K, "f16", schedule, bm=64, bn=64).info["bm"] == 64
     p2 = gsk.plan_for_device(M, N, K, "bf16", schedule, wave_m=2, wave_n=4, stages=0)
     assert p2.info["wave_m"] == 2 and p2.info["wave_n"] == 4
+
+
+def test_debug_drop_signal_needs_a_split_tile():
+    drop = gsk.FLAG_DEBUG_DROP_SIGNAL
+    # 8 tiles of 128x128 over 256 workgroups: every tile is split
+    plan = gsk.plan_for_device(256, 512, 65536, "bf16", "streamk", bm=128, bn=128, flags=drop)
+    assert plan.info["max_pieces"] >= 2
+    for sched in ("dp", "persistent"):
+        with pytest.raises(ValueError, match="splits some tile"):
+            gsk.plan_for_device(256, 512, 65536, "bf16", sched, bm=128, bn=128, flags=drop)
