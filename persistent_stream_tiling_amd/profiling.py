@@ -190,6 +190,59 @@ def counters_table(records, cmd):
     return "\n".join(lines) + "\n"
 
 
+def kernel_resources(out, cmd_note):
+    """Per compiled kernel: registers, spills, scratch, occupancy and LDS, from
+    the compiler's kernel-resource-usage remarks (device code of kernels.hip,
+    compiled exactly as the library is)."""
+    import re
+    import subprocess
+    import tempfile
+    from . import _build
+    src = os.path.join(_build.CSRC, "kernels.hip")
+    with tempfile.TemporaryDirectory() as tmp:
+        cmd = [_build.hipcc(), f"--offload-arch={_build.ARCH}", "-O3", "-std=c++17",
+               f"-I{_build.INCLUDE}", f"-I{_build.CSRC}", "-Xclang", "-target-feature", "-Xclang",
+               "-packed-fp32-ops", "--cuda-device-only", "-c",
+               "-Rpass-analysis=kernel-resource-usage", src, "-o", os.path.join(tmp, "k.o")]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(res.stderr[-4000:])
+    recs, cur = [], None
+    for line in res.stderr.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            cur = {"name": m.group(1)}
+            recs.append(cur)
+            continue
+        m = re.search(r"remark:\s+([A-Za-z ]+?)(?: \[[^\]]*\])?: (\S+) \[-Rpass", line)
+        if m and cur is not None:
+            cur[m.group(1).strip()] = m.group(2)
+
+    def pretty(mangled):
+        m = re.match(r"_ZN3gsk\d+(\w+?)I(.*)EEvNS_10KernelArgsE", mangled)
+        if not m:
+            return mangled
+        args = ", ".join(re.findall(r"Li(\d+)E", m.group(2)))
+        return f"{m.group(1)}<{args}>"
+    gemm = [r for r in recs if "KernelArgs" in r["name"]]
+    lines = ["# Kernel resources (compiler remarks)", "",
+             f"Command: `{cmd_note}`", "",
+             f"Kernel source hash: {source_hash()}.  Template arguments: <dtype (0 fp32, 1 fp16, "
+             "2 bf16), bm, bn, waves along M, waves along N[, ring stages]>.  gemm_kernel_pair is "
+             "the fp16/bf16 default (whole-row A ring), gemm_kernel_dma the half-row A ring, "
+             "gemm_kernel the register-staged kernel (fp32 default).", "",
+             "| kernel | VGPRs | AGPRs | SGPRs | VGPR spills | SGPR spills | scratch B/lane | "
+             "waves/SIMD | LDS B |", "|---|---|---|---|---|---|---|---|---|"]
+    for r in gemm:
+        lines.append(f"| `{pretty(r['name'])}` | {r.get('VGPRs')} | {r.get('AGPRs')} | "
+                     f"{r.get('TotalSGPRs')} | {r.get('VGPRs Spill')} | {r.get('SGPRs Spill')} | "
+                     f"{r.get('ScratchSize')} | {r.get('Occupancy')} | "
+                     f"{r.get('LDS Size')} |")
+    text = "\n".join(lines) + "\n"
+    open(out, "w").write(text)
+    return text
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd_name", required=True)
@@ -216,8 +269,13 @@ def main():
     c.add_argument("--steps", type=int, default=3)
     c.add_argument("--out", required=True)
     c.add_argument("--cmd", required=True)
+    r = sub.add_parser("resources")
+    r.add_argument("--out", required=True)
     a = ap.parse_args()
-    if a.cmd_name == "counters":
+    if a.cmd_name == "resources":
+        print(kernel_resources(a.out, "python -m persistent_stream_tiling_amd.profiling "
+                                      "resources --out " + a.out))
+    elif a.cmd_name == "counters":
         from . import inputs
         table = dict(inputs.WORKLOADS, **inputs.irregular_workloads())
         recs = []
