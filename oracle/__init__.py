@@ -6,7 +6,7 @@ import this package.  The GPU library never imports, links or runs it.
 The arithmetic lives in ``oracle.c`` (plain C, fp64, ascending-k sums); this
 module only compiles it with gcc and marshals numpy arrays through ctypes.
 Inputs are raw bit patterns: ``uint32``/``float32`` for fp32, ``uint16`` for
-fp16 and bf16, exactly as the GPU reads them.
+fp16 and bf16, ``int8`` for int8, exactly as the GPU reads them.
 """
 import ctypes
 import os
@@ -18,7 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
-DTYPES = {"f32": 0, "f16": 1, "bf16": 2}
+DTYPES = {"f32": 0, "f16": 1, "bf16": 2, "i8": 3}
 
 _lib = None
 
@@ -55,8 +55,10 @@ def load(path=LIB):
 
 
 def _bits(x, dtype):
-    want = np.uint32 if dtype == "f32" else np.uint16
+    want = {"f32": np.uint32, "i8": np.int8}.get(dtype, np.uint16)
     x = np.ascontiguousarray(x)
+    if x.dtype == np.uint8 and dtype == "i8":
+        x = x.view(np.int8)
     if x.dtype == np.float32 and dtype == "f32":
         x = x.view(np.uint32)
     if x.dtype == np.float16 and dtype == "f16":

@@ -17,10 +17,13 @@
  *     S[i][j] = sum_{k=0}^{K-1} |a[i][k]| * |b[k][j]|
  *
  * a and b are the input values exactly as stored (fp32, fp16 or bf16 bit
- * patterns, decoded here by hand).  Every product and every partial sum is an
- * IEEE double, summed in ascending k.  Products of two fp32/fp16/bf16 values
- * have at most 48 significant bits, so each product is exact in fp64 and the
- * only rounding is in the sum (|error| <= (K-1) * 2^-53 * S).
+ * patterns, decoded here by hand, or two's-complement int8, whose products
+ * the same revision accumulates in int32).  Every product and every partial
+ * sum is an IEEE double, summed in ascending k.  Products of two
+ * fp32/fp16/bf16 values have at most 48 significant bits, so each product is
+ * exact in fp64 and the only rounding is in the sum (|error| <= (K-1) *
+ * 2^-53 * S); int8 products are at most 2^14 in magnitude, so int8 sums are
+ * exact integers for any K below 2^39.
  *
  * S is the scale used by the acceptance bound |C_gpu - C| <= tol * S.
  *
@@ -43,6 +46,7 @@
 #define ORACLE_F32 0
 #define ORACLE_F16 1
 #define ORACLE_BF16 2
+#define ORACLE_I8 3
 
 /* IEEE binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
 static double decode_f16(uint16_t h)
@@ -98,12 +102,14 @@ static double elem(int dtype, const void *p, int64_t idx)
         return decode_f32(((const uint32_t *)p)[idx]);
     if (dtype == ORACLE_F16)
         return decode_f16(((const uint16_t *)p)[idx]);
+    if (dtype == ORACLE_I8)
+        return (double)((const int8_t *)p)[idx];
     return decode_bf16(((const uint16_t *)p)[idx]);
 }
 
 int oracle_decode_array(int dtype, const void *p, int64_t n, double *out)
 {
-    if (dtype < ORACLE_F32 || dtype > ORACLE_BF16 || n < 0 || (n && (!p || !out)))
+    if (dtype < ORACLE_F32 || dtype > ORACLE_I8 || n < 0 || (n && (!p || !out)))
         return -1;
     for (int64_t i = 0; i < n; ++i)
         out[i] = elem(dtype, p, i);
@@ -143,7 +149,7 @@ static void *full_worker(void *arg)
 int oracle_gemm_full(int dtype, int64_t M, int64_t N, int64_t K, const void *A, const void *B,
                      double *C, double *S, int nthreads)
 {
-    if (dtype < ORACLE_F32 || dtype > ORACLE_BF16 || M < 0 || N < 0 || K < 0 || !C)
+    if (dtype < ORACLE_F32 || dtype > ORACLE_I8 || M < 0 || N < 0 || K < 0 || !C)
         return -1;
     if (M == 0 || N == 0)
         return 0;
@@ -221,7 +227,7 @@ int oracle_gemm_sampled(int dtype, int64_t M, int64_t N, int64_t K, const void *
                         int64_t n, const int64_t *rows, const int64_t *cols, double *C, double *S,
                         int nthreads)
 {
-    if (dtype < ORACLE_F32 || dtype > ORACLE_BF16 || M < 0 || N < 0 || K < 0 || n < 0)
+    if (dtype < ORACLE_F32 || dtype > ORACLE_I8 || M < 0 || N < 0 || K < 0 || n < 0)
         return -1;
     if (n == 0)
         return 0;

@@ -77,12 +77,19 @@ def to_bits(x32, dtype):
         return x32.astype(np.float16).view(np.uint16)
     if dtype == "bf16":
         return f32_to_bf16_bits(x32)
+    if dtype == "i8":
+        # int8 operands are drawn as integers (distributions 'int8', 'int4')
+        if not (np.all(x32 == np.round(x32)) and x32.min(initial=0) >= -128
+                and x32.max(initial=0) <= 127):
+            raise ValueError("i8 operands need integer values in [-128, 127]")
+        return x32.astype(np.int8)
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
 def draw(shape, dist, seed, scale=1.0):
-    """float32 samples: 'normal' = N(0,1), 'uniform' = U[-1,1), 'int4' = integers in [-4,4]."""
-    if dist not in ("normal", "uniform", "int4"):
+    """float32 samples: 'normal' = N(0,1), 'uniform' = U[-1,1), 'int4' = integers in [-4,4],
+    'int8' = integers in [-128, 127]."""
+    if dist not in ("normal", "uniform", "int4", "int8"):
         raise ValueError(f"unknown distribution {dist!r}")
     x = np.empty(shape, dtype=np.float32)
     flat = x.reshape(-1)
@@ -96,8 +103,10 @@ def draw(shape, dist, seed, scale=1.0):
             rng.random(out=part, dtype=np.float32)
             part *= np.float32(2.0)
             part -= np.float32(1.0)
-        else:
+        elif dist == "int4":
             part[:] = rng.integers(-4, 5, size=hi - lo)
+        else:
+            part[:] = rng.integers(-128, 128, size=hi - lo)
         if scale != 1.0:
             part *= np.float32(scale)
 

@@ -243,8 +243,40 @@ def pin_thread_invariance(lib):
     assert not np.isnan(C1).any()
 
 
+def pin_int8(lib):
+    # int8 (the final revision's int32-accumulator branch): every value and
+    # every sum is an exact integer, so C must equal plain Python integer sums
+    every = np.arange(-128, 128, dtype=np.int8)
+    assert np.array_equal(oracle.decode(every, "i8", lib=lib), every.astype(np.float64))
+    rng = np.random.Generator(np.random.PCG64(37))
+    for (M, N, K) in ((1, 1, 1), (3, 4, 5), (7, 2, 9), (5, 6, 33)):
+        a = rng.integers(-128, 128, size=(M, K)).astype(np.int8)
+        b = rng.integers(-128, 128, size=(K, N)).astype(np.int8)
+        C, S = oracle.gemm(a, b, "i8", lib=lib)
+        for i in range(M):
+            for j in range(N):
+                assert C[i, j] == sum(int(a[i, k]) * int(b[k, j]) for k in range(K))
+                assert S[i, j] == sum(abs(int(a[i, k])) * abs(int(b[k, j])) for k in range(K))
+    # extremes: (-128)(-128) summed K times, and 127 * -128
+    K = 4097
+    C, _ = oracle.gemm(np.full((2, K), -128, np.int8), np.full((K, 3), -128, np.int8), "i8",
+                       lib=lib)
+    assert np.all(C == 16384 * K)
+    C, _ = oracle.gemm(np.full((2, K), 127, np.int8), np.full((K, 3), -128, np.int8), "i8",
+                       lib=lib)
+    assert np.all(C == -16256 * K)
+    # the sampled path on a long K: exact int64 sums
+    M, N, K = 4, 5, 70000
+    a = rng.integers(-128, 128, size=(M, K)).astype(np.int8)
+    b = rng.integers(-128, 128, size=(K, N)).astype(np.int8)
+    rows, cols = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    Cs, _ = oracle.gemm_sampled(a, b, "i8", rows.ravel(), cols.ravel(), lib=lib)
+    assert np.array_equal(Cs, (a.astype(np.int64) @ b.astype(np.int64)).astype(np.float64).ravel())
+
+
 ALL_PINS = [
     pin_decode_f16_all, pin_decode_bf16_all, pin_decode_f32_sample, pin_hand_worked,
     pin_rational_tiny, pin_identity_permutation, pin_small_integers, pin_closed_forms,
     pin_invariants, pin_numpy_crosscheck, pin_sampled_matches_full, pin_thread_invariance,
+    pin_int8,
 ]

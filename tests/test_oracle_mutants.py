@@ -39,6 +39,8 @@ MUTANTS = {
                         "double b = elem(jb->dtype, jb->B, j * jb->K + k);"),
     "sampled_col_off_by_one": ("int64_t i = jb->rows[s], j = jb->cols[s];",
                                "int64_t i = jb->rows[s], j = (jb->cols[s] + 1) % jb->N;"),
+    "i8_unsigned": ("return (double)((const int8_t *)p)[idx];",
+                    "return (double)((const uint8_t *)p)[idx];"),
     "last_row_skipped": ("M * t / nthreads, M * (t + 1) / nthreads}",
                          "M * t / nthreads, M * (t + 1) / nthreads - (t == nthreads - 1)}"),
 }
