@@ -22,7 +22,7 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "f32": 157.3}  # dense MFMA, 2.4 GHz
+PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "f32": 157.3, "i8": 5033.2}  # dense MFMA, 2.4 GHz
 PEAK_HBM_GBS = 8000.0
 SCHEDULES = ("dp", "persistent", "streamk", "hybrid")
 METRIC = "GEMM TFLOP/s and % of MFMA peak per schedule (DP / persistent / Stream-K)"
@@ -39,13 +39,15 @@ def kernel_source_hash():
 
 def workload_table():
     from persistent_stream_tiling_amd import inputs
-    return dict(inputs.WORKLOADS, **inputs.irregular_workloads())
+    return dict(inputs.WORKLOADS, **inputs.EXTRA_WORKLOADS, **inputs.irregular_workloads())
 
 
 def to_device(bits, dtype):
     import torch
     if dtype == "f32":
         t = torch.from_numpy(np.ascontiguousarray(bits).view(np.float32))
+    elif dtype == "i8":
+        t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int8))
     else:
         t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
         t = t.view(torch.float16 if dtype == "f16" else torch.bfloat16)
@@ -57,7 +59,7 @@ def algorithmic_bytes(M, N, K, dtype, plan_info):
     plan stores C in it); the callers add the Stream-K partials written and
     read once."""
     from persistent_stream_tiling_amd import FLAG_C_INPUT_DTYPE
-    e = 4 if dtype == "f32" else 2
+    e = {"f32": 4, "i8": 1}.get(dtype, 2)
     ce = e if plan_info["flags"] & FLAG_C_INPUT_DTYPE else 4
     return (M * K + K * N) * e + M * N * ce
 
@@ -455,8 +457,9 @@ def main():
     log(f"[bench] {args.workload}: {M}x{N}x{K} {dt} {wl['dist']} seed {wl['seed']}")
     a_bits, b_bits = inputs.operands(M, N, K, dt, wl["dist"], wl["seed"], wl["scale"])
     a, b = to_device(a_bits, dt), to_device(b_bits, dt)
-    c_half = args.c_dtype == "input" and dt != "f32"
-    c = torch.empty((M, N), dtype=a.dtype if c_half else torch.float32, device="cuda")
+    c_half = args.c_dtype == "input" and dt in ("f16", "bf16")
+    c_type = torch.int32 if dt == "i8" else (a.dtype if c_half else torch.float32)
+    c = torch.empty((M, N), dtype=c_type, device="cuda")
     flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
     flops = 2.0 * M * N * K
     bound = "hbm" if args.workload == "bf16_512x512x65536" else "mfma"
@@ -523,12 +526,13 @@ def main():
         got = c[torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()].float().cpu().numpy()
         rel = np.abs(got.astype(np.float64) - ref) / np.maximum(scale, 1e-300)
         check = {"samples": int(rows.size), "max_err_over_S": float(rel.max()),
-                 "tolerance": 1e-5 if dt == "f32" else 4e-3}
+                 "tolerance": {"f32": 1e-5, "i8": 0.0}.get(dt, 4e-3)}
         log(f"[bench] oracle check on {rows.size} samples: max |C-C_ref|/S = {rel.max():.3e}")
 
     if bound == "mfma":
         roof = {"bound": "mfma", "achieved": rec["tflops"], "peak": PEAK_TFLOPS[dt],
-                "unit": "TFLOP/s", "frac": round(rec["tflops"] / PEAK_TFLOPS[dt], 4)}
+                "unit": "TOP/s" if dt == "i8" else "TFLOP/s",
+                "frac": round(rec["tflops"] / PEAK_TFLOPS[dt], 4)}
     else:
         roof = {"bound": "hbm", "achieved": rec["hbm_gbs"], "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(rec["hbm_gbs"] / PEAK_HBM_GBS, 4)}
@@ -537,7 +541,7 @@ def main():
     line = {
         "metric": METRIC,
         "value": rec["tflops"],
-        "unit": "TFLOP/s",
+        "unit": "TOP/s" if dt == "i8" else "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,

@@ -57,7 +57,11 @@
 extern "C" {
 #endif
 
-typedef enum { GEMM_F32 = 0, GEMM_F16 = 1, GEMM_BF16 = 2 } gemm_dtype;
+/* Input dtype.  fp32/fp16/bf16 accumulate in fp32 and write fp32 C (or the
+ * input dtype, GEMM_FLAG_C_INPUT_DTYPE).  GEMM_I8: int8 inputs accumulate in
+ * int32, exactly, and C is int32 (the accumulator type issue #1393's final
+ * revision picks for int8); K must stay below 2^17 so no sum can overflow. */
+typedef enum { GEMM_F32 = 0, GEMM_F16 = 1, GEMM_BF16 = 2, GEMM_I8 = 3 } gemm_dtype;
 
 typedef enum {
     GEMM_DP = 0,
@@ -119,7 +123,7 @@ typedef struct {
     int32_t bk;       /* k-depth of one MAC iteration, fixed per kernel: 64
                          for the fp16/bf16 ring kernels (32 with
                          GEMM_FLAG_A_HALF_ROWS) and the register-staged one,
-                         32 for fp32; 0 = any */
+                         32 for fp32, 128 for int8; 0 = any */
     int32_t grid;     /* g: workgroups of the persistent / Stream-K launch;
                          0 = number of CUs (issue #1393 uses the SM count) */
     int32_t group_m;  /* tile-order group height (issue #1393 GROUP_M);
@@ -168,8 +172,8 @@ gemm_plan *gemm_plan_create_for_device(int64_t M, int64_t N, int64_t K, gemm_dty
  * when allocated; it may be NULL when that size is 0.  A run leaves the
  * workspace's flags zero again, so it can be reused by later runs without
  * clearing.  Two runs that overlap in time must not share a workspace.
- * C points to M x N fp32 values, or to fp16/bf16 values when the plan was
- * made with GEMM_FLAG_C_INPUT_DTYPE.
+ * C points to M x N fp32 values, to fp16/bf16 values when the plan was made
+ * with GEMM_FLAG_C_INPUT_DTYPE, or to int32 values for int8 inputs.
  * Returns 0, or -1 invalid argument (NULL or misaligned pointer), -2 workspace
  * missing, -3 HIP launch error, -5 plan made for another device.
  */

@@ -5,7 +5,7 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libgemmsk.so")
 
-F32, F16, BF16 = 0, 1, 2
+F32, F16, BF16, I8 = 0, 1, 2, 3
 DP, PERSISTENT, STREAMK, HYBRID = 0, 1, 2, 3
 FLAG_ONE_TILE = 1 << 0
 FLAG_NO_XCD_REMAP = 1 << 1
@@ -18,7 +18,7 @@ FLAG_DEBUG_DROP_SIGNAL = 1 << 7
 ROLE_FULL, ROLE_CONTRIB, ROLE_OWNER = 0, 1, 2
 
 SCHEDULES = {"dp": DP, "persistent": PERSISTENT, "streamk": STREAMK, "hybrid": HYBRID}
-DTYPES = {"f32": F32, "f16": F16, "bf16": BF16}
+DTYPES = {"f32": F32, "f16": F16, "bf16": BF16, "i8": I8}
 
 
 class Tiles(ctypes.Structure):

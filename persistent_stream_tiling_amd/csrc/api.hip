@@ -48,7 +48,7 @@ void set_error(const char *fmt, ...)
     g_error = buf;
 }
 
-int elem_size(int dtype) { return dtype == GEMM_F32 ? 4 : 2; }
+int elem_size(int dtype) { return dtype == GEMM_F32 ? 4 : (dtype == GEMM_I8 ? 1 : 2); }
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -108,7 +108,8 @@ const Variant *find_variant(int dtype, const gemm_tiles &t)
     // then the one with half-row A copies (or only that one when asked for),
     // and fall back to the register-staged one for tiles neither covers
     // (unless staged loads were asked for explicitly).
-    const bool staged_only = (t.flags & GEMM_FLAG_REGISTER_STAGED) || dtype == GEMM_F32;
+    const bool staged_only =
+        (t.flags & GEMM_FLAG_REGISTER_STAGED) || dtype == GEMM_F32 || dtype == GEMM_I8;
     const bool half_rows = (t.flags & GEMM_FLAG_A_HALF_ROWS) != 0;
     int n = 0;
     const Variant *v = variants(&n);
@@ -128,6 +129,8 @@ const Variant *find_variant(int dtype, const gemm_tiles &t)
 // real wait (one workgroup's Stream-K share, milliseconds at most), and it
 // turns a lost signal into an error instead of a hung GPU.
 constexpr int32_t kSpinLimit = 1 << 21;
+// int8: |a*b| <= 2^14, so sums over K < 2^17 stay inside int32
+constexpr int64_t kI8MaxK = (int64_t)1 << 17;
 // GEMM_FLAG_DEBUG_DROP_SIGNAL plans: a few milliseconds
 constexpr int32_t kDebugSpinLimit = 4096;
 
@@ -141,7 +144,7 @@ gemm_plan *create(int64_t M, int64_t N, int64_t K, gemm_dtype dtype, gemm_schedu
         set_error("negative size M=%lld N=%lld K=%lld", (long long)M, (long long)N, (long long)K);
         return nullptr;
     }
-    if (dtype != GEMM_F32 && dtype != GEMM_F16 && dtype != GEMM_BF16) {
+    if (dtype != GEMM_F32 && dtype != GEMM_F16 && dtype != GEMM_BF16 && dtype != GEMM_I8) {
         set_error("unknown dtype %d", (int)dtype);
         return nullptr;
     }
@@ -161,6 +164,8 @@ gemm_plan *create(int64_t M, int64_t N, int64_t K, gemm_dtype dtype, gemm_schedu
     if (t.bm == 0 && t.bn == 0) {
         if (dtype == GEMM_F32)
             t.bm = t.bn = (M * N <= 512 * 512) ? 64 : 128;
+        else if (dtype == GEMM_I8)
+            t.bm = t.bn = cdiv(M, 256) * cdiv(N, 256) >= dev.cus ? 256 : 128;
         else {
             default_tile(M, N, K, schedule, dev.cus, &t.bm, &t.bn);
             // a wave layout, ring depth or kernel family asked for may exist
@@ -170,6 +175,15 @@ gemm_plan *create(int64_t M, int64_t N, int64_t K, gemm_dtype dtype, gemm_schedu
         }
     } else if (t.bm == 0 || t.bn == 0) {
         set_error("give both bm and bn, or neither");
+        return nullptr;
+    }
+    if (dtype == GEMM_I8 && K >= kI8MaxK) {
+        set_error("int8: K = %lld could overflow the int32 sums (K < %lld)", (long long)K,
+                  (long long)kI8MaxK);
+        return nullptr;
+    }
+    if (dtype == GEMM_I8 && (t.flags & GEMM_FLAG_C_INPUT_DTYPE)) {
+        set_error("int8 products are written as int32; GEMM_FLAG_C_INPUT_DTYPE does not apply");
         return nullptr;
     }
     const Variant *var = find_variant(dtype, t);
@@ -367,8 +381,8 @@ const char *sched_name(int s)
 
 const char *dtype_name(int d)
 {
-    static const char *names[] = {"f32", "f16", "bf16"};
-    return (d >= 0 && d < 3) ? names[d] : "?";
+    static const char *names[] = {"f32", "f16", "bf16", "i8"};
+    return (d >= 0 && d < 4) ? names[d] : "?";
 }
 
 }  // namespace
@@ -468,7 +482,10 @@ int gemm_plan_describe(const gemm_plan *p, char *buf, size_t len)
                     "lds=%zu B, capacity=%d wg, xcds=%d | fixup=%s pieces<=%d | pack A=%d B=%d | "
                     "workspace=%zu B",
                     (long long)p->M, (long long)p->N, (long long)p->K, dtype_name(p->dtype),
-                    dtype_name((p->flags & GEMM_FLAG_C_INPUT_DTYPE) ? p->dtype : GEMM_F32),
+                    p->dtype == GEMM_I8 ? "i32"
+                                        : dtype_name((p->flags & GEMM_FLAG_C_INPUT_DTYPE)
+                                                         ? p->dtype
+                                                         : GEMM_F32),
                     sched_name(p->schedule), p->bm, p->bn, p->bk, p->variant->wave_m,
                     p->variant->wave_n, p->variant->kind == 2 ? "ring/rows" : p->variant->kind ? "ring" : "staged",
                     p->variant->kind ? p->variant->stages : 2, p->group_m, p->P.tiles_m,

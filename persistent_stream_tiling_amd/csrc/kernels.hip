@@ -8,8 +8,13 @@
 //                     128-byte rows), an unrolled ring of B stages and A slots.
 //   gemm_kernel_dma   fp16/bf16 with 32-deep iterations and A in 64-byte row
 //                     halves (kept for comparison).
-//   gemm_kernel       fp32, and a register-staged fp16/bf16 variant: loads go
-//                     global -> registers -> LDS, two LDS buffers.
+//   gemm_kernel       fp32 and int8, and a register-staged fp16/bf16 variant:
+//                     loads go global -> registers -> LDS, two LDS buffers.
+//
+// int8 inputs accumulate exactly in int32 (the pages' kernel picks an int32
+// accumulator for int8); the int32 accumulators travel in the same 32-bit
+// registers, partial slots and C stores as fp32 ones, and only the Stream-K
+// fixup's additions differ (integer adds).
 //
 // All use the 32x32 MFMA with the operands swapped (B^T as the "A" operand),
 // so the accumulator block holds C^T: each lane then owns four consecutive
@@ -33,6 +38,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef int32_t s32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t s32x16 __attribute__((ext_vector_type(16)));
 
 constexpr uint32_t kOutOfRange = 0x80000000u;
 // Cache-policy operand of a buffer access that is coherent at agent scope
@@ -69,7 +76,7 @@ __device__ __forceinline__ uint32_t lds_offset(int row, int chunk)
 template <int DT, int BM, int BN, int WM, int WN>
 struct Tile {
     static constexpr int NTH = 64 * WM * WN;
-    static constexpr int E = DT == 0 ? 4 : 2;         // bytes per element
+    static constexpr int E = DT == 0 ? 4 : (DT == 3 ? 1 : 2); // bytes per element
     static constexpr int V = 16 / E;                  // elements per 16-byte chunk
     static constexpr int BK = 128 / E;                // k per MAC iteration (8 chunks)
     static constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -84,6 +91,7 @@ struct Tile {
     static_assert(A_LOADS >= 1 && A_LOADS * NTH == BM * 8, "A slab must split evenly");
     static_assert(B_LOADS >= 2 && B_LOADS * NTH * V == BK * BN, "B slab must split evenly");
     static_assert(NB * R == B_LOADS && (R == 2 || R == 4 || R == 8), "B block shape");
+    static_assert(R * E >= 4, "a transposed block must fill whole 32-bit words");
     static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
@@ -98,6 +106,14 @@ __device__ __forceinline__ void mfma_step(f32x16 &acc, const u32x4 &bt, const u3
     } else if constexpr (DT == 2) {
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, bt),
                                                       __builtin_bit_cast(bf16x8, a), acc, 0, 0, 0);
+    } else if constexpr (DT == 3) {
+        // int8: 16 k per lane and operand, exact int32 sums kept in the
+        // accumulator's 32-bit registers
+        acc = __builtin_bit_cast(
+            f32x16, __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(s32x4, bt),
+                                                          __builtin_bit_cast(s32x4, a),
+                                                          __builtin_bit_cast(s32x16, acc), 0, 0,
+                                                          0));
     } else {
         // fp32: a lane's chunk is 4 consecutive k; instruction e takes element e
         // from both operands, so the same k meets the same k.  (The whole vector
@@ -125,6 +141,25 @@ struct Transposed<2, R> {
 #pragma unroll
         for (int j = 0; j < R / 2; ++j)
             w[j] = __builtin_amdgcn_perm(rows[2 * j + 1][v >> 1], rows[2 * j][v >> 1], sel);
+    }
+};
+
+template <int R>
+struct Transposed<1, R> {
+    uint32_t w[R / 4];
+    __device__ __forceinline__ void gather(const u32x4 *rows, int v)
+    {
+        // byte v&3 of word v>>2 of four rows -> one word, k ascending
+        const uint32_t b = (uint32_t)(v & 3);
+        const uint32_t sel = b | ((4u + b) << 8);
+#pragma unroll
+        for (int j = 0; j < R / 4; ++j) {
+            const uint32_t lo = __builtin_amdgcn_perm(rows[4 * j + 1][v >> 2],
+                                                      rows[4 * j][v >> 2], sel);
+            const uint32_t hi = __builtin_amdgcn_perm(rows[4 * j + 3][v >> 2],
+                                                      rows[4 * j + 2][v >> 2], sel);
+            w[j] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+        }
     }
 };
 
@@ -254,6 +289,27 @@ __device__ __forceinline__ void wait_flags(const KernelArgs &args, int32_t q_fir
     }
 }
 
+// a + b for two accumulator words: fp32 sums, or int32 sums carried in the
+// same 32-bit registers (int8 inputs).  By value (see bits_of).
+template <bool IACC>
+__device__ __forceinline__ float acc_add(float a, float b)
+{
+    if constexpr (IACC)
+        return __builtin_bit_cast(float, (int32_t)((uint32_t)__builtin_bit_cast(int32_t, a) +
+                                                   (uint32_t)__builtin_bit_cast(int32_t, b)));
+    else
+        return a + b;
+}
+
+template <bool IACC>
+__device__ __forceinline__ f32x4 acc_add4(const f32x4 &a, const f32x4 &b)
+{
+    if constexpr (IACC)
+        return __builtin_bit_cast(f32x4, __builtin_bit_cast(u32x4, a) + __builtin_bit_cast(u32x4, b));
+    else
+        return a + b;
+}
+
 // Finish one unit of work: a Stream-K tail is parked in the workgroup's
 // partial slot and signalled; a split tile's head waits for its later
 // workgroups and adds their partials; then the tile is stored to C.
@@ -266,7 +322,7 @@ __device__ __forceinline__ void wait_flags(const KernelArgs &args, int32_t q_fir
 // it are fully coalesced.  Partial slots are addressed through a buffer
 // descriptor: lane offset in a VGPR and the fragment's offset as a scalar
 // constant, so no per-fragment 64-bit addresses stay alive.
-template <int BM, int BN, int MT, int NT>
+template <int BM, int BN, int MT, int NT, bool IACC = false>
 __device__ __forceinline__ void finish_tile(f32x16 (&acc)[MT][NT], const KernelArgs &args,
                                             const WorkItem &w, int p, int m0, int n0, int wave,
                                             int lane, int row0, int col0)
@@ -330,10 +386,10 @@ __device__ __forceinline__ void finish_tile(f32x16 (&acc)[MT][NT], const KernelA
                         const f32x4 v = __builtin_bit_cast(
                             f32x4, __builtin_amdgcn_raw_buffer_load_b128(slots, (int)off,
                                                                          g * 1024, kAgentCoherent));
-                        blk[4 * g] += v[0];
-                        blk[4 * g + 1] += v[1];
-                        blk[4 * g + 2] += v[2];
-                        blk[4 * g + 3] += v[3];
+                        blk[4 * g] = acc_add<IACC>(blk[4 * g], v[0]);
+                        blk[4 * g + 1] = acc_add<IACC>(blk[4 * g + 1], v[1]);
+                        blk[4 * g + 2] = acc_add<IACC>(blk[4 * g + 2], v[2]);
+                        blk[4 * g + 3] = acc_add<IACC>(blk[4 * g + 3], v[3]);
                     }
                 }
                 store_block(blk, args, c_rsrc, m0, n0, row0 + mt * 32 + l32, col0 + nt * 32,
@@ -355,7 +411,7 @@ __device__ __forceinline__ void finish_tile(f32x16 (&acc)[MT][NT], const KernelA
 // head's workgroup would use, so the result does not depend on who reduces.
 // The last workgroup to finish with a tile clears its flags and counter.
 // Blocks are numbered in the writer's fragment order (wave, mt, nt).
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, bool IACC = false>
 __device__ __forceinline__ void reduce_split_tiles(const KernelArgs &args, int p, int wave,
                                                    int lane)
 {
@@ -405,7 +461,7 @@ __device__ __forceinline__ void reduce_split_tiles(const KernelArgs &args, int p
 #pragma unroll
                 for (int i = 0; i < QB; ++i)
                     if (q0 + i <= pl)
-                        sum = q0 + i == pf ? v[i] : sum + v[i];
+                        sum = q0 + i == pf ? v[i] : acc_add4<IACC>(sum, v[i]);
             }
             store_quad(sum, args, c_rsrc, m0, n0, (ww / WN) * WTM + mt * 32 + l32,
                        (ww % WN) * WTN + nt * 32, half, g);
@@ -592,11 +648,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(KernelArgs args)
         }
         compute_slab(s);
 
-        finish_tile<BM, BN, MT, NT>(acc, args, w, p, m0, n0, wave, lane,
-                                    wy * Cfg::WTM, wx * Cfg::WTN);
+        finish_tile<BM, BN, MT, NT, DT == 3>(acc, args, w, p, m0, n0, wave, lane,
+                                             wy * Cfg::WTM, wx * Cfg::WTN);
     }
     if (args.split_fixup)
-        reduce_split_tiles<BM, BN, WM, WN>(args, p, wave, lane);
+        reduce_split_tiles<BM, BN, WM, WN, DT == 3>(args, p, wave, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -1295,6 +1351,7 @@ static const Variant kVariants[] = {
     GSK_STAGED(2, 256, 256, 4, 2), GSK_STAGED(2, 256, 256, 2, 2), GSK_STAGED(2, 128, 128, 2, 2),
     GSK_STAGED(2, 64, 64, 2, 2),
     GSK_STAGED(0, 128, 128, 2, 2), GSK_STAGED(0, 64, 64, 2, 2),
+    GSK_STAGED(3, 256, 256, 4, 2), GSK_STAGED(3, 128, 128, 2, 2),
 };
 
 const Variant *variants(int *count)
@@ -1328,7 +1385,10 @@ int launch_pack(const void *src, void *dst, int64_t rows, int64_t cols, int64_t 
     int64_t blocks = (total + 255) / 256;
     if (blocks > 8192)
         blocks = 8192;
-    if (elem_size == 2)
+    if (elem_size == 1)
+        hipLaunchKernelGGL(pack_kernel<uint8_t>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                           (const uint8_t *)src, (uint8_t *)dst, rows, cols, ld_src, ld_dst);
+    else if (elem_size == 2)
         hipLaunchKernelGGL(pack_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, stream,
                            (const uint16_t *)src, (uint16_t *)dst, rows, cols, ld_src, ld_dst);
     else

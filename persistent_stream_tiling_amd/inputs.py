@@ -180,6 +180,12 @@ WORKLOADS = {
                                  seed=105),
 }
 
+# Beyond the workloads above: the int8 -> int32 path (the pages' kernel picks an
+# int32 accumulator for int8), at the 4096^3 shape; integers uniform in [-128, 127].
+EXTRA_WORKLOADS = {
+    "i8_4096": dict(M=4096, N=4096, K=4096, dtype="i8", dist="int8", scale=1.0, seed=106),
+}
+
 
 def irregular_workloads():
     """The 16 irregular bf16 shapes as workload dicts (value seeds 1050 + j)."""

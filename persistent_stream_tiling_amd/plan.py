@@ -11,7 +11,8 @@ def _torch_dtypes():
     global _TORCH_DTYPES
     if _TORCH_DTYPES is None:
         import torch
-        _TORCH_DTYPES = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}
+        _TORCH_DTYPES = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16",
+                         torch.int8: "i8"}
     return _TORCH_DTYPES
 
 
@@ -147,9 +148,9 @@ _PLANS = {}
 
 def matmul(a, b, schedule="hybrid", out_dtype=None, **tiles):
     """C = a @ b for contiguous CUDA tensors a (M x K) and b (K x N) of
-    float32, float16 or bfloat16, through the library's kernels.  C is fp32,
-    or a's dtype when ``out_dtype`` is a's dtype (fp32 sums rounded to nearest
-    even as they are stored)."""
+    float32, float16, bfloat16 or int8, through the library's kernels.  C is
+    fp32, or a's dtype when ``out_dtype`` is a's dtype (fp32 sums rounded to
+    nearest even as they are stored); int32 for int8 inputs."""
     import torch
     if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[0]:
         raise ValueError(f"incompatible shapes {tuple(a.shape)} and {tuple(b.shape)}")
@@ -157,7 +158,10 @@ def matmul(a, b, schedule="hybrid", out_dtype=None, **tiles):
         raise ValueError(f"unsupported dtypes {a.dtype}, {b.dtype}")
     if not (a.is_cuda and b.is_cuda):
         raise ValueError("a and b must be on the GPU")
-    if out_dtype not in (None, torch.float32, a.dtype):
+    if a.dtype == torch.int8:
+        if out_dtype not in (None, torch.int32):
+            raise ValueError("int8 products are int32")
+    elif out_dtype not in (None, torch.float32, a.dtype):
         raise ValueError(f"out_dtype must be float32 or {a.dtype}, got {out_dtype}")
     if out_dtype == a.dtype and a.dtype != torch.float32:
         tiles["flags"] = tiles.get("flags", 0) | FLAG_C_INPUT_DTYPE
@@ -172,6 +176,7 @@ def matmul(a, b, schedule="hybrid", out_dtype=None, **tiles):
         _PLANS[key] = entry
     plan, ws = entry
     c_half = tiles.get("flags", 0) & FLAG_C_INPUT_DTYPE
-    c = torch.empty((M, N), dtype=a.dtype if c_half else torch.float32, device=a.device)
+    c_type = torch.int32 if a.dtype == torch.int8 else (a.dtype if c_half else torch.float32)
+    c = torch.empty((M, N), dtype=c_type, device=a.device)
     plan.run(a, b, c, ws)
     return c

@@ -11,6 +11,7 @@ _DEFAULTS = {
     "f32": dict(bm=64, bn=64),
     "f16": dict(bm=256, bn=256),
     "bf16": dict(bm=256, bn=256),
+    "i8": dict(bm=256, bn=256),
 }
 
 # workload name -> schedule -> tiles; anything missing falls back to the dtype

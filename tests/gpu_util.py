@@ -2,13 +2,15 @@
 library run, and the element-wise comparison with the oracle."""
 import numpy as np
 
-TOL = {"f32": 1e-5, "f16": 4e-3, "bf16": 4e-3}
+TOL = {"f32": 1e-5, "f16": 4e-3, "bf16": 4e-3, "i8": 0.0}
 
 
 def to_device(bits, dtype):
     import torch
     if dtype == "f32":
         t = torch.from_numpy(np.ascontiguousarray(bits).view(np.float32))
+    elif dtype == "i8":
+        t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int8))
     else:
         t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
         t = t.view(torch.float16 if dtype == "f16" else torch.bfloat16)

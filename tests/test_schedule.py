@@ -337,3 +337,18 @@ def test_debug_drop_signal_needs_a_split_tile():
     for sched in ("dp", "persistent"):
         with pytest.raises(ValueError, match="splits some tile"):
             gsk.plan_for_device(256, 512, 65536, "bf16", sched, bm=128, bn=128, flags=drop)
+
+
+def test_int8_plans():
+    plan = gsk.plan_for_device(300, 200, 704, "i8", "hybrid")
+    assert plan.info["bk"] == 128 and plan.info["kernel_kind"] == 0
+    assert " C=i32 " in plan.describe()
+    # a sum of 2^17 products of -128 * -128 would leave int32
+    with pytest.raises(ValueError, match="overflow"):
+        gsk.plan_for_device(64, 64, 1 << 17, "i8", "dp")
+    assert gsk.plan_for_device(64, 64, (1 << 17) - 1, "i8", "dp").info["K"] == (1 << 17) - 1
+    with pytest.raises(ValueError, match="int32"):
+        gsk.plan_for_device(64, 64, 64, "i8", "dp", flags=gsk.FLAG_C_INPUT_DTYPE)
+    # rows of 701 int8 values are not 16-byte multiples: both operands repacked
+    p = gsk.plan_for_device(257, 203, 701, "i8", "dp")
+    assert p.info["pack_a"] == 1 and p.info["pack_b"] == 1
