@@ -18,12 +18,15 @@ def to_device(bits, dtype):
 
 
 def run_gemm(a, b, M, N, K, dtype, schedule, ws_cache=None, stream=None, **tiles):
-    """C (torch fp32 on the GPU) = a @ b through the C ABI for one plan."""
+    """C (torch fp32, or int32 for int8, on the GPU) = a @ b through the C ABI for one plan."""
     import torch
     import persistent_stream_tiling_amd as gsk
     plan = gsk.GemmPlan(M, N, K, dtype, schedule, **tiles)
     ws = plan.new_workspace()
-    c = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    if dtype == "i8":  # int32 C; a sentinel no int8 product of these sizes reaches
+        c = torch.full((M, N), -(2 ** 31), dtype=torch.int32, device="cuda")
+    else:
+        c = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
     plan.run(a, b, c, ws, stream=stream)
     torch.cuda.synchronize()
     return plan, ws, c

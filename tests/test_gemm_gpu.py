@@ -272,7 +272,7 @@ def full_case(name, n_samples, edges):
     every element of the last two rows and last two columns."""
     if name not in _FULL:
         _FULL.clear()
-        w = dict(inputs.WORKLOADS, **inputs.irregular_workloads())[name]
+        w = dict(inputs.WORKLOADS, **inputs.EXTRA_WORKLOADS, **inputs.irregular_workloads())[name]
         M, N, K, dt = w["M"], w["N"], w["K"], w["dtype"]
         a, b = inputs.operands(M, N, K, dt, w["dist"], w["seed"], w["scale"])
         checks = []
@@ -310,7 +310,7 @@ def check_workload(name, n_samples, edges):
 
 
 BIG = ["fp32_256", "fp16_4096", "fp16_1536x1536x8192", "bf16_512x512x65536",
-       "bf16_8192x28672x8192"]
+       "bf16_8192x28672x8192", "i8_4096"]
 
 
 @pytest.mark.parametrize("name", BIG)
