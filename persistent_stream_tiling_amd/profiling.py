@@ -277,7 +277,7 @@ def main():
                                       "resources --out " + a.out))
     elif a.cmd_name == "counters":
         from . import inputs
-        table = dict(inputs.WORKLOADS, **inputs.irregular_workloads())
+        table = dict(inputs.WORKLOADS, **inputs.EXTRA_WORKLOADS, **inputs.irregular_workloads())
         recs = []
         for d, w in zip(a.csv, a.workload):
             wl = table[w]
