@@ -195,6 +195,21 @@ def test_edge_shapes(shape, schedule):
         compare(c.cpu().numpy(), ref, scale, dtype, what=plan.describe())
 
 
+@pytest.mark.parametrize("schedule", ["streamk", "hybrid", "persistent"])
+def test_degenerate_grids(schedule):
+    # g = 1 (one workgroup walks everything), tiny g, g larger than the
+    # iteration count (q = 0: workgroups past r get nothing) and g = T
+    M, N, K = 257, 203, 701
+    a, b, ref, scale = small_inputs(M, N, K, "bf16")
+    da, db = to_device(a, "bf16"), to_device(b, "bf16")
+    for tiles in (dict(bm=64, bn=64), dict(bm=128, bn=128), dict(bm=256, bn=256)):
+        for g in (1, 2, 3, 250):
+            plan, ws, c = run_gemm(da, db, M, N, K, "bf16", schedule, grid=g, **tiles)
+            compare(c.cpu().numpy(), ref, scale, "bf16", what=plan.describe())
+            if ws is not None:
+                assert plan.workspace_status(ws) == 0
+
+
 @pytest.mark.parametrize("schedule", SCHEDULES)
 def test_empty_shapes(schedule):
     import persistent_stream_tiling_amd as gsk
