@@ -186,16 +186,18 @@ def schedule_table_row(args):
               f"{med['dp'] / med['streamk']:.2f} | {med['dp'] / med['hybrid']:.2f} |", flush=True)
 
 
-SWEEP_VARIANTS = (("streamk", 0), ("hybrid", 0), ("hybrid", "one_tile"))
+SWEEP_VARIANTS = (("streamk", 0), ("hybrid", 0), ("hybrid", "one_tile"), ("streamk", "two_kernel"))
 
 
 def sweep_grids(name, T):
     """Stream-K grid sizes tried per workload: one workgroup per CU (the
-    default), one per tile, 128, 64, and a seeded random even size."""
+    default), one per tile, 128, 64, a seeded random even size, and two per
+    CU (only the two-kernel fixup allows grids beyond one resident workgroup
+    per CU)."""
     import random
     rnd = random.Random(sum(map(ord, name)) + 20261202).randrange(2, 257, 2)
     out = []
-    for g in (256, T, 128, 64, rnd):
+    for g in (256, T, 128, 64, rnd, 512):
         if g not in out:
             out.append(g)
     return out
@@ -214,8 +216,10 @@ def grid_sweep(args, out):
              "line (512 MiB cache flush before each), tuned tiles per schedule.  g = 256 is one "
              "workgroup per CU; g = T is one per tile; with g = s*T and s dividing the "
              "iterations per tile, Stream-K is a fixed split-K with s pieces per tile.  Grids "
-             "above 256 are refused (the fixup needs every workgroup resident).  `one_tile` is "
-             "the hybrid without two_tiles (Stream-K over T mod g tiles only).", "",
+             "above 256 are refused by the in-kernel fixups (they need every workgroup "
+             "resident); `two_kernel` parks every piece and reduces the split tiles in a second "
+             "kernel, which allows them.  `one_tile` is the hybrid without two_tiles (Stream-K "
+             "over T mod g tiles only).", "",
              "| workload | tiles T | schedule | g | us | TFLOP/s | DP us | DP / this |",
              "|---|---|---|---|---|---|---|---|"]
     for name in names:
@@ -231,7 +235,7 @@ def grid_sweep(args, out):
 def grid_sweep_rows(args):
     import torch
     import persistent_stream_tiling_amd as gsk
-    from persistent_stream_tiling_amd import FLAG_ONE_TILE, inputs, tuning
+    from persistent_stream_tiling_amd import FLAG_FIXUP_TWO_KERNEL, FLAG_ONE_TILE, inputs, tuning
     wl = workload_table()[args.workload]
     M, N, K, dt = wl["M"], wl["N"], wl["K"], wl["dtype"]
     log(f"[sweep] {args.workload}: {M}x{N}x{K} {dt}")
@@ -253,8 +257,10 @@ def grid_sweep_rows(args):
         tiles = tuning.bench_tiles(args.workload, sched, dt)
         if variant == "one_tile":
             tiles["flags"] = tiles.get("flags", 0) | FLAG_ONE_TILE
+        if variant == "two_kernel":
+            tiles["flags"] = tiles.get("flags", 0) | FLAG_FIXUP_TWO_KERNEL
         T = gsk.GemmPlan(M, N, K, dt, sched, **tiles).info["tiles"]
-        label = sched + (" one_tile" if variant else "")
+        label = sched + (f" {variant}" if variant else "")
         for g in sweep_grids(args.workload, T):
             try:
                 plan = gsk.GemmPlan(M, N, K, dt, sched, grid=g, **tiles)

@@ -113,7 +113,15 @@ enum {
      * instead of about a second.  A run of such a plan ends normally with
      * workspace status 1 (see gemm_workspace_status) and an invalid C.
      * gemm_plan_create refuses it for a plan that splits no tile. */
-    GEMM_FLAG_DEBUG_DROP_SIGNAL = 1u << 7
+    GEMM_FLAG_DEBUG_DROP_SIGNAL = 1u << 7,
+    /* Two-kernel Stream-K fixup: every piece of a split tile is parked in the
+     * workspace without a flag, and a second kernel, launched by gemm_run on
+     * the same stream, reduces each split tile in ascending k order (the same
+     * additions, so the same bits, as the split fixup).  Nothing waits on
+     * another workgroup, so the Stream-K grid may exceed the number of
+     * workgroups that can be resident at once (e.g. two per CU, which issue
+     * #1393 also tries). */
+    GEMM_FLAG_FIXUP_TWO_KERNEL = 1u << 8
 };
 
 /* Tile and schedule knobs.  Every field 0 means "default". */
@@ -152,8 +160,9 @@ typedef struct gemm_plan gemm_plan;
  * Returns NULL on error (message in gemm_last_error()): negative sizes, a
  * matrix too large for 32-bit indexing, an unknown dtype or schedule, an
  * unsupported tile, or a Stream-K / hybrid grid larger than the number of
- * workgroups that can be resident at once (the fixup waits on other
- * workgroups, so all of them must be running together).
+ * workgroups that can be resident at once (the in-kernel fixups wait on other
+ * workgroups, so all of them must be running together; not with
+ * GEMM_FLAG_FIXUP_TWO_KERNEL).
  */
 gemm_plan *gemm_plan_create(int64_t M, int64_t N, int64_t K, gemm_dtype dtype,
                             gemm_schedule schedule, const gemm_tiles *tiles);

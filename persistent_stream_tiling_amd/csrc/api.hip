@@ -288,9 +288,12 @@ gemm_plan *create(int64_t M, int64_t N, int64_t K, gemm_dtype dtype, gemm_schedu
     if (T_sk > 0) {
         P.q = (int32_t)(p->iters_sk / g);
         P.r = (int32_t)(p->iters_sk % g);
-        if (g > p->wg_capacity) {
+        // the in-kernel fixups wait on other workgroups, which must all be
+        // running; the two-kernel fixup never waits
+        if (g > p->wg_capacity && !(t.flags & GEMM_FLAG_FIXUP_TWO_KERNEL)) {
             set_error("Stream-K grid %d exceeds the %d workgroups that can be resident at once; "
-                      "the fixup needs them all running together",
+                      "the in-kernel fixup needs them all running together "
+                      "(GEMM_FLAG_FIXUP_TWO_KERNEL has no such limit)",
                       g, p->wg_capacity);
             delete p;
             return nullptr;
@@ -304,13 +307,20 @@ gemm_plan *create(int64_t M, int64_t N, int64_t K, gemm_dtype dtype, gemm_schedu
             if (l - f + 1 > p->max_pieces)
                 p->max_pieces = l - f + 1;
         }
-        if (t.flags & GEMM_FLAG_FIXUP_SPLIT)
+        if (t.flags & GEMM_FLAG_FIXUP_TWO_KERNEL)
+            p->split_fixup = p->max_pieces >= 2 ? 2 : 0;
+        else if (t.flags & GEMM_FLAG_FIXUP_SPLIT)
             p->split_fixup = 1;
         else if (t.flags & GEMM_FLAG_FIXUP_HEAD)
             p->split_fixup = 0;
         else
             p->split_fixup = p->max_pieces >= 2;
         P.k_aligned = p->split_fixup;
+        if ((t.flags & GEMM_FLAG_DEBUG_DROP_SIGNAL) && p->split_fixup == 2) {
+            set_error("GEMM_FLAG_DEBUG_DROP_SIGNAL: the two-kernel fixup has no signals");
+            delete p;
+            return nullptr;
+        }
         if (t.flags & GEMM_FLAG_DEBUG_DROP_SIGNAL) {
             // the last workgroup whose work includes a parked piece
             for (int32_t wg = 0; wg < g; ++wg) {
@@ -492,7 +502,9 @@ int gemm_plan_describe(const gemm_plan *p, char *buf, size_t len)
                     p->P.tiles_n, p->P.T, p->P.ipt, p->P.T_sk, p->P.T - p->P.T_sk,
                     (long long)p->iters_sk, p->P.g, p->P.q, p->P.r, p->P.grid,
                     p->variant->threads, p->variant->lds_bytes, p->wg_capacity, p->xcds,
-                    p->P.T_sk == 0 ? "none" : (p->split_fixup ? "split" : "head"),
+                    p->P.T_sk == 0 ? "none"
+                                   : (p->split_fixup == 2 ? "two-kernel"
+                                                          : (p->split_fixup ? "split" : "head")),
                     p->max_pieces, p->pack_a, p->pack_b, p->ws_size);
 }
 
@@ -625,6 +637,11 @@ int gemm_run(const gemm_plan *p, const void *A, const void *B, void *C, void *wo
     args.P = p->P;
     if (p->variant->launch(args, p->P.grid, stream)) {
         set_error("kernel launch failed: %s", hipGetErrorString(hipGetLastError()));
+        return -3;
+    }
+    // two-kernel fixup: the split tiles are reduced after every piece is parked
+    if (p->split_fixup == 2 && p->variant->launch_fixup(args, p->P.T_sk, stream)) {
+        set_error("fixup launch failed: %s", hipGetErrorString(hipGetLastError()));
         return -3;
     }
     return 0;

@@ -22,7 +22,9 @@ struct KernelArgs {
     int32_t *status;       // workspace status word (1 = a fixup wait gave up)
     int32_t split_fixup;   // 0: the head's workgroup adds every partial;
                            // 1: every piece is parked and the tile's workgroups
-                           //    each reduce a share of its blocks
+                           //    each reduce a share of its blocks;
+                           // 2: every piece is parked, without flags, and a
+                           //    second kernel reduces the split tiles
     int32_t M, N, K;
     int32_t lda, ldb, ldc; // leading dimensions in elements
     int32_t c_vec;         // 1: C rows allow whole 4-element vector stores
@@ -42,6 +44,8 @@ struct Variant {
     int stages;            // LDS ring depth of kind 1 (0 for kind 0)
     int (*launch)(const KernelArgs &args, int grid, hipStream_t stream);
     const void *kernel;    // for occupancy queries
+    // the two-kernel fixup's reduction kernel for this variant's piece layout
+    int (*launch_fixup)(const KernelArgs &args, int grid, hipStream_t stream);
 };
 
 // All compiled variants; *count receives the number of entries.

@@ -355,7 +355,7 @@ __device__ __forceinline__ void finish_tile(f32x16 (&acc)[MT][NT], const KernelA
         // every lane's coherent stores have completed before the flag goes up
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (tid == 0 && p != args.drop_signal_wg)
+        if (tid == 0 && p != args.drop_signal_wg && args.split_fixup != 2)
             __hip_atomic_store(args.flags + slot_id, 1, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
         return;
@@ -411,6 +411,58 @@ __device__ __forceinline__ void finish_tile(f32x16 (&acc)[MT][NT], const KernelA
 // head's workgroup would use, so the result does not depend on who reduces.
 // The last workgroup to finish with a tile clears its flags and counter.
 // Blocks are numbered in the writer's fragment order (wave, mt, nt).
+// Reduce blocks [b0, b1) of split tile t (pieces of workgroups pf .. pl) and
+// store them to C.  Every element adds the pieces in ascending k order (head
+// piece first), the order the head's workgroup would use, so the result does
+// not depend on who reduces.  Blocks are numbered in the writer's fragment
+// order (wave, mt, nt); work units are quarter blocks (4 values per lane,
+// 1 KiB per piece) dealt to this workgroup's nwaves waves, and a unit's pieces
+// are loaded QB at a time, all in flight together, then added in order.
+template <int BM, int BN, int WM, int WN, bool IACC>
+__device__ __forceinline__ void reduce_tile_blocks(const KernelArgs &args, int32_t t, int32_t pf,
+                                                   int32_t pl, int32_t b0, int32_t b1, int wave,
+                                                   int nwaves, int lane)
+{
+    constexpr int WTM = BM / WM, WTN = BN / WN, MT = WTM / 32, NT = WTN / 32;
+    const int half = lane >> 5, l32 = lane & 31;
+    int tm, tn;
+    tile_coords(args.P, t, &tm, &tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const __amdgpu_buffer_rsrc_t c_rsrc = c_rows(args, m0);
+    const __amdgpu_buffer_rsrc_t slots = make_rsrc(args.partials);
+    const uint32_t slot_bytes = (uint32_t)(BM * BN * 4);
+    constexpr int QB = 16;
+    const int units = (b1 - b0) * 4;
+    for (int u = wave; u < units; u += nwaves) {
+        const int b = b0 + (u >> 2), g = u & 3;
+        const int ww = b / (MT * NT), mt = (b / NT) % MT, nt = b % NT;
+        const uint32_t frag_off = (uint32_t)(b * 4 * 64 + lane) * 16 + g * 1024;
+        f32x4 sum = f32x4{};
+        for (int32_t q0 = pf; q0 <= pl; q0 += QB) {
+            f32x4 v[QB];
+#pragma unroll
+            for (int i = 0; i < QB; ++i)
+                if (q0 + i <= pl)
+                    v[i] = __builtin_bit_cast(
+                        f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                   slots,
+                                   (int)((uint32_t)split_slot(q0 + i, q0 + i == pf) * slot_bytes +
+                                         frag_off),
+                                   0, kAgentCoherent));
+#pragma unroll
+            for (int i = 0; i < QB; ++i)
+                if (q0 + i <= pl)
+                    sum = q0 + i == pf ? v[i] : acc_add4<IACC>(sum, v[i]);
+        }
+        store_quad(sum, args, c_rsrc, m0, n0, (ww / WN) * WTM + mt * 32 + l32,
+                   (ww % WN) * WTN + nt * 32, half, g);
+    }
+}
+
+// Split fixup, after the workgroup's MAC work: for each split tile it took
+// part in, wait for all of the tile's pieces and reduce its share of the
+// tile's 32x32 blocks.  The last workgroup to finish with a tile clears its
+// flags and counter.
 template <int BM, int BN, int WM, int WN, bool IACC = false>
 __device__ __forceinline__ void reduce_split_tiles(const KernelArgs &args, int p, int wave,
                                                    int lane)
@@ -418,7 +470,7 @@ __device__ __forceinline__ void reduce_split_tiles(const KernelArgs &args, int p
     constexpr int WTM = BM / WM, WTN = BN / WN, MT = WTM / 32, NT = WTN / 32;
     constexpr int NW = WM * WN, NBLK = NW * MT * NT;
     const Partition &P = args.P;
-    const int tid = threadIdx.x, half = lane >> 5, l32 = lane & 31;
+    const int tid = threadIdx.x;
     int32_t tiles[2];
     const int ntiles = split_tiles_of(P, p, tiles);
     for (int it = 0; it < ntiles; ++it) {
@@ -431,41 +483,7 @@ __device__ __forceinline__ void reduce_split_tiles(const KernelArgs &args, int p
         if (wave == 0)
             wait_flags(args, pf, pl, [pf](int32_t q) { return split_slot(q, q == pf); }, false);
         __syncthreads();
-        int tm, tn;
-        tile_coords(P, t, &tm, &tn);
-        const int m0 = tm * BM, n0 = tn * BN;
-        const __amdgpu_buffer_rsrc_t c_rsrc = c_rows(args, m0);
-        const __amdgpu_buffer_rsrc_t slots = make_rsrc(args.partials);
-        const uint32_t slot_bytes = (uint32_t)(BM * BN * 4);
-        // Work units: quarter blocks (4 floats per lane, 1 KiB per piece),
-        // dealt to the waves.  A unit's pieces are loaded QB at a time, all in
-        // flight together, then added in ascending order.
-        constexpr int QB = 16;
-        const int units = (b1 - b0) * 4;
-        for (int u = wave; u < units; u += NW) {
-            const int b = b0 + (u >> 2), g = u & 3;
-            const int ww = b / (MT * NT), mt = (b / NT) % MT, nt = b % NT;
-            const uint32_t frag_off = (uint32_t)(b * 4 * 64 + lane) * 16 + g * 1024;
-            f32x4 sum = f32x4{};
-            for (int32_t q0 = pf; q0 <= pl; q0 += QB) {
-                f32x4 v[QB];
-#pragma unroll
-                for (int i = 0; i < QB; ++i)
-                    if (q0 + i <= pl)
-                        v[i] = __builtin_bit_cast(
-                            f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                       slots,
-                                       (int)((uint32_t)split_slot(q0 + i, q0 + i == pf) *
-                                                 slot_bytes + frag_off),
-                                       0, kAgentCoherent));
-#pragma unroll
-                for (int i = 0; i < QB; ++i)
-                    if (q0 + i <= pl)
-                        sum = q0 + i == pf ? v[i] : acc_add4<IACC>(sum, v[i]);
-            }
-            store_quad(sum, args, c_rsrc, m0, n0, (ww / WN) * WTM + mt * 32 + l32,
-                       (ww % WN) * WTN + nt * 32, half, g);
-        }
+        reduce_tile_blocks<BM, BN, WM, WN, IACC>(args, t, pf, pl, b0, b1, wave, NW, lane);
         // this workgroup's reads of the tile's slots are complete (their values
         // are already summed) before it counts itself done
         __syncthreads();
@@ -482,6 +500,33 @@ __device__ __forceinline__ void reduce_split_tiles(const KernelArgs &args, int p
             }
         }
     }
+}
+
+// Two-kernel fixup (no waits, so no co-residency needed): launched after the
+// GEMM kernel, one workgroup per Stream-K tile reduces all of a split tile's
+// parked pieces in ascending k order and stores it.
+template <int BM, int BN, int WM, int WN, bool IACC>
+__global__ __launch_bounds__(64 * WM * WN, 1) void fixup_kernel(KernelArgs args)
+{
+    constexpr int WTM = BM / WM, WTN = BN / WN, MT = WTM / 32, NT = WTN / 32;
+    constexpr int NW = WM * WN, NBLK = NW * MT * NT;
+    const int32_t t = (int32_t)blockIdx.x;
+    int32_t pf, pl;
+    tile_workers(args.P, t, &pf, &pl);
+    if (pf == pl)
+        return;  // a whole tile: its workgroup stored it
+    reduce_tile_blocks<BM, BN, WM, WN, IACC>(args, t, pf, pl, 0, NBLK, threadIdx.x >> 6, NW,
+                                             threadIdx.x & 63);
+}
+
+template <int BM, int BN, int WM, int WN, bool IACC>
+static int launch_fixup(const KernelArgs &args, int grid, hipStream_t stream)
+{
+    if (grid <= 0)
+        return 0;
+    hipLaunchKernelGGL((fixup_kernel<BM, BN, WM, WN, IACC>), dim3(grid), dim3(64 * WM * WN), 0,
+                       stream, args);
+    return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
 // ---------------------------------------------------------------------------
@@ -651,7 +696,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(KernelArgs args)
         finish_tile<BM, BN, MT, NT, DT == 3>(acc, args, w, p, m0, n0, wave, lane,
                                              wy * Cfg::WTM, wx * Cfg::WTN);
     }
-    if (args.split_fixup)
+    if (args.split_fixup == 1)
         reduce_split_tiles<BM, BN, WM, WN, DT == 3>(args, p, wave, lane);
 }
 
@@ -988,7 +1033,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel_dma(KernelArgs ar
         finish_tile<BM, BN, MT, NT>(acc, args, w, p, m0, n0, wave, lane, wy * Cfg::WTM,
                                     wx * Cfg::WTN);
     }
-    if (args.split_fixup)
+    if (args.split_fixup == 1)
         reduce_split_tiles<BM, BN, WM, WN>(args, p, wave, lane);
 }
 
@@ -1282,7 +1327,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel_pair(KernelArgs a
         finish_tile<BM, BN, MT, NT>(acc, args, w, p, m0, n0, wave, lane, wy * Cfg::WTM,
                                     wx * Cfg::WTN);
     }
-    if (args.split_fixup)
+    if (args.split_fixup == 1)
         reduce_split_tiles<BM, BN, WM, WN>(args, p, wave, lane);
 }
 
@@ -1314,20 +1359,23 @@ static int launch_gemm_pair(const KernelArgs &args, int grid, hipStream_t stream
 #define GSK_STAGED(DT, BM, BN, WM, WN)                                                           \
     Variant{DT, BM, BN, Tile<DT, BM, BN, WM, WN>::BK, WM, WN, Tile<DT, BM, BN, WM, WN>::NTH,     \
             (size_t)Tile<DT, BM, BN, WM, WN>::LDS, 0, 0, &launch_gemm<DT, BM, BN, WM, WN>,        \
-            (const void *)&gemm_kernel<DT, BM, BN, WM, WN>}
+            (const void *)&gemm_kernel<DT, BM, BN, WM, WN>,                                      \
+            &launch_fixup<BM, BN, WM, WN, DT == 3>}
 // Direct-to-LDS ring kernel (fp16/bf16)
 #define GSK_DMA(DT, BM, BN, WM, WN, S)                                                           \
     Variant{DT, BM, BN, 32, WM, WN, DmaTile<DT, BM, BN, WM, WN, S>::NTH,                         \
             (size_t)DmaTile<DT, BM, BN, WM, WN, S>::LDS, 1, S,                                   \
             &launch_gemm_dma<DT, BM, BN, WM, WN, S>,                                             \
-            (const void *)&gemm_kernel_dma<DT, BM, BN, WM, WN, S>}
+            (const void *)&gemm_kernel_dma<DT, BM, BN, WM, WN, S>,                               \
+            &launch_fixup<BM, BN, WM, WN, false>}
 
 // Direct-to-LDS ring kernel with whole-row A copies (fp16/bf16)
 #define GSK_PAIR(DT, BM, BN, WM, WN)                                                             \
     Variant{DT, BM, BN, 64, WM, WN, PairTile<DT, BM, BN, WM, WN>::NTH,                           \
             (size_t)PairTile<DT, BM, BN, WM, WN>::LDS, 2, PairTile<DT, BM, BN, WM, WN>::SB,       \
             &launch_gemm_pair<DT, BM, BN, WM, WN>,                                               \
-            (const void *)&gemm_kernel_pair<DT, BM, BN, WM, WN>}
+            (const void *)&gemm_kernel_pair<DT, BM, BN, WM, WN>,                                 \
+            &launch_fixup<BM, BN, WM, WN, false>}
 
 // The first entry matching a request wins, so each dtype's preferred kernel
 // for a tile comes first.

@@ -16,6 +16,9 @@
 // Threads start after seeded random delays and sleep at random between
 // steps, so the interleavings differ from seed to seed; the result must not.
 // A "drop" workgroup never raises its flag (forced failure of a signal).
+// split = 2 models the two-kernel fixup: every piece is parked without a
+// flag, and after all workgroups have finished (the kernel boundary) the
+// split tiles are reduced in ascending k order.
 //
 // Usage: fixup_emulator IN OUT.  IN holds 24 int32 (see Header) then A (M*K
 // fp32, row-major) and B (K*N fp32, row-major); OUT receives the status word
@@ -112,7 +115,7 @@ static void workgroup(Shared &S, int32_t p)
             const int32_t slot = h.split ? split_slot(p, w.role == ROLE_OWNER) : p;
             std::memcpy(&S.partials[(size_t)slot * tile_elems], acc.data(),
                         tile_elems * sizeof(float));
-            if (p != h.drop)
+            if (p != h.drop && h.split != 2)
                 S.flags[slot].store(1, std::memory_order_release);
             continue;
         }
@@ -125,7 +128,7 @@ static void workgroup(Shared &S, int32_t p)
         }
         store_c(S, acc.data(), m0, n0, 0, h.bm);
     }
-    if (!h.split)
+    if (h.split != 1)
         return;
     int32_t tiles[2];
     const int nt = split_tiles_of(P, p, tiles);
@@ -199,6 +202,24 @@ int main(int argc, char **argv)
         th.emplace_back(workgroup, std::ref(S), p);
     for (auto &t : th)
         t.join();
+    if (h.split == 2) {
+        // second kernel: every split tile, all rows, pieces in ascending k
+        const size_t tile_elems = (size_t)h.bm * h.bn;
+        std::vector<float> acc(tile_elems);
+        for (int32_t t = 0; t < P.T_sk; ++t) {
+            int32_t pf, pl, tm, tn;
+            tile_workers(P, t, &pf, &pl);
+            if (pf == pl)
+                continue;
+            for (int32_t q = pf; q <= pl; ++q) {
+                const float *piece = &S.partials[(size_t)split_slot(q, q == pf) * tile_elems];
+                for (size_t e = 0; e < tile_elems; ++e)
+                    acc[e] = q == pf ? piece[e] : acc[e] + piece[e];
+            }
+            tile_coords(P, t, &tm, &tn);
+            store_c(S, acc.data(), tm * h.bm, tn * h.bn, 0, h.bm);
+        }
+    }
     // a clean run leaves every flag and counter zero for the next one
     int32_t status = S.status.load();
     if (status == 0) {

@@ -4,8 +4,8 @@ tests/emulator/fixup_emulator.cpp runs one thread per workgroup over the
 library's own schedule code and the kernels' workspace protocol (park a
 piece, raise its flag; wait, add in ascending k; clear), with seeded random
 start delays and pauses.  Checked here, for plans the library makes:
-- no interleaving changes a bit of C, and the head and split fixups agree
-  bitwise (both add every element's pieces in ascending k order);
+- no interleaving changes a bit of C, and the head, split and two-kernel
+  fixups agree bitwise (all add every element's pieces in ascending k order);
 - C matches the oracle: exactly for integer-valued inputs, otherwise within
   the bound of fp32 summation, (K + pieces) * 2^-24 * sum_k |a||b|;
 - a clean run leaves every flag and counter zero;
@@ -84,7 +84,7 @@ def test_interleavings_and_fixup_modes_agree_bitwise(case, emulator, tmp_path):
     a, b = a_bits.view(np.float32), b_bits.view(np.float32)
     ref, scale = oracle.gemm(a_bits, b_bits, "f32")
     outs = []
-    for flag in (gsk.FLAG_FIXUP_HEAD, gsk.FLAG_FIXUP_SPLIT):
+    for flag in (gsk.FLAG_FIXUP_HEAD, gsk.FLAG_FIXUP_SPLIT, gsk.FLAG_FIXUP_TWO_KERNEL):
         plan = gsk.plan_for_device(M, N, K, "f32", sched, grid=g, flags=flag, **tiles)
         assert plan.info["max_pieces"] >= 2
         for seed in (1, 2, 3):

@@ -137,6 +137,40 @@ def test_split_and_head_fixups_agree_bitwise(tiles):
     compare(outs["split"][rows, cols], ref, scale, "bf16", what="split fixup")
 
 
+@pytest.mark.parametrize("tiles", [dict(bm=128, bn=128), dict(bm=256, bn=256),
+                                   dict(bm=256, bn=128, wave_m=4, wave_n=2), dict(bm=64, bn=64)],
+                         ids=lambda t: f"{t['bm']}x{t['bn']}")
+def test_two_kernel_fixup(tiles):
+    # same additions in the same order as the split fixup, so the same bits;
+    # and grids beyond one resident workgroup per CU, which only it allows
+    import persistent_stream_tiling_amd as gsk
+    M, N, K = 512, 384, 16384
+    a, b = inputs.operands(M, N, K, "bf16", "normal", seed=21)
+    da, db = to_device(a, "bf16"), to_device(b, "bf16")
+    rows, cols = inputs.sample_positions(M, N, 512, seed=1)
+    ref, scale = oracle.gemm_sampled(a, b, "bf16", rows, cols)
+    for g in (0, 37):
+        _, _, c_split = run_gemm(da, db, M, N, K, "bf16", "streamk", grid=g,
+                                 flags=gsk.FLAG_FIXUP_SPLIT, **tiles)
+        plan, ws, c_two = run_gemm(da, db, M, N, K, "bf16", "streamk", grid=g,
+                                   flags=gsk.FLAG_FIXUP_TWO_KERNEL, **tiles)
+        assert plan.info["split_fixup"] == 2
+        assert torch.equal(c_split.view(torch.int32), c_two.view(torch.int32)), plan.describe()
+        assert not ws[256:].cpu().numpy()[:4 * 2 * plan.info["g"]].any()  # no flag ever set
+    ai, bi = inputs.operands(M, N, K, "bf16", "int4", seed=22)
+    refi, _ = oracle.gemm_sampled(ai, bi, "bf16", rows, cols)
+    dai, dbi = to_device(ai, "bf16"), to_device(bi, "bf16")
+    for sched in ("streamk", "hybrid"):
+        for g in (512, 1024):
+            plan, ws, c = run_gemm(da, db, M, N, K, "bf16", sched, grid=g,
+                                   flags=gsk.FLAG_FIXUP_TWO_KERNEL, **tiles)
+            compare(c.cpu().numpy()[rows, cols], ref, scale, "bf16", what=plan.describe())
+            plan, ws, c = run_gemm(dai, dbi, M, N, K, "bf16", sched, grid=g,
+                                   flags=gsk.FLAG_FIXUP_TWO_KERNEL, **tiles)
+            compare(c.cpu().numpy()[rows, cols], refi, None, "bf16", exact=True,
+                    what=plan.describe())
+
+
 @pytest.mark.parametrize("fixup", ["head", "split"])
 def test_workspace_reuse_with_new_inputs(fixup):
     # partial slots are reused run after run; a stale copy of a slot in some

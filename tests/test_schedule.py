@@ -352,3 +352,19 @@ def test_int8_plans():
     # rows of 701 int8 values are not 16-byte multiples: both operands repacked
     p = gsk.plan_for_device(257, 203, 701, "i8", "dp")
     assert p.info["pack_a"] == 1 and p.info["pack_b"] == 1
+
+
+def test_two_kernel_fixup_plans():
+    two = gsk.FLAG_FIXUP_TWO_KERNEL
+    # 8 tiles of 128x128 over 512 workgroups: more than can be resident at once
+    with pytest.raises(ValueError, match="resident"):
+        gsk.plan_for_device(256, 512, 65536, "bf16", "streamk", grid=512, bm=128, bn=128)
+    plan = gsk.plan_for_device(256, 512, 65536, "bf16", "streamk", grid=512, bm=128, bn=128,
+                               flags=two)
+    assert plan.info["split_fixup"] == 2 and plan.info["g"] == 512
+    assert "fixup=two-kernel" in plan.describe()
+    # the coverage invariants hold for the grid beyond residency too
+    check_plan(plan)
+    with pytest.raises(ValueError, match="no signals"):
+        gsk.plan_for_device(256, 512, 65536, "bf16", "streamk", grid=512, bm=128, bn=128,
+                            flags=two | gsk.FLAG_DEBUG_DROP_SIGNAL)
