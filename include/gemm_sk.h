@@ -121,7 +121,14 @@ enum {
      * another workgroup, so the Stream-K grid may exceed the number of
      * workgroups that can be resident at once (e.g. two per CU, which issue
      * #1393 also tries). */
-    GEMM_FLAG_FIXUP_TWO_KERNEL = 1u << 8
+    GEMM_FLAG_FIXUP_TWO_KERNEL = 1u << 8,
+    /* fp16/bf16 ring kernel: the operand copies carry the non-temporal cache
+     * hint, so A and B lines are not kept for reuse.  Faster where each line
+     * is read by few workgroups at a time (few tiles and a long K, e.g.
+     * 512x512x65536 under Stream-K), slower where tiles share operand panels
+     * in L2.  Built for 256x256 (2x4 waves) and 256x128 (4x2) tiles; other
+     * tiles with this flag have no kernel. */
+    GEMM_FLAG_STREAM_COPIES = 1u << 9
 };
 
 /* Tile and schedule knobs.  Every field 0 means "default". */

@@ -16,6 +16,7 @@ FLAG_A_HALF_ROWS = 1 << 5
 FLAG_C_INPUT_DTYPE = 1 << 6
 FLAG_DEBUG_DROP_SIGNAL = 1 << 7
 FLAG_FIXUP_TWO_KERNEL = 1 << 8
+FLAG_STREAM_COPIES = 1 << 9
 ROLE_FULL, ROLE_CONTRIB, ROLE_OWNER = 0, 1, 2
 
 SCHEDULES = {"dp": DP, "persistent": PERSISTENT, "streamk": STREAMK, "hybrid": HYBRID}

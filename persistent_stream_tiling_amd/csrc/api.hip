@@ -117,6 +117,7 @@ const Variant *find_variant(int dtype, const gemm_tiles &t)
         for (int i = 0; i < n; ++i)
             if (v[i].dtype == dtype && v[i].bm == t.bm && v[i].bn == t.bn && v[i].kind == kind &&
                 !(kind == 2 && half_rows) &&
+                (v[i].stream_copies != 0) == ((t.flags & GEMM_FLAG_STREAM_COPIES) != 0) &&
                 (t.wave_m == 0 || v[i].wave_m == t.wave_m) &&
                 (t.wave_n == 0 || v[i].wave_n == t.wave_n) && (t.bk == 0 || v[i].bk == t.bk) &&
                 (t.stages == 0 || v[i].stages == t.stages))

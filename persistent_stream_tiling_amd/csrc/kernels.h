@@ -46,6 +46,7 @@ struct Variant {
     const void *kernel;    // for occupancy queries
     // the two-kernel fixup's reduction kernel for this variant's piece layout
     int (*launch_fixup)(const KernelArgs &args, int grid, hipStream_t stream);
+    int stream_copies;     // 1: operand copies carry the non-temporal hint
 };
 
 // All compiled variants; *count receives the number of entries.

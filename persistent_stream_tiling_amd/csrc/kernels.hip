@@ -777,14 +777,26 @@ __device__ __forceinline__ i32x4 rsrc_words(const void *base)
 // write: it would otherwise wait for every copy in flight before each
 // transposing LDS read, which defeats the ring.  The ring's own s_waitcnt
 // vmcnt() waits and barriers order these copies against the reads.
+// STREAM adds the non-temporal hint: the lines are not kept for reuse in the
+// caches, which pays where each operand line is read by few workgroups at once
+// (few tiles, long K) and costs where tiles share panels in L2.
+template <bool STREAM = false>
 __device__ __forceinline__ void copy16(i32x4 rsrc, uint32_t voff, uint32_t lds_addr)
 {
-    asm volatile("s_mov_b32 m0, %0\n\t"
-                 "s_nop 0\n\t"
-                 "buffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :
-                 : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(rsrc)
-                 : "m0");
+    if constexpr (STREAM)
+        asm volatile("s_mov_b32 m0, %0\n\t"
+                     "s_nop 0\n\t"
+                     "buffer_load_dwordx4 %1, %2, 0 offen nt lds"
+                     :
+                     : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(rsrc)
+                     : "m0");
+    else
+        asm volatile("s_mov_b32 m0, %0\n\t"
+                     "s_nop 0\n\t"
+                     "buffer_load_dwordx4 %1, %2, 0 offen lds"
+                     :
+                     : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(rsrc)
+                     : "m0");
 }
 
 __device__ __forceinline__ uint32_t lds_address(const uint8_t *p)
@@ -1087,7 +1099,7 @@ struct PairTile {
 
 __device__ __forceinline__ uint32_t swz_row128(int row) { return (uint32_t)(row ^ (row >> 3)) & 7; }
 
-template <int DT, int BM, int BN, int WM, int WN>
+template <int DT, int BM, int BN, int WM, int WN, bool STREAM = false>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel_pair(KernelArgs args)
 {
     using Cfg = PairTile<DT, BM, BN, WM, WN>;
@@ -1206,7 +1218,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel_pair(KernelArgs a
             const bool whole = ka + Cfg::BK <= k_hi;
             const int chunk = (lane & 7) ^ (int)swz_row128(a_copy_row(jj));
             const uint32_t off = whole || chunk * 8 < k_hi - ka ? a_off[jj] : kOutOfRange;
-            copy16(rsrc_words(a_cp), off, lds_wave + A_BASE + a_slot_off + jj * NW * 1024);
+            copy16<STREAM>(rsrc_words(a_cp), off, lds_wave + A_BASE + a_slot_off + jj * NW * 1024);
         };
         auto next_a = [&]() {
             if (ka + Cfg::BK < k_hi)
@@ -1216,7 +1228,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel_pair(KernelArgs a
         auto copy_b = [&](int s_fill, int j) {
             const bool whole = kbh + HK <= k_hi;
             const uint32_t off = whole || b_krow[j] < k_hi - kbh ? b_off[j] : kOutOfRange;
-            copy16(rsrc_words(b_cp), off, lds_wave + s_fill * B_STAGE + j * NW * 1024);
+            copy16<STREAM>(rsrc_words(b_cp), off, lds_wave + s_fill * B_STAGE + j * NW * 1024);
         };
         auto next_b = [&]() {
             if (kbh + HK < k_hi)
@@ -1245,7 +1257,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel_pair(KernelArgs a
                 // half-slab -1: nothing to read, a zero fill keeps the count
 #pragma unroll
                 for (int j = 0; j < B_INSTR; ++j)
-                    copy16(rsrc_words(b_cp), kOutOfRange,
+                    copy16<STREAM>(rsrc_words(b_cp), kOutOfRange,
                            lds_wave + (SB - 1) * B_STAGE + j * NW * 1024);
             } else {
 #pragma unroll
@@ -1347,10 +1359,10 @@ static int launch_gemm_dma(const KernelArgs &args, int grid, hipStream_t stream)
     return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
-template <int DT, int BM, int BN, int WM, int WN>
+template <int DT, int BM, int BN, int WM, int WN, bool STREAM>
 static int launch_gemm_pair(const KernelArgs &args, int grid, hipStream_t stream)
 {
-    hipLaunchKernelGGL((gemm_kernel_pair<DT, BM, BN, WM, WN>), dim3(grid),
+    hipLaunchKernelGGL((gemm_kernel_pair<DT, BM, BN, WM, WN, STREAM>), dim3(grid),
                        dim3(PairTile<DT, BM, BN, WM, WN>::NTH), 0, stream, args);
     return hipGetLastError() == hipSuccess ? 0 : -3;
 }
@@ -1360,22 +1372,26 @@ static int launch_gemm_pair(const KernelArgs &args, int grid, hipStream_t stream
     Variant{DT, BM, BN, Tile<DT, BM, BN, WM, WN>::BK, WM, WN, Tile<DT, BM, BN, WM, WN>::NTH,     \
             (size_t)Tile<DT, BM, BN, WM, WN>::LDS, 0, 0, &launch_gemm<DT, BM, BN, WM, WN>,        \
             (const void *)&gemm_kernel<DT, BM, BN, WM, WN>,                                      \
-            &launch_fixup<BM, BN, WM, WN, DT == 3>}
+            &launch_fixup<BM, BN, WM, WN, DT == 3>, 0}
 // Direct-to-LDS ring kernel (fp16/bf16)
 #define GSK_DMA(DT, BM, BN, WM, WN, S)                                                           \
     Variant{DT, BM, BN, 32, WM, WN, DmaTile<DT, BM, BN, WM, WN, S>::NTH,                         \
             (size_t)DmaTile<DT, BM, BN, WM, WN, S>::LDS, 1, S,                                   \
             &launch_gemm_dma<DT, BM, BN, WM, WN, S>,                                             \
             (const void *)&gemm_kernel_dma<DT, BM, BN, WM, WN, S>,                               \
-            &launch_fixup<BM, BN, WM, WN, false>}
+            &launch_fixup<BM, BN, WM, WN, false>, 0}
 
 // Direct-to-LDS ring kernel with whole-row A copies (fp16/bf16)
-#define GSK_PAIR(DT, BM, BN, WM, WN)                                                             \
+#define GSK_PAIR_X(DT, BM, BN, WM, WN, ST)                                                       \
     Variant{DT, BM, BN, 64, WM, WN, PairTile<DT, BM, BN, WM, WN>::NTH,                           \
             (size_t)PairTile<DT, BM, BN, WM, WN>::LDS, 2, PairTile<DT, BM, BN, WM, WN>::SB,       \
-            &launch_gemm_pair<DT, BM, BN, WM, WN>,                                               \
-            (const void *)&gemm_kernel_pair<DT, BM, BN, WM, WN>,                                 \
-            &launch_fixup<BM, BN, WM, WN, false>}
+            &launch_gemm_pair<DT, BM, BN, WM, WN, ST>,                                           \
+            (const void *)&gemm_kernel_pair<DT, BM, BN, WM, WN, ST>,                             \
+            &launch_fixup<BM, BN, WM, WN, false>, ST}
+#define GSK_PAIR(DT, BM, BN, WM, WN) GSK_PAIR_X(DT, BM, BN, WM, WN, false)
+// Non-temporal operand copies (GEMM_FLAG_STREAM_COPIES), for the layouts the
+// long-K Stream-K shapes use
+#define GSK_PAIR_STREAM(DT, BM, BN, WM, WN) GSK_PAIR_X(DT, BM, BN, WM, WN, true)
 
 // The first entry matching a request wins, so each dtype's preferred kernel
 // for a tile comes first.
@@ -1386,6 +1402,8 @@ static const Variant kVariants[] = {
     GSK_PAIR(2, 256, 256, 2, 4), GSK_PAIR(2, 256, 256, 4, 2), GSK_PAIR(2, 256, 256, 2, 2),
     GSK_PAIR(2, 256, 128, 4, 2), GSK_PAIR(2, 256, 128, 2, 2), GSK_PAIR(2, 128, 256, 2, 4),
     GSK_PAIR(2, 128, 256, 2, 2), GSK_PAIR(2, 128, 128, 2, 2),
+    GSK_PAIR_STREAM(1, 256, 256, 2, 4), GSK_PAIR_STREAM(1, 256, 128, 4, 2),
+    GSK_PAIR_STREAM(2, 256, 256, 2, 4), GSK_PAIR_STREAM(2, 256, 128, 4, 2),
     GSK_DMA(1, 256, 256, 4, 2, 4), GSK_DMA(1, 256, 256, 4, 2, 5), GSK_DMA(1, 256, 256, 2, 4, 4),
     GSK_DMA(1, 256, 256, 2, 2, 4), GSK_DMA(1, 256, 256, 2, 2, 5), GSK_DMA(1, 256, 128, 2, 2, 4),
     GSK_DMA(1, 256, 128, 4, 2, 4), GSK_DMA(1, 128, 256, 2, 2, 4), GSK_DMA(1, 128, 256, 2, 4, 4),

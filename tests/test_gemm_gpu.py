@@ -229,6 +229,24 @@ def test_edge_shapes(shape, schedule):
         compare(c.cpu().numpy(), ref, scale, dtype, what=plan.describe())
 
 
+@pytest.mark.parametrize("schedule", SCHEDULES)
+def test_stream_copies(schedule):
+    # the non-temporal copy hint changes no value: same bits as without it
+    import persistent_stream_tiling_amd as gsk
+    for dtype in ("f16", "bf16"):
+        M, N, K = 257, 203, 701
+        a, b, ref, scale = small_inputs(M, N, K, dtype)
+        da, db = to_device(a, dtype), to_device(b, dtype)
+        for tiles in (dict(bm=256, bn=128, wave_m=4, wave_n=2), dict(bm=256, bn=256, wave_m=2, wave_n=4)):
+            for g in ([0, 37] if schedule in ("streamk", "hybrid") else [0]):
+                _, _, c0 = run_gemm(da, db, M, N, K, dtype, schedule, grid=g, **tiles)
+                plan, _, c1 = run_gemm(da, db, M, N, K, dtype, schedule, grid=g,
+                                       flags=gsk.FLAG_STREAM_COPIES, **tiles)
+                assert plan.info["kernel_kind"] == 2
+                assert torch.equal(c0.view(torch.int32), c1.view(torch.int32)), plan.describe()
+                compare(c1.cpu().numpy(), ref, scale, dtype, what=plan.describe())
+
+
 @pytest.mark.parametrize("schedule", ["streamk", "hybrid", "persistent"])
 def test_degenerate_grids(schedule):
     # g = 1 (one workgroup walks everything), tiny g, g larger than the

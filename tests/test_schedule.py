@@ -368,3 +368,11 @@ def test_two_kernel_fixup_plans():
     with pytest.raises(ValueError, match="no signals"):
         gsk.plan_for_device(256, 512, 65536, "bf16", "streamk", grid=512, bm=128, bn=128,
                             flags=two | gsk.FLAG_DEBUG_DROP_SIGNAL)
+
+
+def test_stream_copies_only_where_built():
+    f = gsk.FLAG_STREAM_COPIES
+    assert gsk.plan_for_device(512, 512, 65536, "bf16", "streamk", bm=256, bn=128,
+                               flags=f).info["kernel_kind"] == 2
+    with pytest.raises(ValueError, match="no kernel"):
+        gsk.plan_for_device(512, 512, 4096, "bf16", "dp", bm=128, bn=128, flags=f)
