@@ -79,3 +79,18 @@ def test_int8_largest_k_does_not_overflow():
     for schedule in ("dp", "streamk"):
         plan, c = run(da, db, M, N, K, schedule, bm=128, bn=128)
         assert_exact(c, want.astype(np.float64), plan.describe())
+
+
+def test_int8_two_kernel_fixup_and_wide_grids():
+    # the second kernel adds int32 pieces as integers too; grids past residency
+    import persistent_stream_tiling_amd as gsk
+    M, N, K = 256, 384, 16384
+    a, b = inputs.operands(M, N, K, "i8", "int8", seed=73)
+    rows, cols = inputs.sample_positions(M, N, 2048, seed=74, tails=True)
+    ref, _ = oracle.gemm_sampled(a, b, "i8", rows, cols)
+    da, db = to_device(a, "i8"), to_device(b, "i8")
+    for g in (37, 256, 512, 1024):
+        plan, c = run(da, db, M, N, K, "streamk", grid=g, flags=gsk.FLAG_FIXUP_TWO_KERNEL,
+                      bm=128, bn=128)
+        assert plan.info["split_fixup"] == 2
+        assert_exact(c[rows, cols], ref, plan.describe())
