@@ -113,7 +113,8 @@ def cpu_baseline(a_bits, b_bits, M, N, K, dtype, seed, target_s):
     t = time.perf_counter()
     ref, scale = oracle.gemm_sampled(a_bits, b_bits, dtype, rows, cols, threads)
     secs = time.perf_counter() - t
-    return {"value": 2.0 * K * n / secs / 1e12, "unit": "TFLOP/s", "cores": threads,
+    return {"value": 2.0 * K * n / secs / 1e12, "unit": "TOP/s" if dtype == "i8" else "TFLOP/s",
+            "cores": threads,
             "kind": "oracle",
             "sample": f"{n} seeded output elements of the {M}x{N}x{K} {dtype} product, each a "
                       f"{K}-term fp64 dot product ({secs:.1f} s on {threads} threads)"}, \
@@ -515,7 +516,7 @@ def main():
                "tiles": tiles, "grid": plan.info["launch_grid"],
                "tiles_sk": plan.info["tiles_sk"], "wall_s": round(wall, 3)}
         results[sched] = (rec, plan, ws)
-        log(f"[bench] {sched}: {mean_ms:.4f} ms  {tflops:.1f} TFLOP/s  "
+        log(f"[bench] {sched}: {mean_ms:.4f} ms  {tflops:.1f} {'TOP/s' if dt == 'i8' else 'TFLOP/s'}  "
             f"({100 * rec['frac_mfma']:.1f}% of MFMA peak), {rec['hbm_gbs']:.0f} GB/s algorithmic")
 
     best = max(results, key=lambda s: results[s][0]["tflops"])
