@@ -5,8 +5,16 @@ A step is one C = A.B of the workload through the C ABI (every MAC, every
 Stream-K fixup, every store).  Each schedule is timed over --steps steps
 after --warmup untimed ones; before every step a 512 MiB fill evicts L2 and
 the Infinity Cache (outside the timed window), and HIP events on the launch
-stream bracket the GEMM alone.  The line's value is the best schedule's
-TFLOP/s; every schedule's figures are in "schedules".
+stream bracket the GEMM alone.
+
+The line's value is the best schedule's TFLOP/s on the 4096^3 fp16 product;
+"configs" holds the same measurement for every other workload (fp32 256^3,
+fp16 1536x1536x8192, bf16 512x512x65536, bf16 8192x28672x8192 and, unless
+--quick, the 16 seeded irregular bf16 shapes), each with an oracle check of
+what was timed: every element against the full CPU oracle where it finishes
+in seconds, seeded samples plus ragged edges otherwise.  The run exits
+non-zero if any check fails.  "cpu_baseline" is the full oracle on the
+4096^3 product, timed on the host's cores in the same run.
 
 Prints exactly one JSON line on stdout; progress goes to stderr.
 """
@@ -82,7 +90,7 @@ def time_schedule(plan, a, b, c, ws, steps, warmup, flush):
     import torch
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
-        plan.run(a, b, c, ws)
+        plan.run(a, b, c, ws, check=False)
     torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
@@ -90,7 +98,7 @@ def time_schedule(plan, a, b, c, ws, steps, warmup, flush):
     for i in range(steps):
         flush.zero_()
         starts[i].record(stream)
-        plan.run(a, b, c, ws)
+        plan.run(a, b, c, ws, check=False)
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -98,27 +106,96 @@ def time_schedule(plan, a, b, c, ws, steps, warmup, flush):
     return ms, wall
 
 
-def cpu_baseline(a_bits, b_bits, M, N, K, dtype, seed, target_s):
-    """The oracle, as it is, on a bounded sample of output elements."""
+def oracle_threads():
+    """Threads for the CPU oracle: the host's cores, capped by the CPU share
+    this process was given (its affinity mask and OMP_NUM_THREADS)."""
+    n = os.cpu_count() or 1
+    try:
+        n = min(n, len(os.sched_getaffinity(0)))
+    except AttributeError:
+        pass
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        n = min(n, int(omp))
+    return max(1, n)
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+# Products up to this many multiply-adds are checked element by element
+# against the full oracle (seconds of CPU time); larger ones on samples.
+FULL_ORACLE_MACS = 4096 ** 3
+TOL = {"f32": 1e-5, "f16": 4e-3, "bf16": 4e-3, "i8": 0.0}
+
+
+def oracle_reference(name, wl, a_bits, b_bits, threads):
+    """Oracle values to check the workload's GPU output against, and the
+    oracle's own timing.  Full products up to FULL_ORACLE_MACS: every
+    element.  Larger ones: 8192 seeded samples (timed, with the extrapolated
+    full-product time) plus, except on the 8192x28672x8192 shape, every
+    element of the last two rows and columns."""
     import oracle
     from persistent_stream_tiling_amd import inputs
-    threads = oracle.default_threads()
-    # calibrate on a small sample, then size the timed sample to ~target_s
-    rows, cols = inputs.sample_positions(M, N, threads * 256, seed=seed)
-    t = time.perf_counter()
-    oracle.gemm_sampled(a_bits, b_bits, dtype, rows, cols, threads)
-    per = (time.perf_counter() - t) / rows.size
-    n = int(min(M * N, max(threads * 8, target_s / max(per, 1e-9))))
-    rows, cols = inputs.sample_positions(M, N, n, seed=seed + 1)
-    t = time.perf_counter()
-    ref, scale = oracle.gemm_sampled(a_bits, b_bits, dtype, rows, cols, threads)
-    secs = time.perf_counter() - t
-    return {"value": 2.0 * K * n / secs / 1e12, "unit": "TOP/s" if dtype == "i8" else "TFLOP/s",
-            "cores": threads,
-            "kind": "oracle",
-            "sample": f"{n} seeded output elements of the {M}x{N}x{K} {dtype} product, each a "
-                      f"{K}-term fp64 dot product ({secs:.1f} s on {threads} threads)"}, \
-        (rows, cols, ref, scale)
+    M, N, K, dt = wl["M"], wl["N"], wl["K"], wl["dtype"]
+    checks = []
+    if M * N * K <= FULL_ORACLE_MACS:
+        t = time.perf_counter()
+        ref, scale = oracle.gemm(a_bits, b_bits, dt, nthreads=threads)
+        secs = time.perf_counter() - t
+        checks.append(("all", None, ref, scale))
+        timing = {"kind": "full", "elements": M * N, "seconds": round(secs, 3),
+                  "gflops": round(2.0 * M * N * K / secs / 1e9, 2), "threads": threads}
+    else:
+        rows, cols = inputs.sample_positions(M, N, 8192, seed=wl["seed"] + 1000)
+        t = time.perf_counter()
+        ref, scale = oracle.gemm_sampled(a_bits, b_bits, dt, rows, cols, threads)
+        secs = time.perf_counter() - t
+        checks.append(("samples", (rows, cols), ref, scale))
+        timing = {"kind": "sampled", "elements": int(rows.size), "seconds": round(secs, 3),
+                  "gflops": round(2.0 * rows.size * K / secs / 1e9, 2), "threads": threads,
+                  "extrapolated_full_seconds": round(secs * M * N / rows.size, 1)}
+        if name != "bf16_8192x28672x8192":
+            ref, scale = oracle.gemm(np.ascontiguousarray(a_bits[M - 2:]), b_bits, dt,
+                                     nthreads=threads)
+            checks.append(("last rows", (slice(M - 2, M), slice(None)), ref, scale))
+            ref, scale = oracle.gemm(a_bits, np.ascontiguousarray(b_bits[:, N - 2:]), dt,
+                                     nthreads=threads)
+            checks.append(("last cols", (slice(None), slice(N - 2, N)), ref, scale))
+    return checks, timing
+
+
+def check_output(c, checks, dt):
+    """max |C - C_ref| / S over every checked element, the element count, and
+    whether all are within the workload's tolerance (bit-exact for int8)."""
+    import torch
+    worst, count, ok = 0.0, 0, True
+    for _, idx, ref, scale in checks:
+        if idx is None:
+            got = c.cpu().numpy()
+        elif isinstance(idx[0], np.ndarray):
+            got = c[torch.from_numpy(idx[0]).cuda(), torch.from_numpy(idx[1]).cuda()].cpu().numpy()
+        else:
+            got = c[idx].cpu().numpy()
+        got = got.astype(np.float64)
+        err = np.abs(got - ref)
+        count += int(ref.size)
+        if dt == "i8":
+            ok &= bool((err == 0).all())
+        else:
+            rel = err / np.maximum(scale, 1e-300)
+            worst = max(worst, float(rel.max()) if rel.size else 0.0)
+            ok &= bool((err <= TOL[dt] * scale).all())
+    return worst, count, ok
 
 
 TABLE_ROUNDS = 4
@@ -328,7 +405,7 @@ def log_sampled(args, out):
             # sanity check on the first rows against an fp32 product (not a parity test:
             # parity is checked against the oracle by the test suite)
             err = max(err, float(((c[:64].float() - ref).abs() / sref.clamp_min(1e-30)).max()))
-            us[sched] = med(lambda: plan.run(a, b, c, ws))
+            us[sched] = med(lambda: plan.run(a, b, c, ws, check=False))
             if ws is not None and plan.workspace_status(ws) != 0:
                 raise RuntimeError(f"{(M, N, K)} {sched}: a fixup wait gave up")
         T = -(-M // 256) * -(-N // 256)  # 256x256 tiles, for the summary by size
@@ -405,11 +482,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="fp16_4096")
     ap.add_argument("--schedules", default=",".join(SCHEDULES))
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the CPU oracle (its timing and every output check)")
     ap.add_argument("--c-dtype", choices=("f32", "input"), default="f32",
                     help="C as fp32 (the workloads' output type, the default) or in the input "
                          "dtype (the pages' fp16 output; fp16/bf16 workloads only)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--configs", choices=("all", "standard", "none"), default="all",
+                    help="after the --workload line, also measure the other standard workloads "
+                         "(standard), plus the 16 irregular shapes (all, the default), or none")
     ap.add_argument("--report", default=None, help="also append per-schedule records here")
     ap.add_argument("--table", default=None, metavar="FILE",
                     help="no JSON line: time the four schedules on each of the workloads named by "
@@ -459,92 +539,43 @@ def main():
     if args.log_sampled:
         log_sampled(args, args.log_sampled_out)
         return
-    wl = workload_table()[args.workload]
-    M, N, K, dt = wl["M"], wl["N"], wl["K"], wl["dtype"]
-    log(f"[bench] {args.workload}: {M}x{N}x{K} {dt} {wl['dist']} seed {wl['seed']}")
-    a_bits, b_bits = inputs.operands(M, N, K, dt, wl["dist"], wl["seed"], wl["scale"])
-    a, b = to_device(a_bits, dt), to_device(b_bits, dt)
-    c_half = args.c_dtype == "input" and dt in ("f16", "bf16")
-    c_type = torch.int32 if dt == "i8" else (a.dtype if c_half else torch.float32)
-    c = torch.empty((M, N), dtype=c_type, device="cuda")
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-    flops = 2.0 * M * N * K
-    bound = "hbm" if args.workload == "bf16_512x512x65536" else "mfma"
-
-    def tiles_for(sched):
-        t = tuning.bench_tiles(args.workload, sched, dt)
-        if c_half:
-            t["flags"] = t.get("flags", 0) | gsk.FLAG_C_INPUT_DTYPE
-        return t
-
     if args.traffic_run:
-        from persistent_stream_tiling_amd.profiling import COPY_BYTES
-        src = torch.ones(COPY_BYTES, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        tiles = tiles_for(args.traffic_run)
-        plan = gsk.GemmPlan(M, N, K, dt, args.traffic_run, **tiles)
-        ws = plan.new_workspace()
-        for _ in range(3):
-            flush.zero_()
-            dst.copy_(src)
-        for _ in range(3):
-            flush.zero_()
-            plan.run(a, b, c, ws)
-        torch.cuda.synchronize()
-        alg = algorithmic_bytes(M, N, K, dt, plan.info) + 2 * partial_bytes(plan)
-        print(json.dumps({"traffic_run": args.workload, "schedule": args.traffic_run,
-                          "algorithmic_bytes": alg, "plan": plan.describe()}), flush=True)
+        traffic_run(args)
         return
 
-    results = {}
-    for sched in args.schedules.split(","):
-        tiles = tiles_for(sched)
-        plan = gsk.GemmPlan(M, N, K, dt, sched, **tiles)
-        ws = plan.new_workspace()
-        log(f"[bench] {sched}: {plan.describe()}")
-        ms, wall = time_schedule(plan, a, b, c, ws, args.steps, args.warmup, flush)
-        if ws is not None and plan.workspace_status(ws) != 0:
-            raise RuntimeError(f"{sched}: a Stream-K fixup wait gave up")
-        mean_ms = float(ms.mean())
-        tflops = flops / (mean_ms * 1e-3) / 1e12
-        bytes_alg = algorithmic_bytes(M, N, K, dt, plan.info) + 2 * partial_bytes(plan)
-        rec = {"tflops": round(tflops, 2), "ms": round(mean_ms, 5),
-               "ms_min": round(float(ms.min()), 5), "ms_median": round(float(np.median(ms)), 5),
-               "frac_mfma": round(tflops / PEAK_TFLOPS[dt], 4),
-               "hbm_gbs": round(bytes_alg / (mean_ms * 1e-3) / 1e9, 1),
-               "algorithmic_bytes": bytes_alg,
-               "tiles": tiles, "grid": plan.info["launch_grid"],
-               "tiles_sk": plan.info["tiles_sk"], "wall_s": round(wall, 3)}
-        results[sched] = (rec, plan, ws)
-        log(f"[bench] {sched}: {mean_ms:.4f} ms  {tflops:.1f} {'TOP/s' if dt == 'i8' else 'TFLOP/s'}  "
-            f"({100 * rec['frac_mfma']:.1f}% of MFMA peak), {rec['hbm_gbs']:.0f} GB/s algorithmic")
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    threads = oracle_threads()
+    failures = []
 
-    best = max(results, key=lambda s: results[s][0]["tflops"])
-    rec, plan, ws = results[best]
+    head = measure_workload(args.workload, args, flush, threads, failures,
+                            schedules=args.schedules.split(","), oracle=not args.no_cpu_baseline)
+    configs = {}
+    if args.configs != "none":
+        names = [n for n in CONFIG_WORKLOADS if n != args.workload]
+        if args.configs == "all":
+            names += sorted(inputs.irregular_workloads())
+        for name in names:
+            configs[name] = measure_workload(name, args, flush, threads, failures,
+                                             oracle=not args.no_cpu_baseline)
 
-    cpu = None
-    check = None
-    if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle on a sample ...")
-        cpu, (rows, cols, ref, scale) = cpu_baseline(a_bits, b_bits, M, N, K, dt, wl["seed"] + 7,
-                                                     args.cpu_seconds)
-        plan.run(a, b, c, ws)
-        torch.cuda.synchronize()
-        got = c[torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()].float().cpu().numpy()
-        rel = np.abs(got.astype(np.float64) - ref) / np.maximum(scale, 1e-300)
-        check = {"samples": int(rows.size), "max_err_over_S": float(rel.max()),
-                 "tolerance": {"f32": 1e-5, "i8": 0.0}.get(dt, 4e-3)}
-        log(f"[bench] oracle check on {rows.size} samples: max |C-C_ref|/S = {rel.max():.3e}")
-
-    if bound == "mfma":
-        roof = {"bound": "mfma", "achieved": rec["tflops"], "peak": PEAK_TFLOPS[dt],
-                "unit": "TOP/s" if dt == "i8" else "TFLOP/s",
-                "frac": round(rec["tflops"] / PEAK_TFLOPS[dt], 4)}
-    else:
-        roof = {"bound": "hbm", "achieved": rec["hbm_gbs"], "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(rec["hbm_gbs"] / PEAK_HBM_GBS, 4)}
+    dt = head["dtype"]
+    best = head["best"]
+    rec = head["schedules"][best]
+    roof = dict(head["roofline"])
     roof["traffic"] = load_traffic(args.workload, best)
-
+    cpu = None
+    if head.get("cpu_oracle"):
+        o = head["cpu_oracle"]
+        M, N, K = head["M"], head["N"], head["K"]
+        what = (f"every element of the {M}x{N}x{K} {dt} product" if o["kind"] == "full" else
+                f"{o['elements']} seeded elements of the {M}x{N}x{K} {dt} product")
+        cpu = {"value": round(2.0 * (M * N if o["kind"] == "full" else o["elements"]) * K
+                              / o["seconds"] / 1e12, 6),
+               "unit": "TOP/s" if dt == "i8" else "TFLOP/s", "cores": o["threads"],
+               "kind": "oracle",
+               "sample": f"{what}, each a {K}-term fp64 dot product in ascending k "
+                         f"({o['seconds']:.1f} s on {o['threads']} threads)",
+               "cpu_model": cpu_model(), "host_cpus": os.cpu_count()}
     line = {
         "metric": METRIC,
         "value": rec["tflops"],
@@ -558,20 +589,141 @@ def main():
         "vs_baseline": None,
         "dtype": dt,
         "data": "synthetic",
-        "config": {"workload": args.workload, "M": M, "N": N, "K": K,
-                   "distribution": wl["dist"], "c_dtype": dt if c_half else "f32",
-                   "schedule": best, "tiles": rec["tiles"],
-                   "grid": rec["grid"]},
-        "schedules": {s: r[0] for s, r in results.items()},
+        "config": {"workload": args.workload, "M": head["M"], "N": head["N"], "K": head["K"],
+                   "distribution": head["distribution"], "c_dtype": head["c_dtype"],
+                   "schedule": best, "tiles": rec["tiles"], "grid": rec["grid"]},
+        "schedules": head["schedules"],
         "roofline": roof,
         "cpu_baseline": cpu,
-        "oracle_check": check,
+        "oracle_check": head.get("oracle_check"),
+        "configs": {n: {k: v for k, v in r.items() if k not in ("dtype",)}
+                    for n, r in configs.items()},
+        "checks_failed": failures,
         "kernel_source": kernel_source_hash(),
     }
     if args.report:
         with open(args.report, "a") as f:
             f.write(json.dumps(line) + "\n")
     print(json.dumps(line), flush=True)
+    if failures:
+        log(f"[bench] FAILED oracle checks: {failures}")
+        sys.exit(3)
+
+
+# Workloads measured after the headline one (the 16 irregular shapes follow
+# unless --configs standard).
+CONFIG_WORKLOADS = ["fp16_4096", "fp32_256", "fp16_1536x1536x8192", "bf16_512x512x65536",
+                    "bf16_8192x28672x8192"]
+HBM_BOUND = {"bf16_512x512x65536"}
+
+
+def measure_workload(name, args, flush, threads, failures, schedules=SCHEDULES, oracle=True):
+    """Time every schedule of one workload in its tuned launch configuration,
+    check each schedule's output against the oracle, and return the record."""
+    import torch
+    import persistent_stream_tiling_amd as gsk
+    from persistent_stream_tiling_amd import inputs, tuning
+    wl = workload_table()[name]
+    M, N, K, dt = wl["M"], wl["N"], wl["K"], wl["dtype"]
+    log(f"[bench] {name}: {M}x{N}x{K} {dt} {wl['dist']} seed {wl['seed']}")
+    a_bits, b_bits = inputs.operands(M, N, K, dt, wl["dist"], wl["seed"], wl["scale"])
+    a, b = to_device(a_bits, dt), to_device(b_bits, dt)
+    c_half = args.c_dtype == "input" and dt in ("f16", "bf16")
+    c_type = torch.int32 if dt == "i8" else (a.dtype if c_half else torch.float32)
+    c = torch.empty((M, N), dtype=c_type, device="cuda")
+    flops = 2.0 * M * N * K
+    unit = "TOP/s" if dt == "i8" else "TFLOP/s"
+    checks, timing = (None, None)
+    if oracle:
+        checks, timing = oracle_reference(name, wl, a_bits, b_bits, threads)
+        log(f"[bench] {name}: oracle ({timing['kind']}, {timing['elements']} elements) "
+            f"{timing['seconds']:.2f} s on {threads} threads")
+    del a_bits, b_bits
+    results = {}
+    worst_all, checked = 0.0, 0
+    for sched in schedules:
+        tiles = tuning.bench_tiles(name, sched, dt)
+        if c_half:
+            tiles["flags"] = tiles.get("flags", 0) | gsk.FLAG_C_INPUT_DTYPE
+        plan = gsk.GemmPlan(M, N, K, dt, sched, **tiles)
+        ws = plan.new_workspace()
+        log(f"[bench] {sched}: {plan.describe()}")
+        ms, wall = time_schedule(plan, a, b, c, ws, args.steps, args.warmup, flush)
+        if ws is not None and plan.workspace_status(ws) != 0:
+            failures.append(f"{name}/{sched}: a Stream-K fixup wait gave up")
+        mean_ms = float(ms.mean())
+        tflops = flops / (mean_ms * 1e-3) / 1e12
+        compulsory = algorithmic_bytes(M, N, K, dt, plan.info)
+        parked = 2 * partial_bytes(plan)
+        rec = {"tflops": round(tflops, 2), "ms": round(mean_ms, 5),
+               "ms_min": round(float(ms.min()), 5), "ms_median": round(float(np.median(ms)), 5),
+               "frac_mfma": round(tflops / PEAK_TFLOPS[dt], 4),
+               "hbm_gbs": round(compulsory / (mean_ms * 1e-3) / 1e9, 1),
+               "compulsory_bytes": compulsory, "parked_bytes": parked,
+               "tiles": tiles, "grid": plan.info["launch_grid"],
+               "tiles_sk": plan.info["tiles_sk"], "wall_s": round(wall, 3)}
+        if checks is not None:
+            worst, count, ok = check_output(c, checks, dt)
+            rec["oracle_max_err_over_S"] = worst
+            worst_all, checked = max(worst_all, worst), count
+            if not ok:
+                failures.append(f"{name}/{sched}: outside the tolerance against the oracle")
+        results[sched] = rec
+        log(f"[bench] {sched}: {mean_ms:.4f} ms  {tflops:.1f} {unit}  "
+            f"({100 * rec['frac_mfma']:.1f}% of MFMA peak), {rec['hbm_gbs']:.0f} GB/s compulsory")
+        del plan, ws
+    best = max(results, key=lambda s_: results[s_]["tflops"])
+    r = results[best]
+    if name in HBM_BOUND:
+        roof = {"bound": "hbm", "achieved": r["hbm_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(r["hbm_gbs"] / PEAK_HBM_GBS, 4),
+                "with_parked_gbs": round((r["compulsory_bytes"] + r["parked_bytes"])
+                                         / (r["ms"] * 1e-3) / 1e9, 1)}
+    else:
+        roof = {"bound": "mfma", "achieved": r["tflops"], "peak": PEAK_TFLOPS[dt], "unit": unit,
+                "frac": round(r["tflops"] / PEAK_TFLOPS[dt], 4)}
+    out = {"M": M, "N": N, "K": K, "dtype": dt, "distribution": wl["dist"],
+           "c_dtype": dt if c_half else ("i32" if dt == "i8" else "f32"), "best": best,
+           "schedules": results, "roofline": roof}
+    if checks is not None:
+        out["oracle_check"] = {"elements": checked, "kind": timing["kind"],
+                               "max_err_over_S": worst_all, "tolerance": TOL[dt],
+                               "schedules_checked": len(results)}
+        out["cpu_oracle"] = timing
+    del a, b, c
+    torch.cuda.empty_cache()
+    return out
+
+
+def traffic_run(args):
+    """No timing: a 256 MiB device copy, then one schedule's GEMM, three times
+    each (for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)."""
+    import torch
+    import persistent_stream_tiling_amd as gsk
+    from persistent_stream_tiling_amd import inputs, tuning
+    from persistent_stream_tiling_amd.profiling import COPY_BYTES
+    wl = workload_table()[args.workload]
+    M, N, K, dt = wl["M"], wl["N"], wl["K"], wl["dtype"]
+    a_bits, b_bits = inputs.operands(M, N, K, dt, wl["dist"], wl["seed"], wl["scale"])
+    a, b = to_device(a_bits, dt), to_device(b_bits, dt)
+    c_type = torch.int32 if dt == "i8" else torch.float32
+    c = torch.empty((M, N), dtype=c_type, device="cuda")
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    src = torch.ones(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    plan = gsk.GemmPlan(M, N, K, dt, args.traffic_run,
+                        **tuning.bench_tiles(args.workload, args.traffic_run, dt))
+    ws = plan.new_workspace()
+    for _ in range(3):
+        flush.zero_()
+        dst.copy_(src)
+    for _ in range(3):
+        flush.zero_()
+        plan.run(a, b, c, ws, check=False)
+    torch.cuda.synchronize()
+    alg = algorithmic_bytes(M, N, K, dt, plan.info) + 2 * partial_bytes(plan)
+    print(json.dumps({"traffic_run": args.workload, "schedule": args.traffic_run,
+                      "algorithmic_bytes": alg, "plan": plan.describe()}), flush=True)
 
 
 if __name__ == "__main__":

@@ -78,9 +78,8 @@ enum {
     /* Do not remap workgroup ids so that each XCD gets a contiguous run of
      * tiles (for measuring what the remap buys). */
     GEMM_FLAG_NO_XCD_REMAP = 1u << 1,
-    /* fp16/bf16: use the kernel that stages A and B through registers (bk 64)
-     * instead of the direct-to-LDS ring kernel (bk 32). */
-    GEMM_FLAG_REGISTER_STAGED = 1u << 2,
+    /* Bits 2 and 5 are reserved (they selected kernel families that are no
+     * longer built); gemm_plan_create refuses a plan that sets them. */
     /* Stream-K fixup mode (default: split whenever some tile is cut):
      *  HEAD  the workgroup holding a split tile's k = 0 adds the other pieces
      *        one by one and stores the tile;
@@ -93,11 +92,6 @@ enum {
      * identical bits. */
     GEMM_FLAG_FIXUP_HEAD = 1u << 3,
     GEMM_FLAG_FIXUP_SPLIT = 1u << 4,
-    /* fp16/bf16: use the ring kernel with 32-deep MAC iterations, which
-     * copies A in 64-byte row halves (kernel_kind 1), instead of the default
-     * one with 64-deep iterations and whole 128-byte A rows (kernel_kind 2).
-     * Kept for comparison: half-line A copies fetch every A line twice. */
-    GEMM_FLAG_A_HALF_ROWS = 1u << 5,
     /* C is written in the input dtype instead of fp32: each fp32 sum is
      * rounded to the nearest fp16 / bf16 value (ties to even) as it is
      * stored.  This is the pages' output type: issue #1393's final revision
@@ -136,9 +130,7 @@ typedef struct {
     int32_t bm, bn;   /* output tile (multiples of 32 from the supported set;
                          default per dtype and shape) */
     int32_t bk;       /* k-depth of one MAC iteration, fixed per kernel: 64
-                         for the fp16/bf16 ring kernels (32 with
-                         GEMM_FLAG_A_HALF_ROWS) and the register-staged one,
-                         32 for fp32, 128 for int8; 0 = any */
+                         for fp16/bf16, 32 for fp32, 128 for int8; 0 = any */
     int32_t grid;     /* g: workgroups of the persistent / Stream-K launch;
                          0 = number of CUs (issue #1393 uses the SM count) */
     int32_t group_m;  /* tile-order group height (issue #1393 GROUP_M);
@@ -147,7 +139,7 @@ typedef struct {
     int32_t wave_m, wave_n; /* waves per workgroup along M and N (each wave
                                computes a (bm/wave_m) x (bn/wave_n) block);
                                0 = the default layout for the tile */
-    int32_t stages;   /* LDS ring depth of the fp16/bf16 ring kernel; 0 = default */
+    int32_t stages;   /* B stages of the fp16/bf16 ring kernel (4); 0 = default */
 } gemm_tiles;
 
 /* Device description for planning without touching a GPU (host tests). */
@@ -162,14 +154,23 @@ typedef struct gemm_plan gemm_plan;
 
 /*
  * Create a plan for C = A.B with the given shape, input dtype and schedule.
+ * This is the host half of the final revision's wrapper (`matmul._call`) on
+ * the Triton issue #1393 page: from M, N, K and the block shape it derives
+ * the tile grid (tiles_m, tiles_n, T), the MAC iterations per tile
+ * (ipt = ceil(K / bk)), the number of Stream-K tiles (the hybrid's T_sk) and
+ * the per-workgroup share q, r of their iterations; here the result is kept
+ * in an immutable plan instead of being recomputed on every call.
+ *
  * tiles may be NULL (all defaults).  The device is the current HIP device.
  * M, N, K >= 0 (M or N = 0: nothing to do; K = 0: C is zero-filled).
- * Returns NULL on error (message in gemm_last_error()): negative sizes, a
- * matrix too large for 32-bit indexing, an unknown dtype or schedule, an
- * unsupported tile, or a Stream-K / hybrid grid larger than the number of
- * workgroups that can be resident at once (the in-kernel fixups wait on other
- * workgroups, so all of them must be running together; not with
- * GEMM_FLAG_FIXUP_TWO_KERNEL).
+ * Returns NULL on error (message in gemm_last_error()): negative sizes; a
+ * matrix too large for the kernels' 32-bit offsets (M, N, K < 2^30, and one
+ * tile's rows of A, C and one iteration's rows of B below 2^30 bytes, e.g.
+ * N < 2^20 for 256-row tiles with fp32 C); an unknown dtype or schedule; a
+ * reserved flag; an unsupported tile; or a Stream-K / hybrid grid larger than
+ * the number of workgroups that can be resident at once (the in-kernel fixups
+ * wait on other workgroups, so all of them must be running together; not
+ * with GEMM_FLAG_FIXUP_TWO_KERNEL).
  */
 gemm_plan *gemm_plan_create(int64_t M, int64_t N, int64_t K, gemm_dtype dtype,
                             gemm_schedule schedule, const gemm_tiles *tiles);
@@ -183,15 +184,36 @@ gemm_plan *gemm_plan_create_for_device(int64_t M, int64_t N, int64_t K, gemm_dty
 
 /*
  * Enqueue C = A.B on stream (a hipStream_t; NULL = the default stream).
+ * This is the launch half of the same wrapper on the Triton issue #1393 page
+ * (its first-wave Stream-K kernel, then its data-parallel kernel over the
+ * remaining tiles); here one persistent launch runs both phases, plus a short
+ * second launch for GEMM_FLAG_FIXUP_TWO_KERNEL plans and, for rows that are
+ * not a multiple of 16 bytes, a repack of A and/or B into the workspace
+ * before it.
+ *
  * Asynchronous: never allocates, never synchronizes.  workspace is a device
- * buffer of at least gemm_plan_workspace_size(plan) bytes, zero-filled once
- * when allocated; it may be NULL when that size is 0.  A run leaves the
- * workspace's flags zero again, so it can be reused by later runs without
- * clearing.  Two runs that overlap in time must not share a workspace.
- * C points to M x N fp32 values, to fp16/bf16 values when the plan was made
- * with GEMM_FLAG_C_INPUT_DTYPE, or to int32 values for int8 inputs.
- * Returns 0, or -1 invalid argument (NULL or misaligned pointer), -2 workspace
- * missing, -3 HIP launch error, -5 plan made for another device.
+ * buffer of at least gemm_plan_workspace_size(plan) bytes, 256-byte aligned,
+ * zero-filled once when allocated; it may be NULL when that size is 0.  A run
+ * leaves the workspace's flags zero again, so it can be reused by later runs
+ * without clearing.  Two runs that overlap in time must not share a
+ * workspace.  C points to M x N fp32 values, to fp16/bf16 values when the
+ * plan was made with GEMM_FLAG_C_INPUT_DTYPE, or to int32 values for int8
+ * inputs.  The caller owns A, B, C and the workspace.
+ *
+ * Co-residency.  Under Stream-K and hybrid plans that split a tile (and not
+ * GEMM_FLAG_FIXUP_TWO_KERNEL), workgroups wait for pieces parked by other
+ * workgroups of the same launch, which needs all g workgroups resident at
+ * once.  The planner caps g at the device's resident capacity for this
+ * kernel, but kernels running concurrently on other streams can hold CUs and
+ * break that assumption.  The waits are bounded (about a second), so the
+ * kernel always ends; a wait that gives up sets the workspace status word,
+ * which gemm_workspace_status reads.  gemm_run cannot return that outcome
+ * (it returns before the kernel runs): a caller that cannot rule out such a
+ * wait must read the status after the run and treat a nonzero status as a
+ * failed product (the Python binding does this by default).
+ *
+ * Returns 0, or -1 invalid argument (NULL or misaligned pointer), -2
+ * workspace missing, -3 HIP launch error, -5 plan made for another device.
  */
 int gemm_run(const gemm_plan *plan, const void *A, const void *B, void *C, void *workspace,
              void *stream);
@@ -202,8 +224,11 @@ void gemm_plan_destroy(gemm_plan *plan);
 /* Bytes of workspace gemm_run needs (0 when none). */
 size_t gemm_plan_workspace_size(const gemm_plan *plan);
 
-/* Human-readable plan summary (tile grid, partition, launch) into buf;
- * returns the length it needed (like snprintf), or -1 on a NULL plan. */
+/* Human-readable plan summary (tile grid, partition, launch) into buf; the
+ * analogue of the debug print in the Triton issue #1393 final revision's
+ * wrapper (M, N, K, block shape, tile counts, iterations per tile, Stream-K
+ * tiles and the per-workgroup split).  Returns the length it needed (like
+ * snprintf), or -1 on a NULL plan. */
 int gemm_plan_describe(const gemm_plan *plan, char *buf, size_t len);
 
 /* Message of the last failed call on this host thread ("" if none). */
@@ -217,8 +242,7 @@ typedef struct {
     int32_t bm, bn, bk, group_m;
     uint32_t flags;
     int32_t wave_m, wave_n;
-    int32_t kernel_kind;  /* 0 register-staged, 1 direct-to-LDS ring (A in row
-                             halves), 2 direct-to-LDS ring (A in whole rows) */
+    int32_t kernel_kind;  /* 0 register-staged, 2 direct-to-LDS ring */
     int32_t stages;
     int32_t split_fixup;  /* 1 when the Stream-K fixup is split (see flags) */
     int32_t max_pieces;   /* most workgroups sharing one Stream-K tile */
@@ -265,6 +289,28 @@ int32_t gemm_plan_logical_wg(const gemm_plan *plan, int32_t hw);
  * workspace must be zero-filled again).  Returns 0 or a negative error. */
 int gemm_workspace_status(const gemm_plan *plan, const void *workspace, void *stream,
                           int32_t *status);
+
+/* One compiled kernel.  gemm_plan_create takes the first entry of the table
+ * whose dtype, tile, bk, wave layout and stages match what the caller asked
+ * for (0 = any) and whose copy hint matches GEMM_FLAG_STREAM_COPIES, so a plan
+ * made with these fields runs exactly this kernel. */
+typedef struct {
+    int32_t dtype;          /* gemm_dtype */
+    int32_t bm, bn, bk;
+    int32_t wave_m, wave_n; /* wave grid of the workgroup */
+    int32_t kind;           /* kernel_kind, as in gemm_plan_info */
+    int32_t stages;
+    int32_t stream_copies;  /* 1: needs GEMM_FLAG_STREAM_COPIES */
+    int32_t threads;
+    size_t lds_bytes;
+} gemm_variant_info;
+
+/* Number of compiled kernels. */
+int32_t gemm_variant_count(void);
+
+/* Kernel i (0 <= i < gemm_variant_count()) into *out; 0, or -1 on a bad
+ * index or NULL out. */
+int gemm_variant_get(int32_t i, gemm_variant_info *out);
 
 #ifdef __cplusplus
 }

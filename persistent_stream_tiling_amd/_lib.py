@@ -9,10 +9,8 @@ F32, F16, BF16, I8 = 0, 1, 2, 3
 DP, PERSISTENT, STREAMK, HYBRID = 0, 1, 2, 3
 FLAG_ONE_TILE = 1 << 0
 FLAG_NO_XCD_REMAP = 1 << 1
-FLAG_REGISTER_STAGED = 1 << 2
 FLAG_FIXUP_HEAD = 1 << 3
 FLAG_FIXUP_SPLIT = 1 << 4
-FLAG_A_HALF_ROWS = 1 << 5
 FLAG_C_INPUT_DTYPE = 1 << 6
 FLAG_DEBUG_DROP_SIGNAL = 1 << 7
 FLAG_FIXUP_TWO_KERNEL = 1 << 8
@@ -56,6 +54,17 @@ class PlanInfo(ctypes.Structure):
         return {name: getattr(self, name) for name, _ in self._fields_}
 
 
+class VariantInfo(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("bm", ctypes.c_int32), ("bn", ctypes.c_int32),
+                ("bk", ctypes.c_int32), ("wave_m", ctypes.c_int32), ("wave_n", ctypes.c_int32),
+                ("kind", ctypes.c_int32), ("stages", ctypes.c_int32),
+                ("stream_copies", ctypes.c_int32), ("threads", ctypes.c_int32),
+                ("lds_bytes", ctypes.c_size_t)]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
 class Segment(ctypes.Structure):
     _fields_ = [("tile", ctypes.c_int32), ("k_begin", ctypes.c_int32), ("k_end", ctypes.c_int32),
                 ("role", ctypes.c_int32), ("peer_last", ctypes.c_int32)]
@@ -64,7 +73,8 @@ class Segment(ctypes.Structure):
 EXPORTS = ("gemm_plan_create", "gemm_plan_create_for_device", "gemm_run", "gemm_plan_destroy",
            "gemm_plan_workspace_size", "gemm_plan_describe", "gemm_last_error",
            "gemm_plan_get_info", "gemm_plan_segments", "gemm_plan_tile_coords",
-           "gemm_plan_logical_wg", "gemm_workspace_status")
+           "gemm_plan_logical_wg", "gemm_workspace_status", "gemm_variant_count",
+           "gemm_variant_get")
 
 _lib = None
 
@@ -106,8 +116,24 @@ def load(path=None):
     lib.gemm_plan_logical_wg.restype = i32
     lib.gemm_workspace_status.argtypes = [vp, vp, vp, ctypes.POINTER(i32)]
     lib.gemm_workspace_status.restype = ctypes.c_int
+    lib.gemm_variant_count.argtypes = []
+    lib.gemm_variant_count.restype = i32
+    lib.gemm_variant_get.argtypes = [i32, ctypes.POINTER(VariantInfo)]
+    lib.gemm_variant_get.restype = ctypes.c_int
     _lib = lib
     return lib
+
+
+def variants():
+    """The compiled kernel table, as dicts (see gemm_variant_info)."""
+    lib = load()
+    out = []
+    for i in range(lib.gemm_variant_count()):
+        v = VariantInfo()
+        if lib.gemm_variant_get(i, ctypes.byref(v)) != 0:
+            raise RuntimeError(last_error())
+        out.append(v.as_dict())
+    return out
 
 
 def last_error():

@@ -104,19 +104,15 @@ void default_tile(int64_t M, int64_t N, int64_t K, gemm_schedule schedule, int c
 // each dtype's preferred kernel for a tile first.
 const Variant *find_variant(int dtype, const gemm_tiles &t)
 {
-    // fp16/bf16 prefer the direct-to-LDS ring kernel with whole-row A copies,
-    // then the one with half-row A copies (or only that one when asked for),
-    // and fall back to the register-staged one for tiles neither covers
-    // (unless staged loads were asked for explicitly).
-    const bool staged_only =
-        (t.flags & GEMM_FLAG_REGISTER_STAGED) || dtype == GEMM_F32 || dtype == GEMM_I8;
-    const bool half_rows = (t.flags & GEMM_FLAG_A_HALF_ROWS) != 0;
+    // fp16/bf16 prefer the direct-to-LDS ring kernel and fall back to the
+    // register-staged one for tiles it does not cover (64x64); fp32 and int8
+    // run the register-staged kernel
+    const bool staged_only = dtype == GEMM_F32 || dtype == GEMM_I8;
     int n = 0;
     const Variant *v = variants(&n);
-    for (int kind = staged_only ? 0 : 2; kind >= 0; --kind)
+    for (int kind = staged_only ? 0 : 2; kind >= 0; kind -= 2)
         for (int i = 0; i < n; ++i)
             if (v[i].dtype == dtype && v[i].bm == t.bm && v[i].bn == t.bn && v[i].kind == kind &&
-                !(kind == 2 && half_rows) &&
                 (v[i].stream_copies != 0) == ((t.flags & GEMM_FLAG_STREAM_COPIES) != 0) &&
                 (t.wave_m == 0 || v[i].wave_m == t.wave_m) &&
                 (t.wave_n == 0 || v[i].wave_n == t.wave_n) && (t.bk == 0 || v[i].bk == t.bk) &&
@@ -124,6 +120,9 @@ const Variant *find_variant(int dtype, const gemm_tiles &t)
                 return &v[i];
     return nullptr;
 }
+
+// Flag bits of kernel families that are no longer built.
+constexpr uint32_t kReservedFlags = (1u << 2) | (1u << 5);
 
 // Polls before a fixup wait gives up.  A poll is a sleep of ~128 cycles plus a
 // memory round trip, so this is about a second: orders of magnitude beyond a
@@ -161,6 +160,10 @@ gemm_plan *create(int64_t M, int64_t N, int64_t K, gemm_dtype dtype, gemm_schedu
     gemm_tiles t = {};
     if (tiles_in)
         t = *tiles_in;
+    if (t.flags & kReservedFlags) {
+        set_error("flags 0x%x: bits 2 and 5 are reserved", t.flags & kReservedFlags);
+        return nullptr;
+    }
     const int E = elem_size(dtype);
     if (t.bm == 0 && t.bn == 0) {
         if (dtype == GEMM_F32)
@@ -201,11 +204,17 @@ gemm_plan *create(int64_t M, int64_t N, int64_t K, gemm_dtype dtype, gemm_schedu
     const int V = 16 / E;
     const int64_t lda = (K * E) % 16 ? cdiv(K, V) * V : K;
     const int64_t ldb = (N * E) % 16 ? cdiv(N, V) * V : N;
-    // 32-bit index limits of the kernel: sizes, per-slab buffer offsets, tiles.
+    // 32-bit index limits of the kernel: sizes, and the buffer offsets within
+    // one tile's rows of A and C and one iteration's rows of B (the kernels
+    // address those through a descriptor based at the tile or slab, with
+    // 32-bit offsets, 0x80000000 meaning "out of range")
+    const int CE = dtype == GEMM_I8 ? 4 : ((t.flags & GEMM_FLAG_C_INPUT_DTYPE) ? E : 4);
     const int64_t lim = (int64_t)1 << 30;
     if (M >= lim || N >= lim || K >= lim || (int64_t)var->bm * lda * E >= lim ||
-        (int64_t)var->bk * ldb * E >= lim) {
-        set_error("matrix too large for 32-bit indexing");
+        (int64_t)var->bk * ldb * E >= lim || (int64_t)var->bm * N * CE >= lim) {
+        set_error("matrix too large for 32-bit indexing (M, N, K < 2^30 and %d rows of A, %d "
+                  "rows of B and %d rows of C each below 2^30 bytes)",
+                  var->bm, var->bk, var->bm);
         return nullptr;
     }
 
@@ -498,7 +507,7 @@ int gemm_plan_describe(const gemm_plan *p, char *buf, size_t len)
                                                          ? p->dtype
                                                          : GEMM_F32),
                     sched_name(p->schedule), p->bm, p->bn, p->bk, p->variant->wave_m,
-                    p->variant->wave_n, p->variant->kind == 2 ? "ring/rows" : p->variant->kind ? "ring" : "staged",
+                    p->variant->wave_n, p->variant->kind == 2 ? "ring" : "staged",
                     p->variant->kind ? p->variant->stages : 2, p->group_m, p->P.tiles_m,
                     p->P.tiles_n, p->P.T, p->P.ipt, p->P.T_sk, p->P.T - p->P.T_sk,
                     (long long)p->iters_sk, p->P.g, p->P.q, p->P.r, p->P.grid,
@@ -645,6 +654,27 @@ int gemm_run(const gemm_plan *p, const void *A, const void *B, void *C, void *wo
         set_error("fixup launch failed: %s", hipGetErrorString(hipGetLastError()));
         return -3;
     }
+    return 0;
+}
+
+int32_t gemm_variant_count(void)
+{
+    int n = 0;
+    variants(&n);
+    return n;
+}
+
+int gemm_variant_get(int32_t i, gemm_variant_info *out)
+{
+    int n = 0;
+    const Variant *v = variants(&n);
+    if (!out || i < 0 || i >= n) {
+        set_error("bad argument");
+        return -1;
+    }
+    const Variant &x = v[i];
+    *out = gemm_variant_info{x.dtype, x.bm,   x.bn,      x.bk,           x.wave_m, x.wave_n,
+                             x.kind,  x.stages, x.stream_copies, x.threads, x.lds_bytes};
     return 0;
 }
 

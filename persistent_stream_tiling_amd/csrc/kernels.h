@@ -40,8 +40,8 @@ struct Variant {
     int wave_m, wave_n;    // wave grid of the workgroup
     int threads;
     size_t lds_bytes;
-    int kind;              // 0: register-staged loads, 1: direct-to-LDS ring
-    int stages;            // LDS ring depth of kind 1 (0 for kind 0)
+    int kind;              // 0: register-staged loads, 2: direct-to-LDS ring
+    int stages;            // B stages of the kind-2 ring (0 for kind 0)
     int (*launch)(const KernelArgs &args, int grid, hipStream_t stream);
     const void *kernel;    // for occupancy queries
     // the two-kernel fixup's reduction kernel for this variant's piece layout

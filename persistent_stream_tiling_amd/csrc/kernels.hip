@@ -6,10 +6,8 @@
 //   gemm_kernel_pair  fp16/bf16 default: 64-deep MAC iterations, operands
 //                     copied straight from global memory into LDS (A in whole
 //                     128-byte rows), an unrolled ring of B stages and A slots.
-//   gemm_kernel_dma   fp16/bf16 with 32-deep iterations and A in 64-byte row
-//                     halves (kept for comparison).
-//   gemm_kernel       fp32 and int8, and a register-staged fp16/bf16 variant:
-//                     loads go global -> registers -> LDS, two LDS buffers.
+//   gemm_kernel       fp32, int8, and fp16/bf16 at 64x64 tiles: loads go
+//                     global -> registers -> LDS, two LDS buffers.
 //
 // int8 inputs accumulate exactly in int32 (the pages' kernel picks an int32
 // accumulator for int8); the int32 accumulators travel in the same 32-bit
@@ -530,7 +528,7 @@ static int launch_fixup(const KernelArgs &args, int grid, hipStream_t stream)
 }
 
 // ---------------------------------------------------------------------------
-// Register-staged kernel (fp32; fp16/bf16 for comparison).
+// Register-staged kernel (fp32, int8, and fp16/bf16 at 64x64 tiles).
 //
 // One MAC iteration consumes a BK-deep slab of A (BM x BK) and B (BK x BN),
 // BK being 128 bytes of input per row (32 fp32 or 64 fp16/bf16 values).  Slabs
@@ -701,51 +699,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(KernelArgs args)
 }
 
 // ---------------------------------------------------------------------------
-// fp16/bf16 kernel with direct global -> LDS loads and an S-stage LDS ring.
+// Helpers of the direct-to-LDS kernel below.
 //
-// Each MAC iteration covers BK = 32 values of k.  Its slab of A (BM rows of 64
-// bytes) and B (32 rows of BN values, row-major as in memory) is copied by
-// buffer loads that write LDS directly, S - 1 iterations ahead of its use, so
-// the copy has S - 2 whole iterations of MFMA work to hide behind and needs no
-// registers.  A rows are read as k-contiguous MFMA fragments with 16-byte
-// reads; B is read with the transposing LDS read (each 16-lane group turns a
-// 4 x 16 block of row-major values into per-lane runs of 4 k), so it never
-// passes through registers on its way in.
-//
-// Swizzles (16-byte chunk index XOR a function of the row):
-//   A: chunk ^ (((row >> 1) ^ (row >> 3)) & 3)   64-byte rows
-//   B: chunk ^ kB[k & 3], kB = {0, 6, 10, 12}    BN * 2-byte rows
-// B transposing reads (4 consecutive k-rows x 32 bytes per 16-lane group) hit
-// distinct banks; the 64-byte A rows still conflict on about a quarter of the
-// LDS cycles (measured), one reason gemm_kernel_pair is preferred.
-//
-// Per iteration and wave: wait for the next stage's copies, barrier, launch
-// the copy S - 1 iterations ahead into the stage everybody has finished with,
-// read the next stage's first fragments while this stage's second half of
-// MFMAs runs.  One barrier per iteration.
-template <int DT, int BM, int BN, int WM, int WN, int S>
-struct DmaTile {
-    static constexpr int NW = WM * WN, NTH = 64 * NW;
-    static constexpr int BK = 32;
-    static constexpr int B_ROW = BN * 2;                   // bytes per B k-row
-    static constexpr int A_STAGE = BM * 64, B_STAGE = BK * BN * 2;
-    static constexpr int STAGE = A_STAGE + B_STAGE;
-    static constexpr int LDS = S * STAGE;
-    static constexpr int A_INSTR = A_STAGE / 1024 / NW;    // 1 KiB copies per wave and stage
-    static constexpr int B_INSTR = B_STAGE / 1024 / NW;
-    static constexpr int LPI = A_INSTR + B_INSTR;
-    static constexpr int WTM = BM / WM, WTN = BN / WN, MT = WTM / 32, NT = WTN / 32;
-    static_assert(DT == 1 || DT == 2, "fp16 / bf16 only");
-    static_assert(A_INSTR * 1024 * NW == A_STAGE && B_INSTR * 1024 * NW == B_STAGE,
-                  "stage copies must split evenly over the waves");
-    static_assert(WTM % 32 == 0 && WTN % 32 == 0 && BN >= 128, "tile shape");
-    static_assert(S >= 3 && LPI * (S - 2) <= 63, "ring depth");
-    static_assert(MT * NT >= LPI, "one copy per MFMA of a slab");
-    static_assert(LDS <= 160 * 1024, "LDS budget");
-};
-
-__device__ __forceinline__ uint32_t swz_a(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
-
+// B sits in LDS row-major as in memory (k-rows of BN values) and is read
+// with the transposing LDS read: each 16-lane group turns a 4 x 16 block of
+// row-major values into per-lane runs of 4 k.  The 16-byte chunks of k-row r
+// are XOR-swizzled with kB[r & 3], kB = {0, 6, 10, 12}, so the four k-rows a
+// transposing read touches (32 bytes each per 16-lane group) hit distinct
+// banks.
 __device__ __forceinline__ uint32_t swz_b(int krow)
 {
     return (0xCA60u >> ((krow & 3) * 4)) & 0xF;  // {0, 6, 10, 12}[krow & 3]
@@ -826,243 +787,20 @@ __device__ __forceinline__ void wait_vmcnt()
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int DT, int BM, int BN, int WM, int WN, int S>
-__global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel_dma(KernelArgs args)
-{
-    using Cfg = DmaTile<DT, BM, BN, WM, WN, S>;
-    constexpr int NW = Cfg::NW, MT = Cfg::MT, NT = Cfg::NT, LPI = Cfg::LPI, BK = Cfg::BK;
-    constexpr int A_INSTR = Cfg::A_INSTR, B_INSTR = Cfg::B_INSTR;
-    constexpr int A_STAGE = Cfg::A_STAGE, B_STAGE = Cfg::B_STAGE, B_ROW = Cfg::B_ROW;
-    constexpr int A_BASE = S * B_STAGE;  // LDS: the S B stages, then the S A stages
-    constexpr int NMFMA = MT * NT;       // MFMAs per slab
-    constexpr int NREAD = MT + NT;       // fragment reads per slab
-    static_assert(2 * NMFMA >= NREAD, "two fragment reads per MFMA");
-
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[Cfg::LDS];
-
-    const Partition &P = args.P;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wy = wave / WN, wx = wave - (wave / WN) * WN;
-    const int half = lane >> 5, l32 = lane & 31;
-    const int p = logical_wg((int32_t)blockIdx.x, P.grid, P.xcds);
-    // LDS address of this wave's first 1 KiB copy block (wave-uniform)
-    const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(lds_address(lds) + wave * 1024);
-
-    // Copy geometry of this lane (fixed for the kernel).  Copy j of this wave
-    // fills the 1 KiB block j * NW + wave of a stage's A (or B) region; the
-    // lane writes bytes [16 * lane, 16 * lane + 16) of it.
-    int a_row[A_INSTR], a_chunk[A_INSTR];
-#pragma unroll
-    for (int j = 0; j < A_INSTR; ++j) {
-        const int o = (j * NW + wave) * 1024 + lane * 16;
-        a_row[j] = o >> 6;
-        a_chunk[j] = ((o >> 4) & 3) ^ swz_a(o >> 6);
-    }
-    int b_krow[B_INSTR], b_chunk[B_INSTR];
-#pragma unroll
-    for (int j = 0; j < B_INSTR; ++j) {
-        const int o = (j * NW + wave) * 1024 + lane * 16;
-        b_krow[j] = o / B_ROW;
-        b_chunk[j] = ((o % B_ROW) >> 4) ^ swz_b(o / B_ROW);
-    }
-
-    // Fragment read addresses (stage 0).  A: the lane's row r0 at chunk
-    // 2*st + half; block mt is 32 rows (2 KiB) on with the same swizzle.  B:
-    // the lane's transposing-read address for k-rows 8*(g/2) + si/4 of block
-    // nt; the other three reads of the block (4 and 16 k-rows on) keep the
-    // swizzle, which depends on the k-row mod 4 only.  Stage s adds s times
-    // the stage size, so every read is a base register plus a constant.
-    uint32_t a_rd[2];
-    {
-        const int r0 = wy * Cfg::WTM + l32;
-#pragma unroll
-        for (int st = 0; st < 2; ++st)
-            a_rd[st] = A_BASE + r0 * 64 + (((2 * st + half) ^ swz_a(r0)) << 4);
-    }
-    uint32_t b_rd[NT];
-    {
-        const int g = lane >> 4, si = lane & 15;
-        const int krow = 8 * (g >> 1) + (si >> 2);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            const int n = wx * Cfg::WTN + nt * 32 + 16 * (g & 1) + 4 * (si & 3);
-            b_rd[nt] = krow * B_ROW + (((n >> 3) ^ swz_b(krow)) << 4) + (n & 7) * 2;
-        }
-    }
-    auto read_a = [&](int s, int st, int mt) {
-        return *(const u32x4 *)(lds + a_rd[st] + s * A_STAGE + mt * 32 * 64);
-    };
-    auto read_b = [&](int s, int st, int nt) {
-        const uint8_t *base = lds + b_rd[nt] + s * B_STAGE + st * 16 * B_ROW;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(GSK_LDS(i16x4, base));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(GSK_LDS(i16x4, base + 4 * B_ROW));
-        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-        return u32x4{l2[0], l2[1], h2[0], h2[1]};
-    };
-    // Fragment read r of slab st, in the order a slab's MFMAs (block
-    // (j / NT, j % NT) for j = 0, 1, ...) first need them: A block 0, B
-    // blocks 0 .. NT-1, then A blocks 1 .. MT-1.
-    auto read_frag = [&](int s, int st, int r, u32x4 (&fa)[MT], u32x4 (&fb)[NT]) {
-        if (r == 0)
-            fa[0] = read_a(s, st, 0);
-        else if (r <= NT)
-            fb[r - 1] = read_b(s, st, r - 1);
-        else
-            fa[r - NT] = read_a(s, st, r - NT);
-    };
-
-    f32x16 acc[MT][NT];
-    u32x4 fa0[MT], fb0[NT], fa1[MT], fb1[NT];
-
-    WorkCursor cur = work_begin(P, p);
-    WorkItem w;
-    while (work_next(P, p, cur, w)) {
-        int tm, tn;
-        tile_coords(P, w.tile, &tm, &tn);
-        const int m0 = tm * BM, n0 = tn * BN;
-        const int kb = w.kb, n = w.ke - w.kb;  // MAC iterations of this item (>= 1)
-        const int k_hi = w.ke * BK < args.K ? w.ke * BK : args.K;
-
-        uint32_t a_off[A_INSTR];
-#pragma unroll
-        for (int j = 0; j < A_INSTR; ++j)
-            a_off[j] = m0 + a_row[j] < args.M
-                           ? (uint32_t)(a_row[j] * args.lda * 2 + a_chunk[j] * 16)
-                           : kOutOfRange;
-        uint32_t b_off[B_INSTR];
-#pragma unroll
-        for (int j = 0; j < B_INSTR; ++j)
-            b_off[j] = n0 + b_chunk[j] * 8 < args.N
-                           ? (uint32_t)(b_krow[j] * args.ldb * 2 + b_chunk[j] * 16)
-                           : kOutOfRange;
-        // Source of the next iteration to be copied: its first k and the A
-        // and B slabs it starts at.  The slab pointers stop at the item's last
-        // iteration, so that a copy past the end (below) never has a base
-        // outside the matrix.
-        int k_cp = kb * BK;
-        const uint8_t *a_cp = args.A + ((int64_t)m0 * args.lda + k_cp) * 2;
-        const uint8_t *b_cp = args.B + ((int64_t)k_cp * args.ldb + n0) * 2;
-        const int64_t b_step = (int64_t)BK * args.ldb * 2;
-
-        // The j-th copy (A copies first, then B) of the next iteration into
-        // stage s.  Every iteration from kb on is copied, also past the end
-        // of the item: there k >= k_hi, every lane reads out of range, and
-        // the stage (one nobody reads again) is filled with zeros.  So every
-        // iteration issues exactly LPI copies and all the waits below have
-        // constant counts.
-        auto copy_one = [&](int s, int j) {
-            const bool whole = k_cp + BK <= k_hi;
-            if (j < A_INSTR) {
-                const uint32_t off = whole || a_chunk[j] * 8 < k_hi - k_cp ? a_off[j] : kOutOfRange;
-                copy16(rsrc_words(a_cp), off, lds_wave + A_BASE + s * A_STAGE + j * NW * 1024);
-            } else {
-                const int jb = j - A_INSTR;
-                const uint32_t off = whole || b_krow[jb] < k_hi - k_cp ? b_off[jb] : kOutOfRange;
-                copy16(rsrc_words(b_cp), off, lds_wave + s * B_STAGE + jb * NW * 1024);
-            }
-        };
-        auto next_copy = [&]() {
-            if (k_cp + BK < k_hi) {
-                a_cp += BK * 2;
-                b_cp += b_step;
-            }
-            k_cp += BK;
-        };
-
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-                acc[mt][nt] = f32x16{};
-
-        // All waves are done with the previous item's stages before refilling.
-        barrier_only();
-        static_for<0, S - 1>([&](auto u) {
-#pragma unroll
-            for (int c = 0; c < LPI; ++c)
-                copy_one(u.value, c);
-            next_copy();
-        });
-        wait_vmcnt<(S - 2) * LPI>();  // iteration kb's copies have landed
-        barrier_only();
-#pragma unroll
-        for (int r = 0; r < NREAD; ++r)
-            read_frag(0, 0, r, fa0, fb0);
-
-        // MAC iteration i (stage s = i mod S, a compile-time constant here);
-        // `surely_more` says at compile time that another iteration follows.
-        auto step = [&](int i, auto s_c, auto surely_more) {
-            constexpr int s = decltype(s_c)::value;
-            constexpr int s_next = (s + 1) % S, s_fill = (s + S - 1) % S;
-            // (a) first slab's MFMAs, with the second slab's fragment reads
-            //     issued two per MFMA in the order the MFMAs consume them
-#pragma unroll
-            for (int j = 0; j < NMFMA; ++j) {
-                mfma_step<DT>(acc[j / NT][j % NT], fb0[j % NT], fa0[j / NT]);
-#pragma unroll
-                for (int r = 2 * j; r < 2 * j + 2 && r < NREAD; ++r)
-                    read_frag(s, 1, r, fa1, fb1);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            const bool more = decltype(surely_more)::value || i + 1 < n;
-            if (more) {
-                // (b) iteration i + 1's copies are complete in every wave (the
-                //     S - 3 later iterations' may still be in flight), and
-                //     every wave is past iteration i - 1's stage
-                wait_vmcnt<(S - 3) * LPI>();
-                barrier_only();
-            }
-            // (c) second slab's MFMAs, with the next iteration's first-slab
-            //     reads (unconditional: on the last iteration they are
-            //     harmless, and a fixed count lets the compiler wait for just
-            //     the fragments each MFMA needs) and the copies S - 1
-            //     iterations ahead into the stage of iteration i - 1.  The
-            //     last iteration copies nothing: without the barrier above
-            //     other waves may still be reading.
-#pragma unroll
-            for (int j = 0; j < NMFMA; ++j) {
-                mfma_step<DT>(acc[j / NT][j % NT], fb1[j % NT], fa1[j / NT]);
-#pragma unroll
-                for (int r = 2 * j; r < 2 * j + 2 && r < NREAD; ++r)
-                    read_frag(s_next, 0, r, fa0, fb0);
-                if (more && j >= NMFMA - LPI)
-                    copy_one(s_fill, j - (NMFMA - LPI));
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            if (more)
-                next_copy();
-        };
-        int i = 0;
-        for (; i + S <= n; i += S)
-            static_for<0, S>([&](auto u) { step(i + u.value, u, IC<(u.value < S - 1)>{}); });
-        static_for<0, S - 1>([&](auto u) {
-            if (i + u.value < n)
-                step(i + u.value, u, IC<0>{});
-        });
-
-        finish_tile<BM, BN, MT, NT>(acc, args, w, p, m0, n0, wave, lane, wy * Cfg::WTM,
-                                    wx * Cfg::WTN);
-    }
-    if (args.split_fixup == 1)
-        reduce_split_tiles<BM, BN, WM, WN>(args, p, wave, lane);
-}
-
 // ---------------------------------------------------------------------------
 // fp16/bf16 kernel with direct global -> LDS loads, A copied in whole rows.
 //
-// Here a MAC iteration is 64 deep (BK = 64): its A slab is BM rows of 128
-// bytes, whole cache lines, and it is multiplied as two 32-deep halves with
-// the MFMA / fragment-read pattern of gemm_kernel_dma.  (gemm_kernel_dma's
-// 64-byte row halves, copied an iteration apart, fetch every A line twice
-// through the vector L1; on a 4096^3 product that made its pure load phase
-// ~20% slower.)
+// A MAC iteration is 64 deep (BK = 64): its A slab is BM rows of 128 bytes,
+// whole cache lines, and it is multiplied as two 32-deep halves.  (Copying A
+// in 64-byte row halves, an iteration apart, fetched every A line twice
+// through the vector L1; on a 4096^3 product that made the pure load phase
+// ~20% slower.)  A fragments are 16-byte LDS reads of k-contiguous rows; B
+// fragments come from the transposing LDS read, so neither operand passes
+// through registers on its way into LDS.
 //
 // LDS: four B stages (one per half-iteration: 32 k-rows x BN values,
-// swizzled as in gemm_kernel_dma) followed by three A slots (one per
-// iteration: BM rows x 128 bytes, 16-byte chunk c of row r at position
-// c ^ ((r ^ r >> 3) & 7)).
+// swizzled with swz_b) followed by three A slots (one per iteration: BM rows
+// x 128 bytes, 16-byte chunk c of row r at position c ^ ((r ^ r >> 3) & 7)).
 //
 // Copy schedule in half-iterations t of the segment: half-iteration t issues
 // the B slab of t + 3 and half (t & 1) of the A slab of iteration (t >> 1) + 2
@@ -1071,9 +809,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel_dma(KernelArgs ar
 // the slot of iteration (t >> 1) - 1, whose last half is t - 1, and B slab
 // t + 3 into the stage of t - 1: both are free once every wave has passed the
 // barrier in the middle of half-iteration t.  The segment starts with the
-// copies that half-iterations -4 .. -1 would have issued.  As in
-// gemm_kernel_dma, copies past the end of the segment read nothing and fill
-// a free slot or stage with zeros, so every wait count is a constant.
+// copies that half-iterations -4 .. -1 would have issued.  Copies past the
+// end of the segment read nothing (out-of-range offsets) and fill a free slot
+// or stage with zeros, so every half-iteration issues the same number of
+// copies and every wait count is a constant.
 template <int DT, int BM, int BN, int WM, int WN>
 struct PairTile {
     static constexpr int NW = WM * WN, NTH = 64 * NW;
@@ -1138,7 +877,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel_pair(KernelArgs a
     // `half` (slab 0 of the first half-iteration).  Slab 1 is chunk + 2, the
     // second half-iteration chunk + 4, and block mt + 1 is 32 rows on, which
     // flips bit 2 of the row's swizzle: bits 5 and 6 of the byte offset (XOR)
-    // and 4 KiB steps (add).  B: as in gemm_kernel_dma.
+    // and 4 KiB steps (add).  B: the lane's transposing-read address for
+    // k-rows 8*(g/2) + si/4 of block nt; the other three reads of the block
+    // (4 and 16 k-rows on) keep the swizzle, which depends on the k-row mod 4
+    // only.  Stage s adds s times the stage size, so every read is a base
+    // register plus a constant.
     const int r0 = wy * Cfg::WTM + l32;
     const uint32_t a_lane = A_BASE + (uint32_t)(r0 * 128) + ((half ^ swz_row128(r0)) << 4);
     uint32_t b_rd[NT];
@@ -1351,14 +1094,6 @@ static int launch_gemm(const KernelArgs &args, int grid, hipStream_t stream)
     return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
-template <int DT, int BM, int BN, int WM, int WN, int S>
-static int launch_gemm_dma(const KernelArgs &args, int grid, hipStream_t stream)
-{
-    hipLaunchKernelGGL((gemm_kernel_dma<DT, BM, BN, WM, WN, S>), dim3(grid),
-                       dim3(DmaTile<DT, BM, BN, WM, WN, S>::NTH), 0, stream, args);
-    return hipGetLastError() == hipSuccess ? 0 : -3;
-}
-
 template <int DT, int BM, int BN, int WM, int WN, bool STREAM>
 static int launch_gemm_pair(const KernelArgs &args, int grid, hipStream_t stream)
 {
@@ -1367,20 +1102,12 @@ static int launch_gemm_pair(const KernelArgs &args, int grid, hipStream_t stream
     return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
-// Register-staged kernel (fp32, and fp16/bf16 for comparison)
+// Register-staged kernel (fp32, int8, fp16/bf16 64x64)
 #define GSK_STAGED(DT, BM, BN, WM, WN)                                                           \
     Variant{DT, BM, BN, Tile<DT, BM, BN, WM, WN>::BK, WM, WN, Tile<DT, BM, BN, WM, WN>::NTH,     \
             (size_t)Tile<DT, BM, BN, WM, WN>::LDS, 0, 0, &launch_gemm<DT, BM, BN, WM, WN>,        \
             (const void *)&gemm_kernel<DT, BM, BN, WM, WN>,                                      \
             &launch_fixup<BM, BN, WM, WN, DT == 3>, 0}
-// Direct-to-LDS ring kernel (fp16/bf16)
-#define GSK_DMA(DT, BM, BN, WM, WN, S)                                                           \
-    Variant{DT, BM, BN, 32, WM, WN, DmaTile<DT, BM, BN, WM, WN, S>::NTH,                         \
-            (size_t)DmaTile<DT, BM, BN, WM, WN, S>::LDS, 1, S,                                   \
-            &launch_gemm_dma<DT, BM, BN, WM, WN, S>,                                             \
-            (const void *)&gemm_kernel_dma<DT, BM, BN, WM, WN, S>,                               \
-            &launch_fixup<BM, BN, WM, WN, false>, 0}
-
 // Direct-to-LDS ring kernel with whole-row A copies (fp16/bf16)
 #define GSK_PAIR_X(DT, BM, BN, WM, WN, ST)                                                       \
     Variant{DT, BM, BN, 64, WM, WN, PairTile<DT, BM, BN, WM, WN>::NTH,                           \
@@ -1394,28 +1121,19 @@ static int launch_gemm_pair(const KernelArgs &args, int grid, hipStream_t stream
 #define GSK_PAIR_STREAM(DT, BM, BN, WM, WN) GSK_PAIR_X(DT, BM, BN, WM, WN, true)
 
 // The first entry matching a request wins, so each dtype's preferred kernel
-// for a tile comes first.
+// for a tile comes first.  Every entry is launched by the GPU tests (they walk
+// this table through gemm_variant_info).
 static const Variant kVariants[] = {
-    GSK_PAIR(1, 256, 256, 2, 4), GSK_PAIR(1, 256, 256, 4, 2), GSK_PAIR(1, 256, 256, 2, 2),
-    GSK_PAIR(1, 256, 128, 4, 2), GSK_PAIR(1, 256, 128, 2, 2), GSK_PAIR(1, 128, 256, 2, 4),
-    GSK_PAIR(1, 128, 256, 2, 2), GSK_PAIR(1, 128, 128, 2, 2),
-    GSK_PAIR(2, 256, 256, 2, 4), GSK_PAIR(2, 256, 256, 4, 2), GSK_PAIR(2, 256, 256, 2, 2),
-    GSK_PAIR(2, 256, 128, 4, 2), GSK_PAIR(2, 256, 128, 2, 2), GSK_PAIR(2, 128, 256, 2, 4),
-    GSK_PAIR(2, 128, 256, 2, 2), GSK_PAIR(2, 128, 128, 2, 2),
+    // fp16 / bf16: direct-to-LDS ring kernel
+    GSK_PAIR(1, 256, 256, 2, 4), GSK_PAIR(1, 256, 128, 4, 2), GSK_PAIR(1, 128, 256, 2, 4),
+    GSK_PAIR(1, 128, 128, 2, 2),
+    GSK_PAIR(2, 256, 256, 2, 4), GSK_PAIR(2, 256, 128, 4, 2), GSK_PAIR(2, 128, 256, 2, 4),
+    GSK_PAIR(2, 128, 128, 2, 2),
     GSK_PAIR_STREAM(1, 256, 256, 2, 4), GSK_PAIR_STREAM(1, 256, 128, 4, 2),
     GSK_PAIR_STREAM(2, 256, 256, 2, 4), GSK_PAIR_STREAM(2, 256, 128, 4, 2),
-    GSK_DMA(1, 256, 256, 4, 2, 4), GSK_DMA(1, 256, 256, 4, 2, 5), GSK_DMA(1, 256, 256, 2, 4, 4),
-    GSK_DMA(1, 256, 256, 2, 2, 4), GSK_DMA(1, 256, 256, 2, 2, 5), GSK_DMA(1, 256, 128, 2, 2, 4),
-    GSK_DMA(1, 256, 128, 4, 2, 4), GSK_DMA(1, 128, 256, 2, 2, 4), GSK_DMA(1, 128, 256, 2, 4, 4),
-    GSK_DMA(1, 128, 128, 2, 2, 4),
-    GSK_DMA(2, 256, 256, 4, 2, 4), GSK_DMA(2, 256, 256, 4, 2, 5), GSK_DMA(2, 256, 256, 2, 4, 4),
-    GSK_DMA(2, 256, 256, 2, 2, 4), GSK_DMA(2, 256, 256, 2, 2, 5), GSK_DMA(2, 256, 128, 2, 2, 4),
-    GSK_DMA(2, 256, 128, 4, 2, 4), GSK_DMA(2, 128, 256, 2, 2, 4), GSK_DMA(2, 128, 256, 2, 4, 4),
-    GSK_DMA(2, 128, 128, 2, 2, 4),
-    GSK_STAGED(1, 256, 256, 4, 2), GSK_STAGED(1, 256, 256, 2, 2), GSK_STAGED(1, 128, 128, 2, 2),
-    GSK_STAGED(1, 64, 64, 2, 2),
-    GSK_STAGED(2, 256, 256, 4, 2), GSK_STAGED(2, 256, 256, 2, 2), GSK_STAGED(2, 128, 128, 2, 2),
-    GSK_STAGED(2, 64, 64, 2, 2),
+    // fp16 / bf16 64x64 tiles (below the ring kernel's smallest tile), fp32, int8:
+    // register-staged kernel
+    GSK_STAGED(1, 64, 64, 2, 2), GSK_STAGED(2, 64, 64, 2, 2),
     GSK_STAGED(0, 128, 128, 2, 2), GSK_STAGED(0, 64, 64, 2, 2),
     GSK_STAGED(3, 256, 256, 4, 2), GSK_STAGED(3, 128, 128, 2, 2),
 };
@@ -1429,37 +1147,63 @@ const Variant *variants(int *count)
 // ---------------------------------------------------------------- helpers
 
 // dst (rows x ld_dst) = src (rows x cols, leading dimension ld_src), zero
-// padded on the right; one thread per destination element.
+// padded on the right; ld_dst * sizeof(T) is a multiple of 16 bytes and dst
+// is 16-byte aligned.  A workgroup fills one 4 KiB span of a destination row:
+// its threads read the span's source elements with consecutive lanes on
+// consecutive elements (whole cache lines per wave, whatever the alignment of
+// the source row), stage them in LDS, and write the span back with one
+// 16-byte store per thread.  Rows are strided over gridDim.y; no division.
+constexpr int kPackThreads = 256;
+constexpr int kPackSpan = kPackThreads * 16;  // destination bytes per workgroup and row
+
 template <typename T>
-__global__ void pack_kernel(const T *__restrict__ src, T *__restrict__ dst, int64_t rows,
-                            int64_t cols, int64_t ld_src, int64_t ld_dst)
+__global__ __launch_bounds__(kPackThreads) void pack_kernel(const T *__restrict__ src,
+                                                            T *__restrict__ dst, int64_t rows,
+                                                            int64_t cols, int64_t ld_src,
+                                                            int64_t ld_dst)
 {
-    const int64_t total = rows * ld_dst;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-         i += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t r = i / ld_dst, c = i - (i / ld_dst) * ld_dst;
-        dst[i] = c < cols ? src[r * ld_src + c] : T(0);
+    constexpr int V = 16 / (int)sizeof(T);          // elements per 16-byte chunk
+    constexpr int PER = kPackSpan / (int)sizeof(T); // elements per span
+    __shared__ __attribute__((aligned(16))) T span[PER];
+    const int tid = threadIdx.x;
+    const int64_t c0 = (int64_t)blockIdx.x * PER;   // first column of this span
+    const int64_t mine = c0 + (int64_t)tid * V;     // first column this thread stores
+    for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
+        const T *s = src + r * ld_src;
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+            const int64_t col = c0 + j * kPackThreads + tid;
+            span[j * kPackThreads + tid] = col < cols ? s[col] : T(0);
+        }
+        __syncthreads();
+        if (mine < ld_dst)
+            *(u32x4 *)(dst + r * ld_dst + mine) = *(const u32x4 *)(span + tid * V);
+        __syncthreads();  // the span is refilled for the next row
     }
+}
+
+template <typename T>
+static void launch_pack_t(const void *src, void *dst, int64_t rows, int64_t cols, int64_t ld_src,
+                          int64_t ld_dst, hipStream_t stream)
+{
+    constexpr int64_t PER = kPackSpan / sizeof(T);
+    const int64_t spans = (ld_dst + PER - 1) / PER;
+    const int64_t ys = rows < 32768 ? rows : 32768;
+    hipLaunchKernelGGL(pack_kernel<T>, dim3((unsigned)spans, (unsigned)ys), dim3(kPackThreads), 0,
+                       stream, (const T *)src, (T *)dst, rows, cols, ld_src, ld_dst);
 }
 
 int launch_pack(const void *src, void *dst, int64_t rows, int64_t cols, int64_t ld_src,
                 int64_t ld_dst, int elem_size, hipStream_t stream)
 {
-    const int64_t total = rows * ld_dst;
-    if (total <= 0)
+    if (rows <= 0 || ld_dst <= 0)
         return 0;
-    int64_t blocks = (total + 255) / 256;
-    if (blocks > 8192)
-        blocks = 8192;
     if (elem_size == 1)
-        hipLaunchKernelGGL(pack_kernel<uint8_t>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                           (const uint8_t *)src, (uint8_t *)dst, rows, cols, ld_src, ld_dst);
+        launch_pack_t<uint8_t>(src, dst, rows, cols, ld_src, ld_dst, stream);
     else if (elem_size == 2)
-        hipLaunchKernelGGL(pack_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                           (const uint16_t *)src, (uint16_t *)dst, rows, cols, ld_src, ld_dst);
+        launch_pack_t<uint16_t>(src, dst, rows, cols, ld_src, ld_dst, stream);
     else
-        hipLaunchKernelGGL(pack_kernel<uint32_t>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                           (const uint32_t *)src, (uint32_t *)dst, rows, cols, ld_src, ld_dst);
+        launch_pack_t<uint32_t>(src, dst, rows, cols, ld_src, ld_dst, stream);
     return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 

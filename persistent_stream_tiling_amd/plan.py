@@ -4,6 +4,11 @@ import ctypes
 from ._lib import (DTYPES, FLAG_C_INPUT_DTYPE, SCHEDULES, DeviceDesc, PlanInfo, Segment, Tiles,
                    last_error, load)
 
+
+class FixupError(RuntimeError):
+    """A Stream-K fixup wait gave up: the run's C is not valid, and the
+    workspace must be zero-filled before it serves another run."""
+
 _TORCH_DTYPES = None
 
 
@@ -26,12 +31,14 @@ def _code(table, key, what):
 
 
 class GemmPlan:
-    """A plan for C = A.B (M x K times K x N, fp32 C) under one schedule.
+    """A plan for C = A.B (M x K times K x N) under one schedule.
 
     ``schedule`` is "dp", "persistent", "streamk" or "hybrid"; ``dtype`` is
-    "f32", "f16" or "bf16".  Tile knobs default to the library's choice.
-    With ``device`` = (cus, xcds, wg_per_cu) the plan is made for a described
-    device without touching a GPU (inspection only).
+    "f32", "f16", "bf16" (fp32 accumulate; C fp32, or the input dtype with
+    ``flags=FLAG_C_INPUT_DTYPE``) or "i8" (exact int32 accumulate, int32 C).
+    Tile knobs default to the library's choice.  With ``device`` =
+    (cus, xcds, wg_per_cu) the plan is made for a described device without
+    touching a GPU (inspection only).
     """
 
     def __init__(self, M, N, K, dtype, schedule="hybrid", bm=0, bn=0, bk=0, grid=0, group_m=0,
@@ -58,6 +65,10 @@ class GemmPlan:
         self.dtype = dtype if isinstance(dtype, str) else {v: k for k, v in DTYPES.items()}[d]
         self.schedule = schedule
         self.workspace_bytes = int(self._lib.gemm_plan_workspace_size(h))
+        # a run can end with a fixup wait that gave up only when workgroups
+        # wait on each other's pieces: some tile split, in-kernel fixup
+        self.may_wait = (self.info["tiles_sk"] > 0 and self.info["max_pieces"] >= 2
+                         and self.info["split_fixup"] != 2)
 
     # -- introspection --------------------------------------------------
     def describe(self):
@@ -96,10 +107,15 @@ class GemmPlan:
         return torch.zeros(self.workspace_bytes, dtype=torch.uint8,
                            device=device or torch.device("cuda"))
 
-    def run(self, A, B, C, workspace=None, stream=None):
+    def run(self, A, B, C, workspace=None, stream=None, check=True):
         """Enqueue C = A.B on ``stream`` (default: torch's current stream).
 
-        A, B, C and workspace are torch tensors (or raw device addresses)."""
+        A, B, C and workspace are torch tensors (or raw device addresses).
+        With ``check`` (the default) and a plan whose workgroups wait on each
+        other (``may_wait``), the workspace status is read after the run,
+        which synchronizes the stream, and a fixup wait that gave up raises
+        FixupError.  ``check=False`` keeps the call asynchronous (the caller
+        then reads ``workspace_status`` itself)."""
         import torch
 
         def ptr(x):
@@ -114,17 +130,29 @@ class GemmPlan:
         rc = self._lib.gemm_run(self._h, ptr(A), ptr(B), ptr(C), ptr(workspace), stream)
         if rc != 0:
             raise RuntimeError(f"gemm_run failed ({rc}): {last_error()}")
+        if check and self.may_wait:
+            st = self._status(ptr(workspace), stream)
+            if st != 0:
+                raise FixupError(f"a Stream-K fixup wait gave up (workspace status {st}): C is "
+                                 "not valid and the workspace must be zero-filled again; "
+                                 f"plan: {self.describe()}")
 
-    def workspace_status(self, workspace, stream=None):
-        import torch
-        if stream is None:
-            stream = torch.cuda.current_stream().cuda_stream
+    def _status(self, ws_ptr, stream_handle):
         st = ctypes.c_int32()
-        ws = workspace.data_ptr() if workspace is not None else None
-        rc = self._lib.gemm_workspace_status(self._h, ws, stream, ctypes.byref(st))
+        rc = self._lib.gemm_workspace_status(self._h, ws_ptr, stream_handle, ctypes.byref(st))
         if rc:
             raise RuntimeError(last_error())
         return st.value
+
+    def workspace_status(self, workspace, stream=None):
+        """Synchronously read the workspace status word (0 ok, 1 a fixup wait gave up)."""
+        import torch
+        if stream is None:
+            stream = torch.cuda.current_stream().cuda_stream
+        elif isinstance(stream, torch.cuda.Stream):
+            stream = stream.cuda_stream
+        ws = workspace.data_ptr() if workspace is not None else None
+        return self._status(ws, stream)
 
     def close(self):
         if self._h:
@@ -150,7 +178,14 @@ def matmul(a, b, schedule="hybrid", out_dtype=None, **tiles):
     """C = a @ b for contiguous CUDA tensors a (M x K) and b (K x N) of
     float32, float16, bfloat16 or int8, through the library's kernels.  C is
     fp32, or a's dtype when ``out_dtype`` is a's dtype (fp32 sums rounded to
-    nearest even as they are stored); int32 for int8 inputs."""
+    nearest even as they are stored); int32 for int8 inputs.
+
+    Plans and their zero-filled workspaces are cached per shape, dtype,
+    schedule, knobs, device and stream, so calls on different streams never
+    share a workspace.  The call reads the workspace status after any run
+    whose workgroups wait on each other (it then synchronizes the stream) and
+    raises FixupError if a fixup wait gave up; the cached workspace is
+    zero-filled again first, so the next call starts clean."""
     import torch
     if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[0]:
         raise ValueError(f"incompatible shapes {tuple(a.shape)} and {tuple(b.shape)}")
@@ -168,7 +203,9 @@ def matmul(a, b, schedule="hybrid", out_dtype=None, **tiles):
     a, b = a.contiguous(), b.contiguous()
     M, K = a.shape
     N = b.shape[1]
-    key = (M, N, K, a.dtype, schedule, tuple(sorted(tiles.items())), a.device.index)
+    stream = torch.cuda.current_stream(a.device)
+    key = (M, N, K, a.dtype, schedule, tuple(sorted(tiles.items())), a.device.index,
+           stream.cuda_stream)
     entry = _PLANS.get(key)
     if entry is None:
         plan = GemmPlan(M, N, K, _torch_dtypes()[a.dtype], schedule, **tiles)
@@ -178,5 +215,9 @@ def matmul(a, b, schedule="hybrid", out_dtype=None, **tiles):
     c_half = tiles.get("flags", 0) & FLAG_C_INPUT_DTYPE
     c_type = torch.int32 if a.dtype == torch.int8 else (a.dtype if c_half else torch.float32)
     c = torch.empty((M, N), dtype=c_type, device=a.device)
-    plan.run(a, b, c, ws)
+    try:
+        plan.run(a, b, c, ws, stream=stream)
+    except FixupError:
+        ws.zero_()
+        raise
     return c

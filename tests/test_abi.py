@@ -90,3 +90,48 @@ def test_plan_describes_its_output_dtype():
                                flags=gsk.FLAG_C_INPUT_DTYPE)
     assert " C=bf16 " in plan.describe()
     assert plan.info["flags"] & gsk.FLAG_C_INPUT_DTYPE
+
+
+def test_variant_table_is_exported_and_each_entry_selectable():
+    vs = gsk.variants()
+    assert len(vs) == gsk.load().gemm_variant_count() > 0
+    names = {0: "f32", 1: "f16", 2: "bf16", 3: "i8"}
+    seen = set()
+    for v in vs:
+        key = (v["dtype"], v["bm"], v["bn"], v["wave_m"], v["wave_n"], v["stream_copies"])
+        assert key not in seen, f"two table entries for {key}"
+        seen.add(key)
+        flags = gsk.FLAG_STREAM_COPIES if v["stream_copies"] else 0
+        plan = gsk.plan_for_device(1000, 1000, 1000, names[v["dtype"]], "dp", bm=v["bm"],
+                                   bn=v["bn"], wave_m=v["wave_m"], wave_n=v["wave_n"],
+                                   stages=v["stages"], flags=flags)
+        info = plan.info
+        assert (info["bm"], info["bn"], info["bk"], info["wave_m"], info["wave_n"],
+                info["kernel_kind"], info["stages"], info["threads"]) == \
+            (v["bm"], v["bn"], v["bk"], v["wave_m"], v["wave_n"], v["kind"], v["stages"],
+             v["threads"])
+    lib = gsk.load()
+    assert lib.gemm_variant_get(len(vs), None) == -1
+    assert lib.gemm_variant_get(-1, None) == -1
+
+
+def test_reserved_flag_bits_are_refused():
+    for bit in (2, 5):
+        with pytest.raises(ValueError, match="reserved"):
+            gsk.plan_for_device(300, 200, 704, "f16", "dp", flags=1 << bit)
+
+
+def test_output_offsets_stay_within_32_bits():
+    # one tile's rows of C are addressed with 32-bit byte offsets, kept below
+    # 2^30: 256 rows of 2^20 fp32 values reach it and are refused, 2^20 - 256
+    # columns stay below it
+    with pytest.raises(ValueError, match="32-bit"):
+        gsk.plan_for_device(256, 1 << 22, 64, "f16", "dp", bm=256, bn=256)
+    with pytest.raises(ValueError, match="32-bit"):
+        gsk.plan_for_device(256, 1 << 20, 64, "f16", "dp", bm=256, bn=256)
+    ok = gsk.plan_for_device(256, (1 << 20) - 256, 64, "f16", "dp", bm=256, bn=256)
+    assert ok.info["N"] == (1 << 20) - 256
+    # with fp16 C the same row block holds twice the columns
+    ok = gsk.plan_for_device(256, (1 << 21) - 256, 64, "f16", "dp", bm=256, bn=256,
+                             flags=gsk.FLAG_C_INPUT_DTYPE)
+    assert ok.info["N"] == (1 << 21) - 256
