@@ -218,6 +218,36 @@ gemm_plan *gemm_plan_create_for_device(int64_t M, int64_t N, int64_t K, gemm_dty
 int gemm_run(const gemm_plan *plan, const void *A, const void *B, void *C, void *workspace,
              void *stream);
 
+/* Most workspace gemm_run_noalloc can provide: 80 MiB per device, held from
+ * its first call on a device until the process ends.  That covers every
+ * Stream-K / hybrid plan with tiles up to 256x128 at the default grid of 256
+ * workgroups (64 MiB of partial slots in split mode), and 256x256 tiles up to
+ * g = 160; plans whose operands are repacked also need room for the packed
+ * copies. */
+#define GEMM_NOALLOC_MAX_WORKSPACE ((size_t)80 << 20)
+
+/*
+ * gemm_run without a caller-owned workspace, for callers that cannot allocate
+ * device memory: code being captured into a HIP graph, tight serving loops,
+ * and harnesses that forbid hipMalloc.  It allocates nothing: the workspace is
+ * a fixed array in the library's device memory (GEMM_NOALLOC_MAX_WORKSPACE
+ * bytes per device, set up on the first call on each device).  The caller
+ * passes A, B, C and the stream exactly as for gemm_run, and gets the same
+ * bits as gemm_run with the same plan.
+ *
+ * Every call on a device shares that device's array, which keeps what the
+ * last call left; each call clears the parts that must start at zero (status
+ * word, flags, counters) with a fill kernel on the stream before the GEMM, so
+ * an earlier call, even one whose fixup wait gave up, leaves no stale state.
+ * Calls that overlap in time on one device race on the array: serialise them
+ * (e.g. issue them on one stream).  gemm_workspace_status(plan, NULL, stream,
+ * &status) reads the array's status word after a call.
+ *
+ * Returns what gemm_run returns, and -2 when the plan needs more workspace
+ * than the array holds (message in gemm_last_error()).
+ */
+int gemm_run_noalloc(const gemm_plan *plan, const void *A, const void *B, void *C, void *stream);
+
 /* Free a plan (NULL is ignored). */
 void gemm_plan_destroy(gemm_plan *plan);
 
@@ -286,7 +316,9 @@ int32_t gemm_plan_logical_wg(const gemm_plan *plan, int32_t hw);
 
 /* Synchronously read the workspace status word written by the last run on
  * stream: 0 = ok, 1 = a fixup wait gave up (the output is not valid and the
- * workspace must be zero-filled again).  Returns 0 or a negative error. */
+ * workspace must be zero-filled again).  workspace NULL: the array that
+ * gemm_run_noalloc uses on the current device.  Returns 0 or a negative
+ * error. */
 int gemm_workspace_status(const gemm_plan *plan, const void *workspace, void *stream,
                           int32_t *status);
 

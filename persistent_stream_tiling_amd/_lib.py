@@ -16,6 +16,7 @@ FLAG_DEBUG_DROP_SIGNAL = 1 << 7
 FLAG_FIXUP_TWO_KERNEL = 1 << 8
 FLAG_STREAM_COPIES = 1 << 9
 ROLE_FULL, ROLE_CONTRIB, ROLE_OWNER = 0, 1, 2
+NOALLOC_MAX_WORKSPACE = 80 << 20  # GEMM_NOALLOC_MAX_WORKSPACE
 
 SCHEDULES = {"dp": DP, "persistent": PERSISTENT, "streamk": STREAMK, "hybrid": HYBRID}
 DTYPES = {"f32": F32, "f16": F16, "bf16": BF16, "i8": I8}
@@ -70,7 +71,8 @@ class Segment(ctypes.Structure):
                 ("role", ctypes.c_int32), ("peer_last", ctypes.c_int32)]
 
 
-EXPORTS = ("gemm_plan_create", "gemm_plan_create_for_device", "gemm_run", "gemm_plan_destroy",
+EXPORTS = ("gemm_plan_create", "gemm_plan_create_for_device", "gemm_run", "gemm_run_noalloc",
+           "gemm_plan_destroy",
            "gemm_plan_workspace_size", "gemm_plan_describe", "gemm_last_error",
            "gemm_plan_get_info", "gemm_plan_segments", "gemm_plan_tile_coords",
            "gemm_plan_logical_wg", "gemm_workspace_status", "gemm_variant_count",
@@ -98,6 +100,8 @@ def load(path=None):
     lib.gemm_plan_create_for_device.restype = vp
     lib.gemm_run.argtypes = [vp, vp, vp, vp, vp, vp]
     lib.gemm_run.restype = ctypes.c_int
+    lib.gemm_run_noalloc.argtypes = [vp, vp, vp, vp, vp]
+    lib.gemm_run_noalloc.restype = ctypes.c_int
     lib.gemm_plan_destroy.argtypes = [vp]
     lib.gemm_plan_destroy.restype = None
     lib.gemm_plan_workspace_size.argtypes = [vp]

@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 #include <new>
 #include <string>
 
@@ -678,6 +679,87 @@ int gemm_variant_get(int32_t i, gemm_variant_info *out)
     return 0;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Workspace of gemm_run_noalloc: one array per device, in the library's own
+// device memory, held until the process ends.  In host code `scratch` is only
+// a stand-in for the symbol; its device address comes from
+// hipGetSymbolAddress, once per device, and only that address is ever handed
+// to a kernel or a fill.
+constexpr size_t kNoAllocBytes = GEMM_NOALLOC_MAX_WORKSPACE;
+static __device__ __align__(256) uint8_t scratch[kNoAllocBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on device dev, which must be current; looked up
+// on the first call for that device.
+void *scratch_on(int dev)
+{
+    if (dev < 0 || dev >= kMaxDevices) {
+        set_error("device %d out of range for the no-alloc workspace", dev);
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr) {
+            set_error("no-alloc workspace: hipGetSymbolAddress failed on device %d: %s", dev,
+                      hipGetErrorString(e));
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_run_noalloc(const gemm_plan *p, const void *A, const void *B, void *C, void *stream_v)
+{
+    if (!p) {
+        set_error("NULL plan");
+        return -1;
+    }
+    if (p->ws_size > kNoAllocBytes) {
+        set_error("plan needs %zu bytes of workspace; gemm_run_noalloc has %zu (use gemm_run "
+                  "with a caller-owned workspace)",
+                  p->ws_size, kNoAllocBytes);
+        return -2;
+    }
+    if (p->ws_size == 0)
+        return gemm_run(p, A, B, C, nullptr, stream_v);
+    if (p->device < 0) {
+        set_error("plan was made for a described device; create it with gemm_plan_create");
+        return -5;
+    }
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess || cur != p->device) {
+        set_error("plan was made for device %d, current device is %d", p->device, cur);
+        return -5;
+    }
+    uint8_t *ws = (uint8_t *)scratch_on(cur);
+    if (!ws)
+        return -3;
+    // The array keeps whatever the last call on this device left: clear the
+    // status word, flags and counters this plan reads (a fill kernel, not a
+    // memset, so the call can be captured in a graph).  Partial slots are
+    // written before they are read; repacked operands are rewritten.
+    if (p->P.T_sk > 0 && p->M > 0 && p->N > 0 && p->K > 0 &&
+        launch_zero(ws, (int64_t)(p->off_partials / sizeof(uint32_t)), (int)sizeof(uint32_t),
+                    (hipStream_t)stream_v)) {
+        set_error("workspace clear failed: %s", hipGetErrorString(hipGetLastError()));
+        return -3;
+    }
+    return gemm_run(p, A, B, C, ws, stream_v);
+}
+
 int gemm_workspace_status(const gemm_plan *p, const void *workspace, void *stream,
                           int32_t *status)
 {
@@ -689,8 +771,10 @@ int gemm_workspace_status(const gemm_plan *p, const void *workspace, void *strea
     if (p->P.T_sk == 0)
         return 0;
     if (!workspace) {
-        set_error("NULL workspace");
-        return -2;
+        // the array gemm_run_noalloc runs in, on the current device
+        int cur = -1;
+        if (hipGetDevice(&cur) != hipSuccess || !(workspace = scratch_on(cur)))
+            return -2;
     }
     hipStream_t s = (hipStream_t)stream;
     if (hipMemcpyAsync(status, workspace, sizeof(int32_t), hipMemcpyDeviceToHost, s) !=

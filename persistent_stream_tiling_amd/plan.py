@@ -137,6 +137,29 @@ class GemmPlan:
                                  "not valid and the workspace must be zero-filled again; "
                                  f"plan: {self.describe()}")
 
+    def run_noalloc(self, A, B, C, stream=None, check=True):
+        """Enqueue C = A.B through gemm_run_noalloc: no workspace argument, no
+        allocation (the library's fixed per-device array serves as the
+        workspace; calls that overlap in time on one device race).  ``check``
+        as in ``run``."""
+        import torch
+
+        def ptr(x):
+            return x.data_ptr() if isinstance(x, torch.Tensor) else int(x)
+
+        if stream is None:
+            stream = torch.cuda.current_stream().cuda_stream
+        elif isinstance(stream, torch.cuda.Stream):
+            stream = stream.cuda_stream
+        rc = self._lib.gemm_run_noalloc(self._h, ptr(A), ptr(B), ptr(C), stream)
+        if rc != 0:
+            raise RuntimeError(f"gemm_run_noalloc failed ({rc}): {last_error()}")
+        if check and self.may_wait:
+            st = self._status(None, stream)
+            if st != 0:
+                raise FixupError(f"a Stream-K fixup wait gave up (status {st}): C is not valid; "
+                                 f"plan: {self.describe()}")
+
     def _status(self, ws_ptr, stream_handle):
         st = ctypes.c_int32()
         rc = self._lib.gemm_workspace_status(self._h, ws_ptr, stream_handle, ctypes.byref(st))
