@@ -122,7 +122,18 @@ enum {
      * 512x512x65536 under Stream-K), slower where tiles share operand panels
      * in L2.  Built for 256x256 (2x4 waves) and 256x128 (4x2) tiles; other
      * tiles with this flag have no kernel. */
-    GEMM_FLAG_STREAM_COPIES = 1u << 9
+    GEMM_FLAG_STREAM_COPIES = 1u << 9,
+    /* Bit 10 is reserved. */
+    /* fp16/bf16, 256x256 tiles: the wave-specialised ping-pong kernel
+     * (kernel_kind 3).  Its eight waves form two groups, one wave of each on
+     * every SIMD, that take turns: one group runs a burst of MFMAs on
+     * fragments already in registers while the other issues its share of the
+     * global -> LDS copies and reads its next fragments ("naive vs
+     * persistent matmul" post on the Hugging Face activity feed page: warp
+     * specialization and ping-pong scheduling, there for NVIDIA's warp groups).
+     * Same results as the default kernel with the same tile (the same MFMAs
+     * in the same order per element). */
+    GEMM_FLAG_PING_PONG = 1u << 11
 };
 
 /* Tile and schedule knobs.  Every field 0 means "default". */
@@ -272,7 +283,7 @@ typedef struct {
     int32_t bm, bn, bk, group_m;
     uint32_t flags;
     int32_t wave_m, wave_n;
-    int32_t kernel_kind;  /* 0 register-staged, 2 direct-to-LDS ring */
+    int32_t kernel_kind;  /* 0 register-staged, 2 direct-to-LDS ring, 3 ping-pong */
     int32_t stages;
     int32_t split_fixup;  /* 1 when the Stream-K fixup is split (see flags) */
     int32_t max_pieces;   /* most workgroups sharing one Stream-K tile */

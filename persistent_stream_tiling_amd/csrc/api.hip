@@ -109,11 +109,15 @@ const Variant *find_variant(int dtype, const gemm_tiles &t)
     // register-staged one for tiles it does not cover (64x64); fp32 and int8
     // run the register-staged kernel
     const bool staged_only = dtype == GEMM_F32 || dtype == GEMM_I8;
+    const bool ping_pong = (t.flags & GEMM_FLAG_PING_PONG) != 0;
     int n = 0;
     const Variant *v = variants(&n);
-    for (int kind = staged_only ? 0 : 2; kind >= 0; kind -= 2)
+    // kinds in order of preference: 3 (ping-pong, only when asked for), else
+    // 2 (ring) then 0 (staged)
+    const int kinds[3] = {ping_pong ? 3 : (staged_only ? 0 : 2), ping_pong ? -1 : 0, -1};
+    for (int ki = 0; ki < 3 && kinds[ki] >= 0; ++ki)
         for (int i = 0; i < n; ++i)
-            if (v[i].dtype == dtype && v[i].bm == t.bm && v[i].bn == t.bn && v[i].kind == kind &&
+            if (v[i].dtype == dtype && v[i].bm == t.bm && v[i].bn == t.bn && v[i].kind == kinds[ki] &&
                 (v[i].stream_copies != 0) == ((t.flags & GEMM_FLAG_STREAM_COPIES) != 0) &&
                 (t.wave_m == 0 || v[i].wave_m == t.wave_m) &&
                 (t.wave_n == 0 || v[i].wave_n == t.wave_n) && (t.bk == 0 || v[i].bk == t.bk) &&
@@ -508,7 +512,7 @@ int gemm_plan_describe(const gemm_plan *p, char *buf, size_t len)
                                                          ? p->dtype
                                                          : GEMM_F32),
                     sched_name(p->schedule), p->bm, p->bn, p->bk, p->variant->wave_m,
-                    p->variant->wave_n, p->variant->kind == 2 ? "ring" : "staged",
+                    p->variant->wave_n, p->variant->kind == 3 ? "pingpong" : p->variant->kind == 2 ? "ring" : "staged",
                     p->variant->kind ? p->variant->stages : 2, p->group_m, p->P.tiles_m,
                     p->P.tiles_n, p->P.T, p->P.ipt, p->P.T_sk, p->P.T - p->P.T_sk,
                     (long long)p->iters_sk, p->P.g, p->P.q, p->P.r, p->P.grid,

@@ -1086,6 +1086,270 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel_pair(KernelArgs a
         reduce_split_tiles<BM, BN, WM, WN>(args, p, wave, lane);
 }
 
+// ---------------------------------------------------------------------------
+// fp16/bf16 wave-specialised "ping-pong" kernel (256x256 tiles, 8 waves).
+//
+// The waves form two groups of four, one wave of each group on every SIMD
+// (wave w runs on SIMD w mod 4): group 0 (waves 0-3) computes tile rows
+// 0-127, group 1 (waves 4-7) rows 128-255, each wave a 128 x 64 block.  Time
+// is cut into phases separated by workgroup barriers, and the groups take
+// turns: while one group runs a burst of 16 MFMAs on fragments it already
+// holds in registers, the other does its memory work for its next burst (its
+// share of the global -> LDS copies, the LDS fragment reads, and the waits),
+// so each SIMD's matrix unit is fed by one wave while the other waits on
+// memory.  With half-iterations h (32 k each):
+//   phase 2h:     group 0 multiplies h;       group 1 reads h
+//   phase 2h + 1: group 0 reads h + 1;        group 1 multiplies h
+// (group 0 reads h = 0 in a phase of its own before phase 0).
+//
+// Copies: in its memory phase for h, group 1 copies the B stage of h + 3 and
+// group 0 the A rows of h + 3 (rows 0-127 of iteration (h + 3) >> 1 when h + 3
+// is even, rows 128-255 when it is odd); each is 16 KiB, four 1 KiB copies
+// per wave.  The item starts with the copies of h = 0, 1, 2.  Every wave waits
+// at the end of every phase until at most two of its copy batches are in
+// flight, so each copy has two phases' worth of time to land.  The LDS layout
+// is gemm_kernel_pair's (four B stages of 32 k-rows, three A slots of 64 k),
+// and a CPU model of this schedule (every read sees landed data; no copy
+// overwrites a buffer still being read, copies past the end included) was
+// checked for every segment length up to 199 half-iterations.  As in
+// gemm_kernel_pair, copies past the end of a segment read nothing and zero a
+// free buffer, so the wait counts are constants.
+//
+// Accumulators, the epilogue and the Stream-K fixups are gemm_kernel_pair's
+// with the 2 x 4 wave layout (group = wave row, wave mod 4 = wave column).
+// The body run by one group (GRP 0 or 1).  Each group has its own copy of
+// the whole work loop, so no register value is merged between the groups'
+// paths; both copies cross the same barriers in the same order.
+template <int DT, int GRP>
+__device__ __forceinline__ void gemm_pp_group(const KernelArgs &args, uint8_t *lds, int q,
+                                              int lane, int p)
+{
+    using Cfg = PairTile<DT, 256, 256, 2, 4>;
+    constexpr int MT = Cfg::MT, NT = Cfg::NT, HK = Cfg::HK, BK = Cfg::BK;
+    constexpr int A_SLOT = Cfg::A_SLOT, B_STAGE = Cfg::B_STAGE, A_BASE = Cfg::A_BASE;
+    constexpr int B_ROW = Cfg::B_ROW, SB = Cfg::SB, SA = Cfg::SA;
+    static_assert(MT == 4 && NT == 2 && SB == 4 && SA == 3, "256x256, 2x4 waves");
+    const Partition &P = args.P;
+    const int wave = GRP * 4 + q;
+    const int half = lane >> 5, l32 = lane & 31;
+    const uint32_t lds_base = __builtin_amdgcn_readfirstlane(lds_address(lds));
+
+    // Copy geometry.  Copy j (0..3) of this wave fills 1 KiB block 4j + q of a
+    // 16 KiB piece.  Group 0: rows 8*(4j + q) + lane/8 of the A row half,
+    // position lane & 7 holding 16-byte chunk (lane & 7) ^ swizzle(row) (the
+    // swizzle is the same for both row halves: they differ by 128 rows).
+    // Group 1: k-rows 2*(4j + q) + lane/32 of the B stage.
+    int cp_row[4], cp_chunk[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if constexpr (GRP == 0) {
+            cp_row[j] = 8 * (4 * j + q) + (lane >> 3);
+            cp_chunk[j] = (lane & 7) ^ (int)swz_row128(cp_row[j]);
+        } else {
+            cp_row[j] = 2 * (4 * j + q) + (lane >> 5);
+            cp_chunk[j] = (lane & 31) ^ (int)swz_b(cp_row[j]);
+        }
+    }
+    const uint32_t cp_lds = lds_base + (uint32_t)q * 1024;
+
+    // Fragment read addresses (gemm_kernel_pair's, with wave row GRP and
+    // wave column q).
+    const int r0 = GRP * Cfg::WTM + l32;
+    const uint32_t a_lane = A_BASE + (uint32_t)(r0 * 128) + ((half ^ swz_row128(r0)) << 4);
+    uint32_t b_rd[NT];
+    {
+        const int g = lane >> 4, si = lane & 15;
+        const int krow = 8 * (g >> 1) + (si >> 2);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const int n = q * Cfg::WTN + nt * 32 + 16 * (g & 1) + 4 * (si & 3);
+            b_rd[nt] = krow * B_ROW + (((n >> 3) ^ swz_b(krow)) << 4) + (n & 7) * 2;
+        }
+    }
+    // a_x: the lane's A address with the half-iteration's parity folded in
+    // (bit 2 of the chunk index); stage_off: the B stage's byte offset
+    auto read_a = [&](uint32_t slot_off, uint32_t a_x, int st, int mt) {
+        const uint32_t x = (uint32_t)((st << 5) | ((mt & 1) << 6));
+        return *(const u32x4 *)(lds + slot_off + mt * 4096 + (a_x ^ x));
+    };
+    auto read_b = [&](uint32_t stage_off, int st, int nt) {
+        const uint8_t *base = lds + stage_off + b_rd[nt] + st * 16 * B_ROW;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(GSK_LDS(i16x4, base));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(GSK_LDS(i16x4, base + 4 * B_ROW));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        return u32x4{l2[0], l2[1], h2[0], h2[1]};
+    };
+
+    f32x16 acc[MT][NT];
+    u32x4 fa[2][MT], fb[2][NT];  // both 16-k slabs of one half-iteration
+
+    WorkCursor cur = work_begin(P, p);
+    WorkItem w;
+    while (work_next(P, p, cur, w)) {
+        int tm, tn;
+        tile_coords(P, w.tile, &tm, &tn);
+        const int m0 = tm * 256, n0 = tn * 256;
+        const int k_lo = w.kb * BK;
+        const int k_hi = w.ke * BK < args.K ? w.ke * BK : args.K;
+        const int n = (k_hi - k_lo + HK - 1) / HK;  // half-iterations of this item (>= 1)
+        // first k of the item's last slab (copy sources never start past it)
+        const int kb_last = k_lo + ((k_hi - k_lo - 1) / HK) * HK;
+        const int ka_last = k_lo + ((k_hi - k_lo - 1) / BK) * BK;
+
+        // per-item source offsets (out of range: rows past M, columns past N);
+        // group 0: off0 for rows 0-127, off1 for rows 128-255 (two named
+        // arrays: one array indexed by the piece's parity was kept in scratch)
+        uint32_t off0[4], off1[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if constexpr (GRP == 0) {
+                const int row = cp_row[j];
+                off0[j] = m0 + row < args.M
+                              ? (uint32_t)(row * args.lda * 2 + (cp_chunk[j] << 4))
+                              : kOutOfRange;
+                off1[j] = m0 + row + 128 < args.M
+                              ? (uint32_t)((row + 128) * args.lda * 2 + (cp_chunk[j] << 4))
+                              : kOutOfRange;
+            } else {
+                off0[j] = n0 + cp_chunk[j] * 8 < args.N
+                              ? (uint32_t)(cp_row[j] * args.ldb * 2 + (cp_chunk[j] << 4))
+                              : kOutOfRange;
+                off1[j] = kOutOfRange;
+            }
+        }
+
+        // Copy piece hc: group 0 the A row half (hc & 1) of iteration hc >> 1,
+        // group 1 the B stage of half-iteration hc.  Pieces past the item's
+        // end read nothing and zero their (free) buffer.
+        auto copy_piece = [&](int hc) {
+            if constexpr (GRP == 0) {
+                const int ph = hc & 1;
+                const int ka = k_lo + (hc >> 1) * BK;
+                const bool whole = ka + BK <= k_hi;
+                const int left = k_hi - ka;  // k values of this slab inside the item
+                const uint8_t *src =
+                    args.A + ((int64_t)m0 * args.lda + (ka <= ka_last ? ka : ka_last)) * 2;
+                const uint32_t dst = cp_lds + A_BASE + (uint32_t)(((hc >> 1) % SA) * A_SLOT) +
+                                     (uint32_t)(ph * (A_SLOT / 2));
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t off = ph ? off1[j] : off0[j];
+                    copy16(rsrc_words(src), whole || cp_chunk[j] * 8 < left ? off : kOutOfRange,
+                           dst + j * 4096);
+                }
+            } else {
+                const int kb = k_lo + hc * HK;
+                const bool whole = kb + HK <= k_hi;
+                const int left = k_hi - kb;
+                const uint8_t *src =
+                    args.B + ((int64_t)(kb <= kb_last ? kb : kb_last) * args.ldb + n0) * 2;
+                const uint32_t dst = cp_lds + (uint32_t)((hc & (SB - 1)) * B_STAGE);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    copy16(rsrc_words(src),
+                           whole || cp_row[j] < left ? off0[j] : kOutOfRange,
+                           dst + j * 4096);
+            }
+        };
+        // Fragments of half-iteration h: B stage h mod 4, A slot of iteration
+        // h >> 1, A chunks 4..7 of the slab when h is odd
+        auto read_frags = [&](int h) {
+            const uint32_t slot_off = (uint32_t)(((h >> 1) % SA) * A_SLOT);
+            const uint32_t stage_off = (uint32_t)((h & (SB - 1)) * B_STAGE);
+            const uint32_t a_x = a_lane ^ ((uint32_t)(h & 1) << 6);
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    fa[st][mt] = read_a(slot_off, a_x, st, mt);
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+                    fb[st][nt] = read_b(stage_off, st, nt);
+            }
+        };
+        auto multiply = [&]() {
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+                for (int j = 0; j < MT * NT; ++j)
+                    mfma_step<DT>(acc[j / NT][j % NT], fb[st][j % NT], fa[st][j / NT]);
+        };
+        // End of a phase: at most two copy batches of this wave in flight
+        // (in-order completion), then the workgroup barrier; the scheduler
+        // keeps everything on its side of it.
+        auto phase_end = [&]() {
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vmcnt<8>();
+            barrier_only();
+            __builtin_amdgcn_sched_barrier(0);
+        };
+
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                acc[mt][nt] = f32x16{};
+
+        // the previous item's copies are drained (below) and its LDS reads done
+        barrier_only();
+        copy_piece(0);
+        copy_piece(1);
+        copy_piece(2);
+        phase_end();
+        if constexpr (GRP == 0) {  // group 0 reads h = 0 and copies piece 3
+            copy_piece(3);
+            read_frags(0);
+        }
+        phase_end();
+
+        // half-iteration h: phases 2h and 2h + 1
+        for (int h = 0; h < n; ++h) {
+            if constexpr (GRP == 0) {
+                multiply();
+                phase_end();
+                if (h + 1 < n) {
+                    copy_piece(h + 4);
+                    read_frags(h + 1);
+                }
+                phase_end();
+            } else {
+                copy_piece(h + 3);
+                read_frags(h);
+                phase_end();
+                multiply();
+                phase_end();
+            }
+        }
+        wait_vmcnt<0>();  // zero-fill copies past the end have landed
+
+        finish_tile<256, 256, MT, NT>(acc, args, w, p, m0, n0, wave, lane, GRP * Cfg::WTM,
+                                      q * Cfg::WTN);
+    }
+}
+
+template <int DT>
+__global__ __launch_bounds__(512, 1) void gemm_kernel_pp(KernelArgs args)
+{
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[PairTile<DT, 256, 256, 2, 4>::LDS];
+    const int lane = threadIdx.x & 63;
+    // wave index as a scalar: the group branch is uniform
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int p = logical_wg((int32_t)blockIdx.x, args.P.grid, args.P.xcds);
+    if (wave < 4)
+        gemm_pp_group<DT, 0>(args, lds, wave, lane, p);
+    else
+        gemm_pp_group<DT, 1>(args, lds, wave - 4, lane, p);
+    if (args.split_fixup == 1)
+        reduce_split_tiles<256, 256, 2, 4>(args, p, wave, lane);
+}
+
+template <int DT>
+static int launch_gemm_pp(const KernelArgs &args, int grid, hipStream_t stream)
+{
+    hipLaunchKernelGGL((gemm_kernel_pp<DT>), dim3(grid), dim3(512), 0, stream, args);
+    return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
 template <int DT, int BM, int BN, int WM, int WN>
 static int launch_gemm(const KernelArgs &args, int grid, hipStream_t stream)
 {
@@ -1102,6 +1366,11 @@ static int launch_gemm_pair(const KernelArgs &args, int grid, hipStream_t stream
     return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
+// Wave-specialised ping-pong kernel (fp16/bf16, 256x256)
+#define GSK_PP(DT)                                                                               \
+    Variant{DT, 256, 256, 64, 2, 4, 512, (size_t)PairTile<DT, 256, 256, 2, 4>::LDS, 3,              \
+            PairTile<DT, 256, 256, 2, 4>::SB, &launch_gemm_pp<DT>,                                 \
+            (const void *)&gemm_kernel_pp<DT>, &launch_fixup<256, 256, 2, 4, false>, 0}
 // Register-staged kernel (fp32, int8, fp16/bf16 64x64)
 #define GSK_STAGED(DT, BM, BN, WM, WN)                                                           \
     Variant{DT, BM, BN, Tile<DT, BM, BN, WM, WN>::BK, WM, WN, Tile<DT, BM, BN, WM, WN>::NTH,     \
@@ -1131,6 +1400,8 @@ static const Variant kVariants[] = {
     GSK_PAIR(2, 128, 128, 2, 2),
     GSK_PAIR_STREAM(1, 256, 256, 2, 4), GSK_PAIR_STREAM(1, 256, 128, 4, 2),
     GSK_PAIR_STREAM(2, 256, 256, 2, 4), GSK_PAIR_STREAM(2, 256, 128, 4, 2),
+    // fp16 / bf16: wave-specialised ping-pong kernel (GEMM_FLAG_PING_PONG)
+    GSK_PP(1), GSK_PP(2),
     // fp16 / bf16 64x64 tiles (below the ring kernel's smallest tile), fp32, int8:
     // register-staged kernel
     GSK_STAGED(1, 64, 64, 2, 2), GSK_STAGED(2, 64, 64, 2, 2),

@@ -98,10 +98,12 @@ def test_variant_table_is_exported_and_each_entry_selectable():
     names = {0: "f32", 1: "f16", 2: "bf16", 3: "i8"}
     seen = set()
     for v in vs:
-        key = (v["dtype"], v["bm"], v["bn"], v["wave_m"], v["wave_n"], v["stream_copies"])
+        key = (v["dtype"], v["bm"], v["bn"], v["wave_m"], v["wave_n"], v["stream_copies"],
+               v["kind"])
         assert key not in seen, f"two table entries for {key}"
         seen.add(key)
-        flags = gsk.FLAG_STREAM_COPIES if v["stream_copies"] else 0
+        flags = (gsk.FLAG_STREAM_COPIES if v["stream_copies"] else 0) | \
+            (gsk.FLAG_PING_PONG if v["kind"] == 3 else 0)
         plan = gsk.plan_for_device(1000, 1000, 1000, names[v["dtype"]], "dp", bm=v["bm"],
                                    bn=v["bn"], wave_m=v["wave_m"], wave_n=v["wave_n"],
                                    stages=v["stages"], flags=flags)

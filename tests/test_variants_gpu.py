@@ -64,6 +64,8 @@ def _tiles(v):
              stages=v["stages"])
     if v["stream_copies"]:
         t["flags"] = gsk.FLAG_STREAM_COPIES
+    if v["kind"] == 3:
+        t["flags"] = t.get("flags", 0) | gsk.FLAG_PING_PONG
     return t
 
 
@@ -116,3 +118,26 @@ def test_variant_split_long_k(v):
                 plan, ws, c = run_gemm(da, db, M, N, K, dtype, sched, grid=g, **t)
                 assert plan.info["max_pieces"] >= 2, plan.describe()
                 _check(plan, c, idx, ref, scale, dtype, v)
+
+
+PP_SHAPES = [(257, 203, 701), (512, 768, 1000), (300, 520, 4096), (1024, 1024, 2112)]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("shape", PP_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_ping_pong_matches_the_ring_kernel_bitwise(shape, dtype):
+    # the wave-specialised kernel runs the same MFMAs in the same order per
+    # element as the ring kernel with the same tile: identical bits in every
+    # schedule (split tiles included), and within the oracle's bound
+    M, N, K = shape
+    a, b = inputs.operands(M, N, K, dtype, "normal", seed=M ^ N ^ K)
+    ref, scale = oracle.gemm(a, b, dtype)
+    da, db = to_device(a, dtype), to_device(b, dtype)
+    for sched in SCHEDULES:
+        for g in ((0, 37) if sched in ("streamk", "hybrid") else (0,)):
+            _, _, c_ring = run_gemm(da, db, M, N, K, dtype, sched, grid=g, bm=256, bn=256)
+            plan, _, c_pp = run_gemm(da, db, M, N, K, dtype, sched, grid=g, bm=256, bn=256,
+                                     flags=gsk.FLAG_PING_PONG)
+            assert plan.info["kernel_kind"] == 3
+            assert torch.equal(c_ring.view(torch.int32), c_pp.view(torch.int32)), plan.describe()
+            compare(c_pp.cpu().numpy(), ref, scale, dtype, what=plan.describe())
