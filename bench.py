@@ -487,6 +487,12 @@ def main():
     ap.add_argument("--c-dtype", choices=("f32", "input"), default="f32",
                     help="C as fp32 (the workloads' output type, the default) or in the input "
                          "dtype (the pages' fp16 output; fp16/bf16 workloads only)")
+    ap.add_argument("--order", choices=("tuned", "bands", "hilbert", "rows"), default="tuned",
+                    help="tile order of every plan: the tuned one, GROUP_M bands, the Hilbert "
+                         "curve, or row-major")
+    ap.add_argument("--kernel", choices=("tuned", "ring", "pingpong"), default="tuned",
+                    help="fp16/bf16 256x256 kernel: the tuned one, the ring kernel, or the "
+                         "wave-specialised ping-pong kernel")
     ap.add_argument("--configs", choices=("all", "standard", "none"), default="all",
                     help="after the --workload line, also measure the other standard workloads "
                          "(standard), plus the 16 irregular shapes (all, the default), or none")
@@ -617,6 +623,30 @@ CONFIG_WORKLOADS = ["fp16_4096", "fp32_256", "fp16_1536x1536x8192", "bf16_512x51
 HBM_BOUND = {"bf16_512x512x65536"}
 
 
+def launch_tiles(name, schedule, dtype, args):
+    """The tuned launch configuration of one workload and schedule, with the
+    tile order and 256x256 kernel family the command line asks for."""
+    import persistent_stream_tiling_amd as gsk
+    from persistent_stream_tiling_amd import tuning
+    t = tuning.bench_tiles(name, schedule, dtype)
+    flags = t.get("flags", 0)
+    order, kernel = getattr(args, "order", "tuned"), getattr(args, "kernel", "tuned")
+    if order == "hilbert":
+        flags |= gsk.FLAG_HILBERT_ORDER
+    elif order in ("bands", "rows"):
+        flags &= ~gsk.FLAG_HILBERT_ORDER
+        t["group_m"] = t.get("group_m", 0) if order == "bands" else -1
+    if kernel != "tuned" and (t.get("bm"), t.get("bn")) == (256, 256) and dtype in ("f16", "bf16"):
+        if kernel == "pingpong":
+            flags = (flags | gsk.FLAG_PING_PONG) & ~gsk.FLAG_STREAM_COPIES
+            t.pop("wave_m", None)
+            t.pop("wave_n", None)
+        else:
+            flags &= ~gsk.FLAG_PING_PONG
+    t["flags"] = flags
+    return t
+
+
 def measure_workload(name, args, flush, threads, failures, schedules=SCHEDULES, oracle=True):
     """Time every schedule of one workload in its tuned launch configuration,
     check each schedule's output against the oracle, and return the record."""
@@ -642,7 +672,7 @@ def measure_workload(name, args, flush, threads, failures, schedules=SCHEDULES, 
     results = {}
     worst_all, checked = 0.0, 0
     for sched in schedules:
-        tiles = tuning.bench_tiles(name, sched, dt)
+        tiles = launch_tiles(name, sched, dt, args)
         if c_half:
             tiles["flags"] = tiles.get("flags", 0) | gsk.FLAG_C_INPUT_DTYPE
         plan = gsk.GemmPlan(M, N, K, dt, sched, **tiles)
@@ -712,7 +742,7 @@ def traffic_run(args):
     src = torch.ones(COPY_BYTES, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
     plan = gsk.GemmPlan(M, N, K, dt, args.traffic_run,
-                        **tuning.bench_tiles(args.workload, args.traffic_run, dt))
+                        **launch_tiles(args.workload, args.traffic_run, dt, args))
     ws = plan.new_workspace()
     for _ in range(3):
         flush.zero_()

@@ -123,7 +123,14 @@ enum {
      * in L2.  Built for 256x256 (2x4 waves) and 256x128 (4x2) tiles; other
      * tiles with this flag have no kernel. */
     GEMM_FLAG_STREAM_COPIES = 1u << 9,
-    /* Bit 10 is reserved. */
+    /* Tile order along a Hilbert curve over the tile grid instead of
+     * GROUP_M bands (the "Inside NVIDIA GPUs: Anatomy of high performance
+     * matmul kernels" page lists Hilbert curves among tile scheduling
+     * policies): tile ids follow the classic curve on the power-of-two square
+     * enclosing the grid, counting only tiles inside the grid, so runs of
+     * consecutive ids (what one die and one wave of workgroups hold) cover
+     * compact blocks of tiles on any grid shape.  group_m is ignored. */
+    GEMM_FLAG_HILBERT_ORDER = 1u << 10,
     /* fp16/bf16, 256x256 tiles: the wave-specialised ping-pong kernel
      * (kernel_kind 3).  Its eight waves form two groups, one wave of each on
      * every SIMD, that take turns: one group runs a burst of MFMAs on
@@ -145,7 +152,8 @@ typedef struct {
     int32_t grid;     /* g: workgroups of the persistent / Stream-K launch;
                          0 = number of CUs (issue #1393 uses the SM count) */
     int32_t group_m;  /* tile-order group height (issue #1393 GROUP_M);
-                         0 = 8, < 0 = plain row-major tile order */
+                         0 = 8, < 0 = plain row-major tile order (see also
+                         GEMM_FLAG_HILBERT_ORDER) */
     uint32_t flags;   /* GEMM_FLAG_* */
     int32_t wave_m, wave_n; /* waves per workgroup along M and N (each wave
                                computes a (bm/wave_m) x (bn/wave_n) block);

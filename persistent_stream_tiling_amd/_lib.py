@@ -15,6 +15,7 @@ FLAG_C_INPUT_DTYPE = 1 << 6
 FLAG_DEBUG_DROP_SIGNAL = 1 << 7
 FLAG_FIXUP_TWO_KERNEL = 1 << 8
 FLAG_STREAM_COPIES = 1 << 9
+FLAG_HILBERT_ORDER = 1 << 10
 FLAG_PING_PONG = 1 << 11
 ROLE_FULL, ROLE_CONTRIB, ROLE_OWNER = 0, 1, 2
 NOALLOC_MAX_WORKSPACE = 80 << 20  # GEMM_NOALLOC_MAX_WORKSPACE

@@ -268,6 +268,7 @@ gemm_plan *create(int64_t M, int64_t N, int64_t K, gemm_dtype dtype, gemm_schedu
     P.T = (int32_t)T;
     P.ipt = (int32_t)ipt;
     P.group_m = p->group_m;
+    P.hilbert = (t.flags & GEMM_FLAG_HILBERT_ORDER) ? 1 : 0;
     P.xcds = p->xcds;
     const int32_t g = t.grid > 0 ? t.grid : dev.cus;
     int64_t T_sk = 0;
@@ -501,8 +502,15 @@ int gemm_plan_describe(const gemm_plan *p, char *buf, size_t len)
         set_error("NULL plan");
         return -1;
     }
+    char order[32];
+    if (p->P.hilbert)
+        snprintf(order, sizeof order, "hilbert");
+    else if (p->group_m > 0)
+        snprintf(order, sizeof order, "bands%d", p->group_m);
+    else
+        snprintf(order, sizeof order, "rows");
     return snprintf(buf, buf ? len : 0,
-                    "M,N,K=%lld,%lld,%lld %s C=%s %s tile=%dx%dx%d waves=%dx%d %s%d group_m=%d | tiles %dx%d=%d "
+                    "M,N,K=%lld,%lld,%lld %s C=%s %s tile=%dx%dx%d waves=%dx%d %s%d order=%s | tiles %dx%d=%d "
                     "ipt=%d | T_sk=%d T_dp=%d I_sk=%lld g=%d q=%d r=%d | grid=%d x %d threads, "
                     "lds=%zu B, capacity=%d wg, xcds=%d | fixup=%s pieces<=%d | pack A=%d B=%d | "
                     "workspace=%zu B",
@@ -513,7 +521,8 @@ int gemm_plan_describe(const gemm_plan *p, char *buf, size_t len)
                                                          : GEMM_F32),
                     sched_name(p->schedule), p->bm, p->bn, p->bk, p->variant->wave_m,
                     p->variant->wave_n, p->variant->kind == 3 ? "pingpong" : p->variant->kind == 2 ? "ring" : "staged",
-                    p->variant->kind ? p->variant->stages : 2, p->group_m, p->P.tiles_m,
+                    p->variant->kind ? p->variant->stages : 2,
+                    order, p->P.tiles_m,
                     p->P.tiles_n, p->P.T, p->P.ipt, p->P.T_sk, p->P.T - p->P.T_sk,
                     (long long)p->iters_sk, p->P.g, p->P.q, p->P.r, p->P.grid,
                     p->variant->threads, p->variant->lds_bytes, p->wg_capacity, p->xcds,

@@ -37,6 +37,7 @@ struct Partition {
     int32_t xcds;     // dies that hardware workgroup ids are dealt to in turn
     int32_t k_aligned; // walk a Stream-K range as whole tiles, head piece, tail
                        // piece (see work_next); only with the split fixup
+    int32_t hilbert;   // tile order: 1 = Hilbert curve over the tile grid
 };
 
 GSK_HD int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
@@ -59,12 +60,79 @@ GSK_HD int32_t sk_wg_of_iter(const Partition &P, int64_t it)
     return (int32_t)(P.r + (it - long_part) / P.q);  // q > 0 whenever this is reached
 }
 
-// Output tile (tile_m, tile_n) of tile id t.  With group_m > 0 the ids walk
-// down a band of group_m tile rows before moving one tile column right, so
-// tiles that run at the same time share A row panels and B column panels in
-// cache (issue #1393's GROUP_M re-ordering "for better L2 performance").
+// Tile (x, y) of the t-th cell of the grid [0, gm) x [0, gn) in Hilbert-curve
+// order ("Inside NVIDIA GPUs: Anatomy of high performance matmul kernels"
+// page: Hilbert curves as a tile scheduling policy).  The curve is the classic
+// one on the power-of-two square of side >= max(gm, gn), restricted to the
+// cells inside the grid: t counts in-grid cells only, so the map is a
+// bijection on [0, gm * gn) for any grid, and on a power-of-two square grid
+// it is the textbook curve.
+//
+// Top-down walk: the current square is mapped to the grid by an affine map
+// x = ox + a*u + b*v, y = oy + c*u + d*v of its local (u, v) (a, b, c, d in
+// {-1, 0, 1}).  Its four quadrants are visited in the curve's order
+// (0,0) (0,h) (h,h) (h,0) (local, h the half side), the first transposed and
+// the last anti-transposed; the walk counts each quadrant's cells inside the
+// grid, enters the one holding cell t, and composes its map.
+GSK_HD void hilbert_coords(int32_t gm, int32_t gn, int32_t t, int32_t *x, int32_t *y)
+{
+    int32_t side = 1;
+    while (side < gm || side < gn)
+        side *= 2;
+    int32_t ox = 0, oy = 0, a = 1, b = 0, c = 0, d = 1;
+    for (int32_t s = side; s > 1; s /= 2) {
+        const int32_t h = s / 2;
+        for (int32_t q = 0; q < 4; ++q) {
+            // quadrant q: local offset (p, r) and map (u, v) = (p + e*u' + f*v', r + g*u' + k*v')
+            int32_t p, r, e, f, g, k;
+            if (q == 0) {
+                p = 0; r = 0; e = 0; f = 1; g = 1; k = 0;
+            } else if (q == 1) {
+                p = 0; r = h; e = 1; f = 0; g = 0; k = 1;
+            } else if (q == 2) {
+                p = h; r = h; e = 1; f = 0; g = 0; k = 1;
+            } else {
+                p = 2 * h - 1; r = h - 1; e = 0; f = -1; g = -1; k = 0;
+            }
+            // the quadrant's cells in grid coordinates: the image of the
+            // local cells [qu, qu + h) x [qv, qv + h) of the current square
+            const int32_t qu = q >= 2 ? h : 0, qv = (q == 1 || q == 2) ? h : 0;
+            const int32_t x0 = ox + a * qu + b * qv, x1 = ox + a * (qu + h - 1) + b * (qv + h - 1);
+            const int32_t y0 = oy + c * qu + d * qv, y1 = oy + c * (qu + h - 1) + d * (qv + h - 1);
+            const int32_t xl = x0 < x1 ? x0 : x1, xh = (x0 < x1 ? x1 : x0) + 1;
+            const int32_t yl = y0 < y1 ? y0 : y1, yh = (y0 < y1 ? y1 : y0) + 1;
+            const int32_t nx = (xh < gm ? xh : gm) - (xl > 0 ? xl : 0);
+            const int32_t ny = (yh < gn ? yh : gn) - (yl > 0 ? yl : 0);
+            const int32_t cells = nx > 0 && ny > 0 ? nx * ny : 0;
+            if (t < cells || q == 3) {
+                const int32_t ox2 = ox + a * p + b * r, oy2 = oy + c * p + d * r;
+                const int32_t a2 = a * e + b * g, b2 = a * f + b * k;
+                const int32_t c2 = c * e + d * g, d2 = c * f + d * k;
+                ox = ox2; oy = oy2; a = a2; b = b2; c = c2; d = d2;
+                break;
+            }
+            t -= cells;
+        }
+    }
+    *x = ox;
+    *y = oy;
+}
+
+// Output tile (tile_m, tile_n) of tile id t.
+//  - hilbert: the Hilbert-curve order above over the tiles_m x tiles_n grid;
+//  - group_m > 0: issue #1393's GROUP_M re-ordering "for better L2
+//    performance" (the final revision's swizzle_tile): ids walk down a band of
+//    group_m tile rows before moving one tile column right, so tiles that run
+//    at the same time share A row panels and B column panels in cache; in a
+//    shorter last band the row is tile_id mod (band height) of the global id,
+//    as on the page;
+//  - otherwise row-major.
 GSK_HD void tile_coords(const Partition &P, int32_t t, int32_t *tm, int32_t *tn)
 {
+    if (P.hilbert) {
+        hilbert_coords(P.tiles_m, P.tiles_n, t, tm, tn);
+        return;
+    }
     if (P.group_m <= 0) {
         *tm = t / P.tiles_n;
         *tn = t - (t / P.tiles_n) * P.tiles_n;
@@ -77,7 +145,7 @@ GSK_HD void tile_coords(const Partition &P, int32_t t, int32_t *tm, int32_t *tn)
     if (rows > P.group_m)
         rows = P.group_m;
     int32_t in_band = t - b * band;
-    *tm = first_row + in_band % rows;
+    *tm = first_row + t % rows;
     *tn = in_band / rows;
 }
 

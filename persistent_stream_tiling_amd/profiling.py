@@ -155,6 +155,28 @@ def counters_summary(csv_dir, workload, schedules, warmup, steps, flops):
     return out
 
 
+def pmc_summary(csv_dir, schedules, warmup, steps):
+    """Per schedule: the mean over the timed GEMM dispatches of every counter
+    in a --pmc run of bench.py (one run of warm-up + timed steps per schedule,
+    in order), and the dispatch duration."""
+    rows = list(csv.DictReader(open(_find(csv_dir, "counter_collection.csv"))))
+    disp = {}
+    for r in rows:
+        if not _is_gemm(r["Kernel_Name"]):
+            continue
+        d = disp.setdefault(int(r["Dispatch_Id"]), {"us": (int(r["End_Timestamp"]) -
+                                                           int(r["Start_Timestamp"])) / 1e3})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    seq = [disp[k] for k in sorted(disp)]
+    per = warmup + steps
+    out = {}
+    for i, sched in enumerate(schedules):
+        timed = seq[i * per:(i + 1) * per][warmup:]
+        if timed:
+            out[sched] = {k: statistics.mean(d.get(k, 0.0) for d in timed) for k in timed[0]}
+    return out
+
+
 def counters_table(records, cmd):
     lines = [f"# rocprofv3 counters per workload and schedule", "",
              f"Command per workload: `{cmd}`", "",
@@ -269,10 +291,45 @@ def main():
     c.add_argument("--steps", type=int, default=3)
     c.add_argument("--out", required=True)
     c.add_argument("--cmd", required=True)
+    m = sub.add_parser("pmc", help="counter means per (label, workload, schedule) table")
+    m.add_argument("--csv", required=True, nargs="+", help="one --pmc run directory each")
+    m.add_argument("--label", required=True, nargs="+")
+    m.add_argument("--workload", required=True, nargs="+")
+    m.add_argument("--schedules", default="dp,persistent,streamk,hybrid")
+    m.add_argument("--warmup", type=int, default=1)
+    m.add_argument("--steps", type=int, default=3)
+    m.add_argument("--title", required=True)
+    m.add_argument("--out", required=True)
+    m.add_argument("--cmd", required=True, nargs="+", help="the commands that made the runs")
     r = sub.add_parser("resources")
     r.add_argument("--out", required=True)
     a = ap.parse_args()
-    if a.cmd_name == "resources":
+    if a.cmd_name == "pmc":
+        groups = {}
+        for d, lab, w in zip(a.csv, a.label, a.workload):
+            for sched, vals in pmc_summary(d, a.schedules.split(","), a.warmup, a.steps).items():
+                groups.setdefault((w, sched), {})[lab] = vals
+        counters = sorted({k for g in groups.values() for v in g.values() for k in v} - {"us"})
+        lines = [f"# {a.title}", "", "Commands (one rocprofv3 run per line; counters summed over "
+                 "dies and channels per dispatch, then averaged over the timed dispatches):", ""]
+        lines += [f"    {c}" for c in a.cmd]
+        lines += ["", f"Kernel source hash: {source_hash()}.", "",
+                  "| workload | schedule | run | us | " + " | ".join(counters) +
+                  (" | L2 hit rate |" if {"TCC_HIT_sum", "TCC_MISS_sum"} <= set(counters) else " |"),
+                  "|---" * (4 + len(counters) + ({"TCC_HIT_sum", "TCC_MISS_sum"} <= set(counters)))
+                  + "|"]
+        for (w, sched), labs in groups.items():
+            for lab, v in labs.items():
+                row = f"| {w} | {sched} | {lab} | {v['us']:.1f} | " + \
+                      " | ".join(f"{v.get(c, 0.0):.4g}" for c in counters)
+                if {"TCC_HIT_sum", "TCC_MISS_sum"} <= set(counters):
+                    h, mi = v.get("TCC_HIT_sum", 0.0), v.get("TCC_MISS_sum", 0.0)
+                    row += f" | {100 * h / max(h + mi, 1.0):.1f}%"
+                lines.append(row + " |")
+        text = "\n".join(lines) + "\n"
+        open(a.out, "w").write(text)
+        print(text)
+    elif a.cmd_name == "resources":
         print(kernel_resources(a.out, "python -m persistent_stream_tiling_amd.profiling "
                                       "resources --out " + a.out))
     elif a.cmd_name == "counters":

@@ -173,7 +173,7 @@ int main(int argc, char **argv)
     Header h;
     if (std::fread(&h, sizeof h, 1, f) != 1)
         return 2;
-    Partition P;
+    Partition P = {};
     P.tiles_m = h.tiles_m;
     P.tiles_n = h.tiles_n;
     P.T = h.T;

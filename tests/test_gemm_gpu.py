@@ -401,3 +401,24 @@ def test_workload_parity(name):
 @pytest.mark.parametrize("name", sorted(inputs.irregular_workloads()))
 def test_irregular_sweep_parity(name):
     check_workload(name, 8192, edges=True)
+
+
+@pytest.mark.parametrize("schedule", SCHEDULES)
+def test_hilbert_tile_order(schedule):
+    # the Hilbert order changes which tile a workgroup computes, never the
+    # result's tolerance: ragged, repacked shapes at several tile sizes and
+    # grids, against the oracle element by element
+    import persistent_stream_tiling_amd as gsk
+    for dtype, shape in (("f16", (257, 203, 701)), ("bf16", (1000, 777, 1500)),
+                         ("f16", (320, 384, 512))):
+        M, N, K = shape
+        a, b, ref, scale = small_inputs(M, N, K, dtype)
+        da, db = to_device(a, dtype), to_device(b, dtype)
+        for tiles in (dict(bm=64, bn=64), dict(bm=128, bn=128), dict(bm=256, bn=256),
+                      dict(bm=256, bn=256, flags=gsk.FLAG_PING_PONG)):
+            for g in ([0, 37] if schedule in ("streamk", "hybrid") else [0]):
+                t = dict(tiles)
+                t["flags"] = t.get("flags", 0) | gsk.FLAG_HILBERT_ORDER
+                plan, ws, c = run_gemm(da, db, M, N, K, dtype, schedule, grid=g, **t)
+                assert "order=hilbert" in plan.describe()
+                compare(c.cpu().numpy(), ref, scale, dtype, what=plan.describe())

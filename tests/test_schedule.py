@@ -376,3 +376,76 @@ def test_stream_copies_only_where_built():
                                flags=f).info["kernel_kind"] == 2
     with pytest.raises(ValueError, match="no kernel"):
         gsk.plan_for_device(512, 512, 4096, "bf16", "dp", bm=128, bn=128, flags=f)
+
+
+def _page_swizzle(t, grid_m, grid_n, group_m):
+    # the GROUP_M re-ordering of issue #1393's final revision (swizzle_tile),
+    # restated: bands of group_m tile rows; the row is the global tile id mod
+    # the band's height, the column the id within the band over that height
+    width = group_m * grid_n
+    group_id = t // width
+    group_size = min(grid_m - group_id * group_m, group_m)
+    return group_id * group_m + t % group_size, (t % width) // group_size
+
+
+@pytest.mark.parametrize("tiles_m,tiles_n,group_m", [(11, 2, 8), (10, 3, 8), (13, 5, 4), (7, 7, 3),
+                                                     (32, 16, 8), (5, 9, 8)])
+def test_band_order_is_the_pages_swizzle(tiles_m, tiles_n, group_m):
+    # on a short last band whose width is not a multiple of its height the
+    # page's row index is a rotation of the within-band one
+    p = plan(tiles_m * 64, tiles_n * 64, 64, "f16", "dp", bm=64, bn=64, group_m=group_m)
+    assert (p.info["tiles_m"], p.info["tiles_n"]) == (tiles_m, tiles_n)
+    T = tiles_m * tiles_n
+    assert [p.tile_coords(t) for t in range(T)] == \
+        [_page_swizzle(t, tiles_m, tiles_n, group_m) for t in range(T)]
+
+
+def _hilbert_d2xy(order, d):
+    # the textbook Hilbert index -> (x, y) map on a 2^order square (iterative,
+    # bottom-up: rotate, then offset the quadrant)
+    x = y = 0
+    s, t = 1, d
+    while s < (1 << order):
+        rx = 1 & (t // 2)
+        ry = 1 & (t ^ rx)
+        if ry == 0:
+            if rx == 1:
+                x, y = s - 1 - x, s - 1 - y
+            x, y = y, x
+        x += s * rx
+        y += s * ry
+        t //= 4
+        s *= 2
+    return x, y
+
+
+@pytest.mark.parametrize("tiles_m,tiles_n", [(1, 1), (2, 2), (4, 4), (8, 8), (16, 16), (3, 5),
+                                             (7, 1), (1, 9), (11, 6), (17, 32), (32, 112), (23, 22)])
+def test_hilbert_order(tiles_m, tiles_n):
+    p = plan(tiles_m * 64, tiles_n * 64, 64, "f16", "dp", bm=64, bn=64,
+             flags=gsk.FLAG_HILBERT_ORDER)
+    assert "order=hilbert" in p.describe()
+    T = tiles_m * tiles_n
+    coords = [p.tile_coords(t) for t in range(T)]
+    # the textbook curve on the enclosing power-of-two square, cells outside
+    # the grid skipped (brute force over the whole square)
+    order = max(tiles_m - 1, tiles_n - 1, 0).bit_length()
+    want = [xy for xy in (_hilbert_d2xy(order, d) for d in range(4 ** order))
+            if xy[0] < tiles_m and xy[1] < tiles_n]
+    assert coords == want
+    # on a power-of-two square each step moves to a neighbouring tile
+    if tiles_m == tiles_n and tiles_m & (tiles_m - 1) == 0:
+        assert all(abs(a[0] - b[0]) + abs(a[1] - b[1]) == 1 for a, b in zip(coords, coords[1:]))
+    # every schedule still covers each (tile, k-iteration) pair exactly once
+    for sched in ("streamk", "hybrid"):
+        check_plan(plan(tiles_m * 64, tiles_n * 64, 1000, "f16", sched, bm=64, bn=64, grid=37,
+                        flags=gsk.FLAG_HILBERT_ORDER))
+
+
+def test_hilbert_textbook_pins():
+    # d2xy pinned to hand-drawn curves: order 1 is the U (0,0) (0,1) (1,1) (1,0);
+    # order 2 starts with a transposed U and ends with an anti-transposed one
+    assert [_hilbert_d2xy(1, d) for d in range(4)] == [(0, 0), (0, 1), (1, 1), (1, 0)]
+    assert [_hilbert_d2xy(2, d) for d in range(16)] == [
+        (0, 0), (1, 0), (1, 1), (0, 1), (0, 2), (0, 3), (1, 3), (1, 2),
+        (2, 2), (2, 3), (3, 3), (3, 2), (3, 1), (2, 1), (2, 0), (3, 0)]
