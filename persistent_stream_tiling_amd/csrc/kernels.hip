@@ -1419,13 +1419,14 @@ const Variant *variants(int *count)
 
 // dst (rows x ld_dst) = src (rows x cols, leading dimension ld_src), zero
 // padded on the right; ld_dst * sizeof(T) is a multiple of 16 bytes and dst
-// is 16-byte aligned.  A workgroup fills one 4 KiB span of a destination row:
-// its threads read the span's source elements with consecutive lanes on
-// consecutive elements (whole cache lines per wave, whatever the alignment of
-// the source row), stage them in LDS, and write the span back with one
-// 16-byte store per thread.  Rows are strided over gridDim.y; no division.
+// is 16-byte aligned.  One thread per 16-byte chunk of a destination row: a
+// chunk that lies wholly inside the source row is one 16-byte load from the
+// (only element-aligned) source address (gfx950 code objects run with
+// unaligned global access enabled, and the compiler emits such loads itself
+// for under-aligned data), a row's last, partial chunk is read element by
+// element and zero padded, so no load reaches past its row.  Rows are
+// strided over gridDim.y; no division.
 constexpr int kPackThreads = 256;
-constexpr int kPackSpan = kPackThreads * 16;  // destination bytes per workgroup and row
 
 template <typename T>
 __global__ __launch_bounds__(kPackThreads) void pack_kernel(const T *__restrict__ src,
@@ -1433,23 +1434,23 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const T *__restrict_
                                                             int64_t cols, int64_t ld_src,
                                                             int64_t ld_dst)
 {
-    constexpr int V = 16 / (int)sizeof(T);          // elements per 16-byte chunk
-    constexpr int PER = kPackSpan / (int)sizeof(T); // elements per span
-    __shared__ __attribute__((aligned(16))) T span[PER];
-    const int tid = threadIdx.x;
-    const int64_t c0 = (int64_t)blockIdx.x * PER;   // first column of this span
-    const int64_t mine = c0 + (int64_t)tid * V;     // first column this thread stores
+    constexpr int V = 16 / (int)sizeof(T);  // elements per 16-byte chunk
+    const int64_t c0 = ((int64_t)blockIdx.x * kPackThreads + threadIdx.x) * V;
+    if (c0 >= ld_dst)
+        return;
     for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
-        const T *s = src + r * ld_src;
+        const T *s = src + r * ld_src + c0;
+        u32x4 v;
+        if (c0 + V <= cols) {
+            __builtin_memcpy(&v, s, 16);
+        } else {
+            T e[V];
 #pragma unroll
-        for (int j = 0; j < V; ++j) {
-            const int64_t col = c0 + j * kPackThreads + tid;
-            span[j * kPackThreads + tid] = col < cols ? s[col] : T(0);
+            for (int i = 0; i < V; ++i)
+                e[i] = c0 + i < cols ? s[i] : T(0);
+            __builtin_memcpy(&v, e, 16);
         }
-        __syncthreads();
-        if (mine < ld_dst)
-            *(u32x4 *)(dst + r * ld_dst + mine) = *(const u32x4 *)(span + tid * V);
-        __syncthreads();  // the span is refilled for the next row
+        *(u32x4 *)(dst + r * ld_dst + c0) = v;
     }
 }
 
@@ -1457,8 +1458,9 @@ template <typename T>
 static void launch_pack_t(const void *src, void *dst, int64_t rows, int64_t cols, int64_t ld_src,
                           int64_t ld_dst, hipStream_t stream)
 {
-    constexpr int64_t PER = kPackSpan / sizeof(T);
+    constexpr int64_t PER = (int64_t)kPackThreads * (16 / sizeof(T));  // elements per workgroup
     const int64_t spans = (ld_dst + PER - 1) / PER;
+    // enough rows per launch to keep every CU busy, each workgroup then loops
     const int64_t ys = rows < 32768 ? rows : 32768;
     hipLaunchKernelGGL(pack_kernel<T>, dim3((unsigned)spans, (unsigned)ys), dim3(kPackThreads), 0,
                        stream, (const T *)src, (T *)dst, rows, cols, ld_src, ld_dst);
