@@ -638,11 +638,11 @@ def launch_tiles(name, schedule, dtype, args):
         t["group_m"] = t.get("group_m", 0) if order == "bands" else -1
     if kernel != "tuned" and (t.get("bm"), t.get("bn")) == (256, 256) and dtype in ("f16", "bf16"):
         if kernel == "pingpong":
-            flags = (flags | gsk.FLAG_PING_PONG) & ~gsk.FLAG_STREAM_COPIES
+            flags = (flags | gsk.FLAG_PING_PONG) & ~(gsk.FLAG_STREAM_COPIES | gsk.FLAG_RING_KERNEL)
             t.pop("wave_m", None)
             t.pop("wave_n", None)
         else:
-            flags &= ~gsk.FLAG_PING_PONG
+            flags = (flags | gsk.FLAG_RING_KERNEL) & ~gsk.FLAG_PING_PONG
     t["flags"] = flags
     return t
 

@@ -132,15 +132,21 @@ enum {
      * compact blocks of tiles on any grid shape.  group_m is ignored. */
     GEMM_FLAG_HILBERT_ORDER = 1u << 10,
     /* fp16/bf16, 256x256 tiles: the wave-specialised ping-pong kernel
-     * (kernel_kind 3).  Its eight waves form two groups, one wave of each on
-     * every SIMD, that take turns: one group runs a burst of MFMAs on
-     * fragments already in registers while the other issues its share of the
-     * global -> LDS copies and reads its next fragments ("naive vs
-     * persistent matmul" post on the Hugging Face activity feed page: warp
-     * specialization and ping-pong scheduling, there for NVIDIA's warp groups).
-     * Same results as the default kernel with the same tile (the same MFMAs
-     * in the same order per element). */
-    GEMM_FLAG_PING_PONG = 1u << 11
+     * (kernel_kind 3), the default wherever it is built (256x256 tiles in
+     * the 2x4 wave layout, without GEMM_FLAG_STREAM_COPIES); this flag asks
+     * for it explicitly and refuses tiles without it.  Its eight waves form
+     * two groups, one wave of each on every SIMD, that take turns: one group
+     * runs a burst of MFMAs on fragments already in registers while the other
+     * issues its share of the global -> LDS copies and reads its next
+     * fragments ("naive vs persistent matmul" post on the Hugging Face
+     * activity feed page: warp specialization and ping-pong scheduling, there
+     * for NVIDIA's warp groups).  Same results as the ring kernel with the
+     * same tile (the same MFMAs in the same order per element). */
+    GEMM_FLAG_PING_PONG = 1u << 11,
+    /* fp16/bf16: never the ping-pong kernel; 256x256 tiles then run the ring
+     * kernel (kernel_kind 2), which is otherwise the default for the other
+     * tiles (for comparing the two). */
+    GEMM_FLAG_RING_KERNEL = 1u << 12
 };
 
 /* Tile and schedule knobs.  Every field 0 means "default". */

@@ -35,5 +35,24 @@ def build(out=LIB, verbose=False, extra=()):
     return out
 
 
+PROBES = os.path.join(PKG, "probes")
+
+
+def build_probes(verbose=False):
+    """Compile the hardware-ceiling probe program (probes/ceilings.hip), a
+    measurement tool kept out of the library; returns its path."""
+    src = os.path.join(PROBES, "ceilings.hip")
+    out = os.path.join(PROBES, "ceilings")
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", src, "-o", out + ".tmp"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + res.stderr[-8000:])
+    if verbose:
+        print(res.stderr)
+    os.replace(out + ".tmp", out)
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose=False))

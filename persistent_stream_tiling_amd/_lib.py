@@ -17,6 +17,7 @@ FLAG_FIXUP_TWO_KERNEL = 1 << 8
 FLAG_STREAM_COPIES = 1 << 9
 FLAG_HILBERT_ORDER = 1 << 10
 FLAG_PING_PONG = 1 << 11
+FLAG_RING_KERNEL = 1 << 12
 ROLE_FULL, ROLE_CONTRIB, ROLE_OWNER = 0, 1, 2
 NOALLOC_MAX_WORKSPACE = 80 << 20  # GEMM_NOALLOC_MAX_WORKSPACE
 

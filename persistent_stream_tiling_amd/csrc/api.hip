@@ -109,12 +109,19 @@ const Variant *find_variant(int dtype, const gemm_tiles &t)
     // register-staged one for tiles it does not cover (64x64); fp32 and int8
     // run the register-staged kernel
     const bool staged_only = dtype == GEMM_F32 || dtype == GEMM_I8;
-    const bool ping_pong = (t.flags & GEMM_FLAG_PING_PONG) != 0;
     int n = 0;
     const Variant *v = variants(&n);
-    // kinds in order of preference: 3 (ping-pong, only when asked for), else
-    // 2 (ring) then 0 (staged)
-    const int kinds[3] = {ping_pong ? 3 : (staged_only ? 0 : 2), ping_pong ? -1 : 0, -1};
+    // kinds in order of preference: the ping-pong kernel where one is built
+    // (256x256), then the ring kernel, then the register-staged one;
+    // GEMM_FLAG_PING_PONG asks for the first only, GEMM_FLAG_RING_KERNEL
+    // skips it
+    int kinds[3] = {3, 2, 0};
+    if (staged_only)
+        kinds[0] = 0, kinds[1] = kinds[2] = -1;
+    else if (t.flags & GEMM_FLAG_PING_PONG)
+        kinds[1] = kinds[2] = -1;
+    else if (t.flags & GEMM_FLAG_RING_KERNEL)
+        kinds[0] = 2, kinds[1] = 0, kinds[2] = -1;
     for (int ki = 0; ki < 3 && kinds[ki] >= 0; ++ki)
         for (int i = 0; i < n; ++i)
             if (v[i].dtype == dtype && v[i].bm == t.bm && v[i].bn == t.bn && v[i].kind == kinds[ki] &&
@@ -167,6 +174,10 @@ gemm_plan *create(int64_t M, int64_t N, int64_t K, gemm_dtype dtype, gemm_schedu
         t = *tiles_in;
     if (t.flags & kReservedFlags) {
         set_error("flags 0x%x: bits 2 and 5 are reserved", t.flags & kReservedFlags);
+        return nullptr;
+    }
+    if ((t.flags & GEMM_FLAG_PING_PONG) && (t.flags & GEMM_FLAG_RING_KERNEL)) {
+        set_error("GEMM_FLAG_PING_PONG and GEMM_FLAG_RING_KERNEL exclude each other");
         return nullptr;
     }
     const int E = elem_size(dtype);

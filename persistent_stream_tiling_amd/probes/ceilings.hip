@@ -1,0 +1,246 @@
+// Hardware ceilings of the MI355X paths the GEMM kernels lean on, measured
+// by small in-bounds kernels (not part of the library; run by
+// `python -m persistent_stream_tiling_amd.profiling ceilings`):
+//
+//   mfma     back-to-back v_mfma_f32_32x32x16_f16 on register operands, four
+//            independent accumulators per wave, one or two waves per SIMD:
+//            the matrix-core rate the power limit allows with no memory work.
+//   lds      16-byte LDS reads (ds_read_b128), 4..16 waves per CU.
+//   copy     the 4096^3 fp16 GEMM's operand traffic: 256 workgroups of 8
+//            waves, one 256x256 tile each, copying the A slab (256 rows x 128
+//            bytes) and the B slab (64 rows x 512 bytes) of every 64-deep
+//            iteration global -> LDS (buffer_load_dwordx4 ... lds), waiting
+//            for each iteration's copies before the next; tiles dealt to the
+//            dies in hardware order, in 4x8 blocks per die, or every
+//            workgroup reading the same tile's panels (all L2 hits).
+//   mix      the same copies plus, per wave and iteration, the 32 MFMAs a
+//            128x64 wave tile of that GEMM issues, with no LDS fragment reads
+//            (and the MFMAs alone).
+//
+// Every launch is preceded by a 512 MiB fill that evicts L2 and the Infinity
+// Cache; times are medians of 6 runs.  Every global and LDS offset stays
+// inside its buffer (the copy offsets reach exactly the last byte of the
+// 4096 x 4096 fp16 matrices); no kernel waits on another workgroup.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <stdio.h>
+#include <stdlib.h>
+#include <vector>
+
+#define CHECK(x)                                                                              \
+    do {                                                                                      \
+        hipError_t e_ = (x);                                                                  \
+        if (e_ != hipSuccess) {                                                               \
+            fprintf(stderr, "HIP error %s at line %d\n", hipGetErrorString(e_), __LINE__);    \
+            exit(1);                                                                          \
+        }                                                                                     \
+    } while (0)
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kIters = 64;            // 64-deep iterations of a 4096-deep product
+constexpr int kLd = 8192;             // bytes per row of a 4096-wide fp16 matrix
+constexpr size_t kMat = 32u << 20;    // bytes of a 4096 x 4096 fp16 matrix
+
+__device__ __forceinline__ i32x4 rsrc_words(const void *base)
+{
+    const uint64_t b = (uint64_t)base;
+    return i32x4{(int)(uint32_t)b, (int)((uint32_t)(b >> 32) & 0xffff), 0x7fffffff, 0x00020000};
+}
+
+// 16 bytes per lane from buffer offset voff into LDS at lds_addr + 16 * lane
+__device__ __forceinline__ void copy16(i32x4 rsrc, uint32_t voff, uint32_t lds_addr)
+{
+    asm volatile("s_mov_b32 m0, %0\n\t"
+                 "s_nop 0\n\t"
+                 "buffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(rsrc)
+                 : "m0");
+}
+
+__global__ __launch_bounds__(256) void mfma_kernel(float *out, int iters, float seed)
+{
+    f32x16 acc[4] = {};
+    f16x8 a, b;
+    for (int i = 0; i < 8; ++i) {
+        a[i] = (_Float16)(seed * (float)(threadIdx.x + i));
+        b[i] = (_Float16)(seed * (float)(i - 3));
+    }
+    for (int it = 0; it < iters; ++it)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc[j], 0, 0, 0);
+    float s = 0.0f;
+    for (int j = 0; j < 4; ++j)
+        for (int e = 0; e < 16; ++e)
+            s += acc[j][e];
+    out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+__global__ __launch_bounds__(256) void lds_kernel(uint32_t *out, int iters)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t lds[64 * 1024];
+    for (int i = threadIdx.x; i < 64 * 1024 / 4; i += blockDim.x)
+        ((uint32_t *)lds)[i] = (uint32_t)i * 2654435761u;
+    __syncthreads();
+    u32x4 x = u32x4{0, 0, 0, 0};
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint32_t base = (uint32_t)(wave * 16384 + lane * 16);
+    for (int it = 0; it < iters; ++it)
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            x ^= *(const u32x4 *)(lds + ((base + j * 1024 + it * 64) & (64 * 1024 - 16)));
+    out[blockIdx.x * blockDim.x + threadIdx.x] = x[0] ^ x[1] ^ x[2] ^ x[3];
+}
+
+// order 0: hardware order (die = workgroup id mod 8), tiles row-major;
+// order 1: die x holds a 4 x 8 block of tiles; order 2: all the same tile.
+template <int NMFMA, bool COPY>
+__global__ __launch_bounds__(512, 1) void copy_kernel(const uint8_t *A, const uint8_t *B,
+                                                      int order, float *out)
+{
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[128 * 1024];
+    const int hw = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    int tm = 0, tn = 0;
+    if (order == 0) {
+        tm = hw / 16;
+        tn = hw % 16;
+    } else if (order == 1) {
+        const int die = hw % 8, slot = hw / 8;
+        tm = 4 * (die / 2) + slot / 8;
+        tn = 8 * (die % 2) + slot % 8;
+    }
+    const uint8_t *a0 = A + (size_t)tm * 256 * kLd;
+    const uint8_t *b0 = B + (size_t)tn * 512;
+    const uint32_t lds_base =
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)lds;
+    uint32_t a_off[4], b_off[4];
+    for (int j = 0; j < 4; ++j) {
+        const int blk = j * 8 + wave;  // 1 KiB block of a 32 KiB slab
+        a_off[j] = (uint32_t)((blk * 8 + (lane >> 3)) * kLd + (lane & 7) * 16);
+        b_off[j] = (uint32_t)((blk * 2 + (lane >> 5)) * kLd + (lane & 31) * 16);
+    }
+    f32x16 acc[4] = {};
+    f16x8 x, y;
+    for (int i = 0; i < 8; ++i) {
+        x[i] = (_Float16)(0.001f * (float)(lane + i));
+        y[i] = (_Float16)(0.002f * (float)(i - 3));
+    }
+    for (int it = 0; it < kIters; ++it) {
+        const i32x4 ra = rsrc_words(a0 + it * 128);
+        const i32x4 rb = rsrc_words(b0 + (size_t)it * 64 * kLd);
+        const uint32_t slot = lds_base + (uint32_t)((it & 1) * 65536 + wave * 1024);
+        if (COPY) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                copy16(ra, a_off[j], slot + j * 8192);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                copy16(rb, b_off[j], slot + 32768 + j * 8192);
+        }
+#pragma unroll
+        for (int m = 0; m < NMFMA; ++m)
+            acc[m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(x, y, acc[m & 3], 0, 0, 0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    float s = 0.0f;
+    for (int j = 0; j < 4; ++j)
+        for (int e = 0; e < 16; ++e)
+            s += acc[j][e];
+    out[hw * 512 + threadIdx.x] = s;
+}
+
+struct Timer {
+    hipEvent_t e0, e1;
+    uint8_t *flush;
+    Timer()
+    {
+        CHECK(hipEventCreate(&e0));
+        CHECK(hipEventCreate(&e1));
+        CHECK(hipMalloc(&flush, 512u << 20));
+    }
+    template <typename F>
+    float median_us(F launch)
+    {
+        std::vector<float> t;
+        for (int r = 0; r < 7; ++r) {
+            CHECK(hipMemsetAsync(flush, r, 512u << 20));
+            CHECK(hipEventRecord(e0));
+            launch();
+            CHECK(hipGetLastError());
+            CHECK(hipEventRecord(e1));
+            CHECK(hipEventSynchronize(e1));
+            float ms = 0.0f;
+            CHECK(hipEventElapsedTime(&ms, e0, e1));
+            if (r)
+                t.push_back(ms * 1e3f);
+        }
+        std::sort(t.begin(), t.end());
+        return t[t.size() / 2];
+    }
+};
+
+int main()
+{
+    int cus = 0;
+    CHECK(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, 0));
+    Timer T;
+    float *fout;
+    uint32_t *uout;
+    uint8_t *A, *B;
+    CHECK(hipMalloc(&fout, (size_t)cus * 8 * 512 * 4));
+    CHECK(hipMalloc(&uout, (size_t)cus * 8 * 256 * 4));
+    CHECK(hipMalloc(&A, kMat));
+    CHECK(hipMalloc(&B, kMat));
+    CHECK(hipMemset(A, 1, kMat));
+    CHECK(hipMemset(B, 2, kMat));
+
+    printf("| probe | configuration | us | rate |\n|---|---|---|---|\n");
+    for (int wps : {1, 2}) {  // waves per SIMD: one or two workgroups of 4 waves per CU
+        const int g = cus * wps, iters = 20000;
+        const float us = T.median_us([&] {
+            hipLaunchKernelGGL(mfma_kernel, dim3(g), dim3(256), 0, 0, fout, iters, 1e-3f);
+        });
+        const double flops = (double)g * 4 * iters * 4 * 32768.0;
+        printf("| mfma | %d wave(s) per SIMD, %d x 4 MFMA 32x32x16 f16 per wave | %.1f | %.1f "
+               "TFLOP/s (%.1f%% of 2516.6) |\n",
+               wps, iters, us, flops / us / 1e6, flops / us / 1e6 / 2516.6 * 100);
+    }
+    for (int wpc : {1, 2, 4}) {  // workgroups of 4 waves per CU
+        const int g = cus * wpc, iters = 20000;
+        const float us = T.median_us(
+            [&] { hipLaunchKernelGGL(lds_kernel, dim3(g), dim3(256), 0, 0, uout, iters); });
+        const double bytes = (double)g * 256 * iters * 16 * 16.0;
+        printf("| lds | %d workgroup(s) of 4 waves per CU, ds_read_b128 | %.1f | %.1f TB/s, %.0f "
+               "B/clk/CU at 2.4 GHz |\n",
+               wpc, us, bytes / us / 1e6, bytes / (us * 1e-6) / cus / 2.4e9);
+    }
+    const double copy_bytes = 256.0 * kIters * 65536;
+    const char *orders[3] = {"hardware die order", "4x8 tile block per die", "one tile's panels (L2 hits)"};
+    for (int order = 0; order < 3; ++order) {
+        const float us = T.median_us([&] {
+            hipLaunchKernelGGL((copy_kernel<0, true>), dim3(256), dim3(512), 0, 0, A, B, order, fout);
+        });
+        printf("| copy | 4096^3 operand slabs global -> LDS, %s | %.1f | %.2f TB/s, %.1f GB/s "
+               "per CU |\n",
+               orders[order], us, copy_bytes / us / 1e6, copy_bytes / us / 1e3 / 256);
+    }
+    const float m0 = T.median_us([&] {
+        hipLaunchKernelGGL((copy_kernel<32, false>), dim3(256), dim3(512), 0, 0, A, B, 1, fout);
+    });
+    printf("| mix | no copies, 32 MFMAs per wave and iteration (the 4096^3 GEMM's MFMA work) | "
+           "%.1f | %.0f TFLOP/s |\n",
+           m0, 2.0 * 4096.0 * 4096.0 * 4096.0 / m0 / 1e6);
+    const float m32 = T.median_us([&] {
+        hipLaunchKernelGGL((copy_kernel<32, true>), dim3(256), dim3(512), 0, 0, A, B, 1, fout);
+    });
+    printf("| mix | the copies above (4x8 block per die) plus 32 MFMAs per wave and iteration "
+           "(the 4096^3 GEMM's MFMA work) | %.1f | %.0f TFLOP/s-equivalent |\n",
+           m32, 2.0 * 4096.0 * 4096.0 * 4096.0 / m32 / 1e6);
+    return 0;
+}

@@ -301,10 +301,31 @@ def main():
     m.add_argument("--title", required=True)
     m.add_argument("--out", required=True)
     m.add_argument("--cmd", required=True, nargs="+", help="the commands that made the runs")
+    h = sub.add_parser("ceilings", help="run the hardware-ceiling probes, write a table")
+    h.add_argument("--out", required=True)
     r = sub.add_parser("resources")
     r.add_argument("--out", required=True)
     a = ap.parse_args()
-    if a.cmd_name == "pmc":
+    if a.cmd_name == "ceilings":
+        import subprocess
+        from . import _build
+        exe = os.path.join(_build.PROBES, "ceilings")
+        if not os.path.exists(exe):
+            raise RuntimeError(f"{exe} is missing: build it with _build.build_probes()")
+        res = subprocess.run([exe], capture_output=True, text=True, timeout=600)
+        if res.returncode != 0:
+            raise RuntimeError(res.stderr[-4000:])
+        text = "\n".join([
+            "# Hardware ceilings of the paths the GEMM kernels use (MI355X)", "",
+            "Command: `python -m persistent_stream_tiling_amd.profiling ceilings --out <file>` "
+            "(runs `persistent_stream_tiling_amd/probes/ceilings`, built from "
+            "`probes/ceilings.hip` by `__graft_entry__.build()`; the probe kernels are "
+            "described in that file's header).  A 512 MiB fill before every launch evicts "
+            "L2 and the Infinity Cache; medians of 6 runs.", "",
+            res.stdout.strip(), ""])
+        open(a.out, "w").write(text)
+        print(text)
+    elif a.cmd_name == "pmc":
         groups = {}
         for d, lab, w in zip(a.csv, a.label, a.workload):
             for sched, vals in pmc_summary(d, a.schedules.split(","), a.warmup, a.steps).items():

@@ -1,9 +1,11 @@
 """Launch configuration (tile shape, grid) per workload and schedule.
 
 The benchmark times exactly these, and the full-size GPU parity tests run
-exactly these, so what is measured is what is checked.
+exactly these, so what is measured is what is checked.  fp16/bf16 256x256
+tiles in the default wave layout run the library's default kernel for that
+tile, the wave-specialised ping-pong kernel.
 """
-from ._lib import FLAG_NO_XCD_REMAP, FLAG_PING_PONG, FLAG_STREAM_COPIES
+from ._lib import FLAG_NO_XCD_REMAP, FLAG_STREAM_COPIES
 
 SCHEDULES = ("dp", "persistent", "streamk", "hybrid")
 
@@ -135,23 +137,6 @@ IRREGULAR_TILES = {
 }
 
 BENCH_TILES.update(IRREGULAR_TILES)
-
-
-def _ping_pong_on_256x256(table):
-    """Every fp16/bf16 entry with 256x256 tiles in the default wave layout runs
-    the wave-specialised ping-pong kernel: the same bits as the ring kernel,
-    measured 1.006-1.033x faster on the same tiles and schedules (4096^3 fp16,
-    8192x28672x8192 and two irregular bf16 shapes, rounds interleaved)."""
-    for name, per_sched in table.items():
-        if name == "fp32_256":
-            continue
-        for sched, t in per_sched.items():
-            if (t.get("bm"), t.get("bn")) == (256, 256) and "wave_m" not in t and \
-                    not t.get("flags", 0) & FLAG_STREAM_COPIES:
-                t["flags"] = t.get("flags", 0) | FLAG_PING_PONG
-
-
-_ping_pong_on_256x256(BENCH_TILES)
 
 
 def bench_tiles(workload, schedule, dtype):

@@ -103,7 +103,8 @@ def test_variant_table_is_exported_and_each_entry_selectable():
         assert key not in seen, f"two table entries for {key}"
         seen.add(key)
         flags = (gsk.FLAG_STREAM_COPIES if v["stream_copies"] else 0) | \
-            (gsk.FLAG_PING_PONG if v["kind"] == 3 else 0)
+            (gsk.FLAG_PING_PONG if v["kind"] == 3 else 0) | \
+            (gsk.FLAG_RING_KERNEL if v["kind"] == 2 else 0)
         plan = gsk.plan_for_device(1000, 1000, 1000, names[v["dtype"]], "dp", bm=v["bm"],
                                    bn=v["bn"], wave_m=v["wave_m"], wave_n=v["wave_n"],
                                    stages=v["stages"], flags=flags)
@@ -137,3 +138,23 @@ def test_output_offsets_stay_within_32_bits():
     ok = gsk.plan_for_device(256, (1 << 21) - 256, 64, "f16", "dp", bm=256, bn=256,
                              flags=gsk.FLAG_C_INPUT_DTYPE)
     assert ok.info["N"] == (1 << 21) - 256
+
+
+def test_ping_pong_is_the_256x256_default():
+    for dt in ("f16", "bf16"):
+        p = gsk.plan_for_device(4096, 4096, 4096, dt, "dp", bm=256, bn=256)
+        assert p.info["kernel_kind"] == 3 and "pingpong" in p.describe()
+        assert gsk.plan_for_device(4096, 4096, 4096, dt, "dp", bm=256, bn=256,
+                                   flags=gsk.FLAG_RING_KERNEL).info["kernel_kind"] == 2
+        # other tiles, the non-temporal copies and other wave layouts: the ring kernel
+        assert gsk.plan_for_device(4096, 4096, 4096, dt, "dp", bm=256, bn=128).info["kernel_kind"] == 2
+        assert gsk.plan_for_device(4096, 4096, 4096, dt, "dp", bm=256, bn=256,
+                                   flags=gsk.FLAG_STREAM_COPIES).info["kernel_kind"] == 2
+        with pytest.raises(ValueError, match="no kernel"):
+            gsk.plan_for_device(4096, 4096, 4096, dt, "dp", bm=128, bn=128,
+                                flags=gsk.FLAG_PING_PONG)
+    with pytest.raises(ValueError, match="exclude"):
+        gsk.plan_for_device(4096, 4096, 4096, "f16", "dp", bm=256, bn=256,
+                            flags=gsk.FLAG_PING_PONG | gsk.FLAG_RING_KERNEL)
+    # fp32 and int8 keep the register-staged kernel
+    assert gsk.plan_for_device(1024, 1024, 1024, "i8", "dp", bm=256, bn=256).info["kernel_kind"] == 0

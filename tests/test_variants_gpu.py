@@ -66,6 +66,8 @@ def _tiles(v):
         t["flags"] = gsk.FLAG_STREAM_COPIES
     if v["kind"] == 3:
         t["flags"] = t.get("flags", 0) | gsk.FLAG_PING_PONG
+    elif v["kind"] == 2:
+        t["flags"] = t.get("flags", 0) | gsk.FLAG_RING_KERNEL
     return t
 
 
@@ -135,9 +137,9 @@ def test_ping_pong_matches_the_ring_kernel_bitwise(shape, dtype):
     da, db = to_device(a, dtype), to_device(b, dtype)
     for sched in SCHEDULES:
         for g in ((0, 37) if sched in ("streamk", "hybrid") else (0,)):
-            _, _, c_ring = run_gemm(da, db, M, N, K, dtype, sched, grid=g, bm=256, bn=256)
-            plan, _, c_pp = run_gemm(da, db, M, N, K, dtype, sched, grid=g, bm=256, bn=256,
-                                     flags=gsk.FLAG_PING_PONG)
-            assert plan.info["kernel_kind"] == 3
+            ring, _, c_ring = run_gemm(da, db, M, N, K, dtype, sched, grid=g, bm=256, bn=256,
+                                       flags=gsk.FLAG_RING_KERNEL)
+            plan, _, c_pp = run_gemm(da, db, M, N, K, dtype, sched, grid=g, bm=256, bn=256)
+            assert plan.info["kernel_kind"] == 3 and ring.info["kernel_kind"] == 2
             assert torch.equal(c_ring.view(torch.int32), c_pp.view(torch.int32)), plan.describe()
             compare(c_pp.cpu().numpy(), ref, scale, dtype, what=plan.describe())
