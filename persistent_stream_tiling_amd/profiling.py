@@ -32,8 +32,10 @@ COPY_BYTES = 256 << 20  # the copy in bench.py --traffic-run (read and written o
 
 
 def source_hash():
+    """Hash of the device code (the kernels and the schedule arithmetic they
+    run): counters and traffic taken on one build stay valid while it holds."""
     h = hashlib.sha256()
-    for f in ("kernels.hip", "kernels.h", "schedule.h", "api.hip"):
+    for f in ("kernels.hip", "kernels.h", "schedule.h"):
         with open(os.path.join(ROOT, "persistent_stream_tiling_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -244,15 +246,18 @@ def kernel_resources(out, cmd_note):
         m = re.match(r"_ZN3gsk\d+(\w+?)I(.*)EEvNS_10KernelArgsE", mangled)
         if not m:
             return mangled
-        args = ", ".join(re.findall(r"Li(\d+)E", m.group(2)))
+        args = ", ".join(re.findall(r"Li(\d+)E|Lb(\d)E", m.group(2)) and
+                         [x or y for x, y in re.findall(r"Li(\d+)E|Lb(\d)E", m.group(2))])
         return f"{m.group(1)}<{args}>"
     gemm = [r for r in recs if "KernelArgs" in r["name"]]
     lines = ["# Kernel resources (compiler remarks)", "",
              f"Command: `{cmd_note}`", "",
              f"Kernel source hash: {source_hash()}.  Template arguments: <dtype (0 fp32, 1 fp16, "
-             "2 bf16), bm, bn, waves along M, waves along N[, ring stages]>.  gemm_kernel_pair is "
-             "the fp16/bf16 default (whole-row A ring), gemm_kernel_dma the half-row A ring, "
-             "gemm_kernel the register-staged kernel (fp32 default).", "",
+             "2 bf16, 3 int8), bm, bn, waves along M, waves along N[, non-temporal copies]>; "
+             "gemm_kernel_pp<dtype> is 256x256 with 2x4 waves.  gemm_kernel_pp is the fp16/bf16 "
+             "default at 256x256 (wave-specialised ping-pong), gemm_kernel_pair the direct-to-LDS "
+             "ring kernel (the other fp16/bf16 tiles), gemm_kernel the register-staged kernel "
+             "(fp32, int8, fp16/bf16 64x64).", "",
              "| kernel | VGPRs | AGPRs | SGPRs | VGPR spills | SGPR spills | scratch B/lane | "
              "waves/SIMD | LDS B |", "|---|---|---|---|---|---|---|---|---|"]
     for r in gemm:
@@ -301,12 +306,47 @@ def main():
     m.add_argument("--title", required=True)
     m.add_argument("--out", required=True)
     m.add_argument("--cmd", required=True, nargs="+", help="the commands that made the runs")
+    tt = sub.add_parser("traffic-table", help="markdown table of profiles/traffic.json records")
+    tt.add_argument("--json", default=os.path.join(ROOT, "profiles", "traffic.json"))
+    tt.add_argument("--workload", required=True)
+    tt.add_argument("--kernel", required=True, help="kernel name for the title")
+    tt.add_argument("--out", required=True)
     h = sub.add_parser("ceilings", help="run the hardware-ceiling probes, write a table")
     h.add_argument("--out", required=True)
     r = sub.add_parser("resources")
     r.add_argument("--out", required=True)
     a = ap.parse_args()
-    if a.cmd_name == "ceilings":
+    if a.cmd_name == "traffic-table":
+        table = json.load(open(a.json))
+        recs = {k.split("/", 1)[1]: v for k, v in table.items() if k.split("/", 1)[0] == a.workload}
+        any_rec = next(iter(recs.values()))
+        lines = [f"# HBM-side traffic per launch, {a.workload} (`{a.kernel}`)", "",
+                 "Commands (one rocprofv3 run per counter, each on committed files), then the "
+                 "table from `profiles/traffic.json`:", "",
+                 "    " + any_rec["command"].replace("(then WRITE_SIZE) ", ""),
+                 "    " + any_rec["command"].replace("FETCH_SIZE (then WRITE_SIZE)", "WRITE_SIZE"),
+                 "    python3 -m persistent_stream_tiling_amd.profiling traffic --fetch <dir> "
+                 "--write <dir> --workload <workload> --schedule <schedule> ...",
+                 f"    python3 -m persistent_stream_tiling_amd.profiling traffic-table --workload "
+                 f"{a.workload} --kernel ... --out <file>", "",
+                 "Each run first copies 256 MiB device to device, then runs the GEMM three times; "
+                 "a counter's calibration factor is 256 MiB over what it reads for that copy.  "
+                 "Algorithmic bytes: A and B read once, C written once, plus every parked "
+                 f"Stream-K piece written and read once.  Kernel source hash: "
+                 f"{any_rec['source_hash']}.", "",
+                 "| schedule | FETCH MB | WRITE MB | total MB | algorithmic MB | traffic / "
+                 "algorithmic | FETCH factor | WRITE factor |", "|---|---|---|---|---|---|---|---|"]
+        for sched in ("dp", "persistent", "streamk", "hybrid"):
+            if sched in recs:
+                r = recs[sched]
+                lines.append(f"| {sched} | {r['fetch_bytes'] / 1e6:.1f} | {r['write_bytes'] / 1e6:.1f} "
+                             f"| {r['bytes_per_launch'] / 1e6:.1f} | {r['algorithmic_bytes'] / 1e6:.1f} "
+                             f"| {r['traffic_over_algorithmic']:.3f} | {r['fetch_calibration']:.2f} | "
+                             f"{r['write_calibration']:.2f} |")
+        text = "\n".join(lines) + "\n"
+        open(a.out, "w").write(text)
+        print(text)
+    elif a.cmd_name == "ceilings":
         import subprocess
         from . import _build
         exe = os.path.join(_build.PROBES, "ceilings")
