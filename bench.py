@@ -217,8 +217,9 @@ def schedule_table(args, out):
              "runs per schedule (rounds interleaved, 512 MiB cache flush before each run), tuned "
              "tiles, default grid (one workgroup per CU); one process per workload.", "",
              "| workload | M x N x K | tiles T | dp us | persistent us | Stream-K us | hybrid us "
-             "| best | best TFLOP/s | Stream-K / DP | hybrid / DP |",
-             "|---|---|---|---|---|---|---|---|---|---|---|"]
+             "| best | best TFLOP/s | Stream-K / DP | hybrid / DP | Stream-K splits tiles | "
+             "hybrid T_sk (splits) |",
+             "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
     for name in names:
         r = subprocess.run([sys.executable, os.path.abspath(__file__), "--workload", name,
                             "--steps", str(args.steps), "--table-row"],
@@ -258,10 +259,14 @@ def schedule_table_row(args):
         med = {s: float(np.median(v[2])) * 1e3 for s, v in runs.items()}
         best = min(med, key=med.get)
         T = runs["dp"][0].info["tiles"]
+        sk, hy = runs["streamk"][0].info, runs["hybrid"][0].info
+        sk_split = "yes" if sk["max_pieces"] >= 2 else "no"
+        hy_split = f"{hy['tiles_sk']} ({'yes' if hy['tiles_sk'] and hy['max_pieces'] >= 2 else 'no'})"
         print(f"| {name} | {M} x {N} x {K} | {T} | " +
               " | ".join(f"{med[s]:.1f}" for s in SCHEDULES) +
               f" | {best} | {2.0 * M * N * K / (med[best] * 1e-6) / 1e12:.0f} | "
-              f"{med['dp'] / med['streamk']:.2f} | {med['dp'] / med['hybrid']:.2f} |", flush=True)
+              f"{med['dp'] / med['streamk']:.2f} | {med['dp'] / med['hybrid']:.2f} | "
+              f"{sk_split} | {hy_split} |", flush=True)
 
 
 SWEEP_VARIANTS = (("streamk", 0), ("hybrid", 0), ("hybrid", "one_tile"), ("streamk", "two_kernel"))
@@ -291,15 +296,19 @@ def grid_sweep(args, out):
     lines = [f"# Stream-K grid sweep: `python bench.py --workload {args.workload} "
              f"--steps {args.steps} --grid-sweep <file>`", "",
              f"Kernel source hash: {kernel_source_hash()}.  Median of {args.steps} timed runs per "
-             "line (512 MiB cache flush before each), tuned tiles per schedule.  g = 256 is one "
+             "line and of as many data-parallel runs timed in alternating rounds with them "
+             "(512 MiB cache flush before each), tuned tiles per schedule.  'splits tiles' says "
+             "whether the plan does any Stream-K work (some tile cut over two or more "
+             "workgroups); a plan that does not is a data-parallel run of whole tiles.  g = 256 is one "
              "workgroup per CU; g = T is one per tile; with g = s*T and s dividing the "
              "iterations per tile, Stream-K is a fixed split-K with s pieces per tile.  Grids "
              "above 256 are refused by the in-kernel fixups (they need every workgroup "
              "resident); `two_kernel` parks every piece and reduces the split tiles in a second "
              "kernel, which allows them.  `one_tile` is the hybrid without two_tiles (Stream-K "
              "over T mod g tiles only).", "",
-             "| workload | tiles T | schedule | g | us | TFLOP/s | DP us | DP / this |",
-             "|---|---|---|---|---|---|---|---|"]
+             "| workload | tiles T | schedule | g | T_sk | splits tiles | us | TFLOP/s | DP us "
+             "(interleaved) | DP / this |",
+             "|---|---|---|---|---|---|---|---|---|---|"]
     for name in names:
         r = subprocess.run([sys.executable, os.path.abspath(__file__), "--workload", name,
                             "--steps", str(args.steps), "--grid-sweep-rows"],
@@ -323,14 +332,22 @@ def grid_sweep_rows(args):
     flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
     flops = 2.0 * M * N * K
 
-    def med(plan, ws):
-        ms, _ = time_schedule(plan, a, b, c, ws, args.steps, 2, flush)
+    def interleaved(plan, ws, dp, dp_ws):
+        """Medians of this plan and of data-parallel, timed in alternating
+        rounds so that drift hits both alike."""
+        ts, td = [], []
+        half = max(1, args.steps // 2)
+        for _ in range(2):
+            ms, _ = time_schedule(plan, a, b, c, ws, half, 1, flush)
+            ts.extend(ms.tolist())
+            ms, _ = time_schedule(dp, a, b, c, dp_ws, half, 1, flush)
+            td.extend(ms.tolist())
         if ws is not None and plan.workspace_status(ws) != 0:
             raise RuntimeError("a Stream-K fixup wait gave up")
-        return float(np.median(ms)) * 1e3
+        return float(np.median(ts)) * 1e3, float(np.median(td)) * 1e3
 
     dp = gsk.GemmPlan(M, N, K, dt, "dp", **tuning.bench_tiles(args.workload, "dp", dt))
-    dp_us = med(dp, dp.new_workspace())
+    dp_ws = dp.new_workspace()
     for sched, variant in SWEEP_VARIANTS:
         tiles = tuning.bench_tiles(args.workload, sched, dt)
         if variant == "one_tile":
@@ -343,13 +360,18 @@ def grid_sweep_rows(args):
             try:
                 plan = gsk.GemmPlan(M, N, K, dt, sched, grid=g, **tiles)
             except ValueError as e:
-                print(f"| {args.workload} | {T} | {label} | {g} | refused: {str(e)[:60]} "
+                print(f"| {args.workload} | {T} | {label} | {g} | | | refused: {str(e)[:60]} "
                       "| | | |", flush=True)
                 continue
-            us = med(plan, plan.new_workspace())
-            print(f"| {args.workload} | {T} | {label} | {g} | {us:.1f} | "
-                  f"{flops / (us * 1e-6) / 1e12:.0f} | {dp_us:.1f} | {dp_us / us:.2f} |",
-                  flush=True)
+            info = plan.info
+            # Stream-K work: tiles split over several workgroups (T_sk > 0 and
+            # a tile with two or more pieces); otherwise the plan runs whole
+            # tiles only and is data-parallel under another name
+            splits = "yes" if info["tiles_sk"] > 0 and info["max_pieces"] >= 2 else "no"
+            us, dp_us = interleaved(plan, plan.new_workspace(), dp, dp_ws)
+            print(f"| {args.workload} | {T} | {label} | {g} | {info['tiles_sk']} | {splits} | "
+                  f"{us:.1f} | {flops / (us * 1e-6) / 1e12:.0f} | {dp_us:.1f} | "
+                  f"{dp_us / us:.2f} |", flush=True)
 
 
 def log_sampled_shapes(n, seed=20261203, lo=256, hi=8192, step=256):
