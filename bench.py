@@ -374,71 +374,60 @@ def grid_sweep_rows(args):
                   f"{dp_us / us:.2f} |", flush=True)
 
 
-def log_sampled_shapes(n, seed=20261203, lo=256, hi=8192, step=256):
-    """n (M, N, K), each log-uniform in [lo, hi] and rounded to a multiple of
-    step, as the pages' shape benchmark draws them."""
-    import math
-    import random
-    rnd = random.Random(seed)
-
-    def one():
-        v = math.exp(rnd.uniform(math.log(lo), math.log(hi)))
-        return int(min(hi, max(lo, round(v / step) * step)))
-    return [(one(), one(), one()) for _ in range(n)]
-
-
 def log_sampled(args, out):
     """The pages' shape benchmark: fp16 GEMMs of log-sampled shapes, fp16 C.
-    Per shape: data-parallel, Stream-K and hybrid (library default tiles,
-    g = 256) and, as context only, torch.matmul (hipBLASLt) with the same
-    fp16 output; median of --steps runs each, cache flush before every run."""
+    Per shape: data-parallel, Stream-K and hybrid (library default plans)
+    and, as context only, torch.matmul (hipBLASLt) with the same fp16
+    output; median of --steps rounds interleaved over the four, cache flush
+    before every run."""
     import torch
     import persistent_stream_tiling_amd as gsk
+    from persistent_stream_tiling_amd.inputs import log_sampled_shapes
     shapes = log_sampled_shapes(args.log_sampled)
     flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
     gen = torch.Generator(device="cuda")
     gen.manual_seed(7)
     rows = []
 
-    def med(fn):
-        ts = []
-        for _ in range(args.steps + 1):
-            flush.zero_()
-            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            s.record()
-            fn()
-            e.record()
-            e.synchronize()
-            ts.append(s.elapsed_time(e) * 1e3)
-        return float(np.median(ts[1:]))
-
     for i, (M, N, K) in enumerate(shapes):
         a = torch.randn((M, K), device="cuda", generator=gen).half()
         b = torch.randn((K, N), device="cuda", generator=gen).half()
         c = torch.empty((M, N), dtype=torch.float16, device="cuda")
-        us, err = {}, 0.0
+        err = 0.0
         ref = a[:64].float() @ b.float()
         sref = a[:64].float().abs() @ b.float().abs()
+        runs = []
         for sched in ("dp", "streamk", "hybrid"):
             plan = gsk.GemmPlan(M, N, K, "f16", sched, flags=gsk.FLAG_C_INPUT_DTYPE)
             ws = plan.new_workspace()
-            plan.run(a, b, c, ws)
+            plan.run(a, b, c, ws)  # raises if a fixup wait gave up
             torch.cuda.synchronize()
             # sanity check on the first rows against an fp32 product (not a parity test:
             # parity is checked against the oracle by the test suite)
             err = max(err, float(((c[:64].float() - ref).abs() / sref.clamp_min(1e-30)).max()))
-            us[sched] = med(lambda: plan.run(a, b, c, ws, check=False))
-            if ws is not None and plan.workspace_status(ws) != 0:
-                raise RuntimeError(f"{(M, N, K)} {sched}: a fixup wait gave up")
+            runs.append((sched, (lambda p=plan, w=ws: p.run(a, b, c, w, check=False)), []))
+        runs.append(("torch", lambda: torch.matmul(a, b, out=c), []))
+        # rounds interleaved over the four: kernels of ~10 us vary by several us
+        # with the state the GPU is in, and every line sees the same mixture of it
+        for rnd in range(args.steps + 1):
+            for _, fn, ts in runs:
+                flush.zero_()
+                s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                s.record()
+                fn()
+                e.record()
+                e.synchronize()
+                if rnd:
+                    ts.append(s.elapsed_time(e) * 1e3)
+        us = {name: float(np.median(ts)) for name, _, ts in runs}
         T = -(-M // 256) * -(-N // 256)  # 256x256 tiles, for the summary by size
-        us["torch"] = med(lambda: torch.matmul(a, b, out=c))
         if err > 4e-3 + 2.0 ** -11:
             raise RuntimeError(f"{(M, N, K)}: max |C - A.B| / S = {err:.2e}")
         rows.append((M, N, K, T, us))
         if i % 50 == 0:
             log(f"[log-sampled] {i}/{len(shapes)} {M}x{N}x{K}: " +
                 " ".join(f"{k} {v:.1f}" for k, v in us.items()))
-        del a, b, c
+        del a, b, c, runs
 
     def gmean(x):
         return float(np.exp(np.mean(np.log(x))))
@@ -451,8 +440,10 @@ def log_sampled(args, out):
              f"--steps {args.steps} --log-sampled-out <file>`", "",
              f"Kernel source hash: {kernel_source_hash()}.  {len(rows)} shapes (M, N, K) drawn "
              "log-uniformly in [256, 8192] and rounded to multiples of 256 (seeded); fp16 inputs "
-             "N(0,1), fp16 C (fp32 accumulate); library default tiles, g = 256; median of "
-             f"{args.steps} runs per line, 512 MiB cache flush before each; T below counts "
+             "N(0,1), fp16 C (fp32 accumulate); library default plans (tile and, for Stream-K "
+             "and hybrid, g from the planner's cost model); median of "
+             f"{args.steps} rounds interleaved over the four lines, 512 MiB cache flush before "
+             "each run; T below counts "
              "256x256 tiles whatever tile the plan chose.  torch.matmul "
              "(hipBLASLt, same fp16 output) is context, not a target.", "",
              "| statistic | value |", "|---|---|",

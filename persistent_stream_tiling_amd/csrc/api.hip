@@ -6,7 +6,9 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
+#include <cmath>
 #include <mutex>
 #include <new>
 #include <string>
@@ -33,6 +35,7 @@ struct gemm_plan {
     int32_t spin_limit;
     int32_t drop_wg;           // GEMM_FLAG_DEBUG_DROP_SIGNAL: workgroup that never signals
     int split_fixup, max_pieces;
+    bool grid_from_model;      // tile and g picked by the Stream-K cost model
 };
 
 namespace {
@@ -99,6 +102,78 @@ void default_tile(int64_t M, int64_t N, int64_t K, gemm_schedule schedule, int c
             *bn = c.bn;
         }
     }
+}
+
+// Default Stream-K / hybrid plan for fp16/bf16 when the caller names neither a
+// tile nor a grid.  The Triton Stream-K issue's benchmark picks g per shape
+// from a sweep; a library call cannot sweep, so the planner estimates a few
+// candidate plans and takes the cheapest.  Candidates, for each of the tiles
+// 256x256, 256x128, 128x128 with T tiles of ipt 64-deep iterations:
+//   - g = s*T for s in {1, 2, 3, 4, 6, 8, 16} dividing ipt, g <= CUs: every
+//     workgroup runs one piece of exactly ipt/s iterations of one tile (s = 1
+//     is one whole tile per workgroup, no fixup);
+//   - g = CUs when that does not split the tiles evenly: Stream-K's even
+//     split of all T*ipt iterations, whose ranges cross tile boundaries.
+// Estimated us, with q the iterations of the longest range and a = bm*bn/65536:
+//   c0 + it[tile]*q + [s > 1]*(split[tile] + c_log*a*log2(s))
+//      + [ranges cross tiles]*cross
+// The numbers are a least-squares fit to MI355X measurements of these
+// candidates on 260 log-sampled fp16 shapes (mean data-parallel time / model
+// pick 1.17, against 0.92 for one workgroup per CU); `cross` is what a
+// workgroup running pieces of two tiles costs: a second pipeline fill and a
+// second parked piece, which the tile's whole fixup then waits for.  Returns
+// false (keep the one-workgroup-per-CU default) when every tile shape has more
+// than CUs tiles.
+struct StreamKModel {
+    double c0, it[3], split[3], c_log, cross;
+};
+static const StreamKModel kSkModel = {13.12, {1.299, 0.975, 0.766}, {24.85, 14.02, 9.09}, -3.29,
+                                      13.36};
+static const int kSkTiles[3][2] = {{256, 256}, {256, 128}, {128, 128}};
+static const int kSkSplits[] = {1, 2, 3, 4, 6, 8, 16};
+
+double streamk_estimate(int ti, int64_t T, int64_t ipt, int64_t g)
+{
+    const StreamKModel &m = kSkModel;
+    const double area = kSkTiles[ti][0] * kSkTiles[ti][1] / 65536.0;
+    const bool aligned = g % T == 0 && ipt % (g / T) == 0;
+    const int64_t s = aligned ? g / T : std::max<int64_t>(2, cdiv(g, T));
+    const int64_t q = aligned ? ipt / s : cdiv(T * ipt, g);
+    double est = m.c0 + m.it[ti] * (double)q + (aligned ? 0.0 : m.cross);
+    if (s > 1)
+        est += m.split[ti] + m.c_log * area * std::log2((double)s);
+    return est;
+}
+
+bool streamk_default_plan(int64_t M, int64_t N, int64_t K, int cus, int *bm, int *bn, int *grid)
+{
+    const int64_t ipt = cdiv(K > 0 ? K : 1, 64);
+    double best = 0.0;
+    bool found = false, any_aligned = false;
+    for (int ti = 0; ti < 3; ++ti) {
+        const int64_t T = cdiv(M, kSkTiles[ti][0]) * cdiv(N, kSkTiles[ti][1]);
+        if (T <= 0)
+            continue;
+        auto consider = [&](int64_t g) {
+            const double e = streamk_estimate(ti, T, ipt, g);
+            if (!found || e < best) {
+                best = e;
+                found = true;
+                *bm = kSkTiles[ti][0];
+                *bn = kSkTiles[ti][1];
+                *grid = (int)g;
+            }
+        };
+        for (int s : kSkSplits)
+            if (ipt % s == 0 && s * T <= cus) {
+                any_aligned = true;
+                consider(s * T);
+            }
+        const int64_t g = cus;
+        if (T * ipt >= g && !(g % T == 0 && ipt % (g / T) == 0))
+            consider(g);
+    }
+    return found && any_aligned;
 }
 
 // The first compiled variant matching the request (0 = any): the table lists
@@ -181,17 +256,29 @@ gemm_plan *create(int64_t M, int64_t N, int64_t K, gemm_dtype dtype, gemm_schedu
         return nullptr;
     }
     const int E = elem_size(dtype);
+    bool grid_from_model = false;
     if (t.bm == 0 && t.bn == 0) {
         if (dtype == GEMM_F32)
             t.bm = t.bn = (M * N <= 512 * 512) ? 64 : 128;
         else if (dtype == GEMM_I8)
             t.bm = t.bn = cdiv(M, 256) * cdiv(N, 256) >= dev.cus ? 256 : 128;
         else {
-            default_tile(M, N, K, schedule, dev.cus, &t.bm, &t.bn);
-            // a wave layout, ring depth or kernel family asked for may exist
-            // only at the 256x256 tile
-            if (!find_variant(dtype, t))
-                t.bm = t.bn = 256;
+            // Stream-K / hybrid with neither a tile nor a grid (and no kernel
+            // asked for): the cost model picks both
+            const uint32_t kernel_flags =
+                GEMM_FLAG_PING_PONG | GEMM_FLAG_RING_KERNEL | GEMM_FLAG_STREAM_COPIES;
+            if ((schedule == GEMM_STREAMK || schedule == GEMM_HYBRID) && t.grid == 0 &&
+                t.bk == 0 && t.wave_m == 0 && t.wave_n == 0 && t.stages == 0 &&
+                !(t.flags & kernel_flags) &&
+                streamk_default_plan(M, N, K, dev.cus, &t.bm, &t.bn, &t.grid)) {
+                grid_from_model = true;
+            } else {
+                default_tile(M, N, K, schedule, dev.cus, &t.bm, &t.bn);
+                // a wave layout, ring depth or kernel family asked for may
+                // exist only at the 256x256 tile
+                if (!find_variant(dtype, t))
+                    t.bm = t.bn = 256;
+            }
         }
     } else if (t.bm == 0 || t.bn == 0) {
         set_error("give both bm and bn, or neither");
@@ -255,6 +342,7 @@ gemm_plan *create(int64_t M, int64_t N, int64_t K, gemm_dtype dtype, gemm_schedu
     p->device = device;
     p->spin_limit = kSpinLimit;
     p->drop_wg = -1;
+    p->grid_from_model = grid_from_model;
 
     int occ = dev.wg_per_cu > 0 ? dev.wg_per_cu : 1;
     if (query_occupancy) {
@@ -522,7 +610,7 @@ int gemm_plan_describe(const gemm_plan *p, char *buf, size_t len)
         snprintf(order, sizeof order, "rows");
     return snprintf(buf, buf ? len : 0,
                     "M,N,K=%lld,%lld,%lld %s C=%s %s tile=%dx%dx%d waves=%dx%d %s%d order=%s | tiles %dx%d=%d "
-                    "ipt=%d | T_sk=%d T_dp=%d I_sk=%lld g=%d q=%d r=%d | grid=%d x %d threads, "
+                    "ipt=%d | T_sk=%d T_dp=%d I_sk=%lld g=%d%s q=%d r=%d | grid=%d x %d threads, "
                     "lds=%zu B, capacity=%d wg, xcds=%d | fixup=%s pieces<=%d | pack A=%d B=%d | "
                     "workspace=%zu B",
                     (long long)p->M, (long long)p->N, (long long)p->K, dtype_name(p->dtype),
@@ -535,7 +623,8 @@ int gemm_plan_describe(const gemm_plan *p, char *buf, size_t len)
                     p->variant->kind ? p->variant->stages : 2,
                     order, p->P.tiles_m,
                     p->P.tiles_n, p->P.T, p->P.ipt, p->P.T_sk, p->P.T - p->P.T_sk,
-                    (long long)p->iters_sk, p->P.g, p->P.q, p->P.r, p->P.grid,
+                    (long long)p->iters_sk, p->P.g, p->grid_from_model ? " (cost model)" : "",
+                    p->P.q, p->P.r, p->P.grid,
                     p->variant->threads, p->variant->lds_bytes, p->wg_capacity, p->xcds,
                     p->P.T_sk == 0 ? "none"
                                    : (p->split_fixup == 2 ? "two-kernel"

@@ -169,6 +169,21 @@ def irregular_shapes(seed=20261202, count=16):
 
 
 # The five workloads: (name, M, N, K, dtype, distribution, scale, value seed).
+def log_sampled_shapes(n, seed=20261203, lo=256, hi=8192, step=256):
+    """n shapes (M, N, K), each dimension drawn log-uniformly in [lo, hi] and
+    rounded to a multiple of step (seeded).  The Triton Stream-K issue's shape
+    benchmark (its later revisions) takes the cube of a log-spaced grid of
+    sizes over the same range, rounded to multiples of 256; this draws from
+    the same distribution instead of walking the whole cube."""
+    import math
+    rnd = random.Random(seed)
+
+    def one():
+        v = math.exp(rnd.uniform(math.log(lo), math.log(hi)))
+        return int(min(hi, max(lo, round(v / step) * step)))
+    return [(one(), one(), one()) for _ in range(n)]
+
+
 WORKLOADS = {
     "fp32_256": dict(M=256, N=256, K=256, dtype="f32", dist="uniform", scale=1.0, seed=101),
     "fp16_4096": dict(M=4096, N=4096, K=4096, dtype="f16", dist="normal", scale=1.0, seed=102),

@@ -285,7 +285,7 @@ def test_fixup_mode_choice_and_workspace():
     p = plan(256, 512, 2048, "f16", "streamk", bm=64, bn=64, grid=82)
     assert p.info["max_pieces"] == 4 and p.info["split_fixup"] == 1
     # two pieces per tile are split too
-    p = plan(2372, 5997, 6089, "bf16", "streamk")
+    p = plan(2372, 5997, 6089, "bf16", "streamk", bm=256, bn=256, grid=256)
     assert p.info["max_pieces"] == 2 and p.info["split_fixup"] == 1
     # whole tiles only: nothing to fix up
     p = plan(4096, 4096, 4096, "f16", "streamk")
@@ -315,9 +315,10 @@ def test_split_tiles_per_workgroup_at_most_two():
     ((8192, 28672, 8192), "persistent", (256, 256)),  # 14 full waves
     ((1536, 1536, 8192), "dp", (128, 128)),           # 36 big tiles would idle 86% of the CUs
     ((5376, 256, 512), "dp", (128, 128)),
-    ((1536, 1536, 8192), "streamk", (256, 128)),      # few big tiles: the split tile is 256x128
-    ((512, 512, 65536), "hybrid", (256, 128)),
-    ((4096, 4096, 4096), "streamk", (256, 256)),
+    # Stream-K / hybrid: the planner's cost model (tests/test_grid_model.py)
+    ((1536, 1536, 8192), "streamk", (256, 256)),      # one workgroup per CU, 18 iterations each
+    ((512, 512, 65536), "hybrid", (128, 128)),        # 16 tiles in 16 pieces of 64 iterations
+    ((4096, 4096, 4096), "streamk", (256, 256)),      # one whole tile per CU
 ])
 def test_default_tile_follows_the_wave_model(shape, schedule, tile):
     M, N, K = shape
