@@ -156,7 +156,17 @@ typedef struct {
     int32_t bk;       /* k-depth of one MAC iteration, fixed per kernel: 64
                          for fp16/bf16, 32 for fp32, 128 for int8; 0 = any */
     int32_t grid;     /* g: workgroups of the persistent / Stream-K launch;
-                         0 = number of CUs (issue #1393 uses the SM count) */
+                         0 = number of CUs (issue #1393 uses the SM count).
+                         fp16/bf16 Stream-K and hybrid with bm = bn = 0 and
+                         grid = 0 (and no wave layout, stages or kernel
+                         flag): the planner picks the tile (256x256,
+                         256x128 or 128x128) and g from a cost model fitted
+                         on MI355X, among g = s*T that cut every tile into
+                         s equal pieces (s in 1, 2, 3, 4, 6, 8, 16 dividing
+                         the iterations per tile, g <= CUs) and g = CUs;
+                         where every tile shape gives more than CUs tiles,
+                         g = CUs.  (Issue #1393's benchmark picks g per
+                         shape from a sweep; a library call cannot.) */
     int32_t group_m;  /* tile-order group height (issue #1393 GROUP_M);
                          0 = 8, < 0 = plain row-major tile order (see also
                          GEMM_FLAG_HILBERT_ORDER) */
