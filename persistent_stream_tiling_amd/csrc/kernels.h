@@ -27,7 +27,8 @@ struct KernelArgs {
                            //    second kernel reduces the split tiles
     int32_t M, N, K;
     int32_t lda, ldb, ldc; // leading dimensions in elements
-    int32_t c_vec;         // 1: C rows allow whole 4-element vector stores
+    int32_t c_vec;         // 1: N % 4 == 0 and C 4-element aligned: vector stores in every
+                           //    tile (otherwise only in tiles left of column N)
     int32_t spin_limit;    // polls before a fixup wait gives up
     int32_t drop_signal_wg;// testing: this workgroup never raises its piece's flag (-1: none)
     Partition P;

@@ -199,9 +199,18 @@ __device__ __forceinline__ uint32_t bf16_bits(float x)
 // first row; an element outside C gets an out-of-range offset so its write is
 // dropped: no branches around the stores.  C is fp32, or fp16 / bf16 rounded
 // to nearest even from the fp32 sums (args.c_dtype, uniform per launch).
+//
+// A lane's four consecutive elements go out as one vector store when `vec`
+// (uniform): the four are then either all inside C or all outside, which
+// holds when N % 4 == 0 (args.c_vec) and in every tile that ends at or
+// before column N.  The vector's address is only element-aligned when N % 4
+// != 0; gfx950 runs with unaligned memory access enabled, as the repack's
+// 16-byte loads from element-aligned rows also rely on.  Otherwise (the tile
+// on the right edge of a C whose rows are not whole vectors) each element is
+// stored on its own.
 __device__ __forceinline__ void store_quad(const f32x4 &v, const KernelArgs &args,
                                            __amdgpu_buffer_rsrc_t c_rsrc, int m0, int n0, int row,
-                                           int col, int half, int g)
+                                           int col, int half, int g, bool vec)
 {
     const bool row_ok = m0 + row < args.M;
     const int n = n0 + col + 8 * g + 4 * half;
@@ -211,7 +220,7 @@ __device__ __forceinline__ void store_quad(const f32x4 &v, const KernelArgs &arg
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             h[e] = args.c_dtype == 1 ? f16_bits(v[e]) : bf16_bits(v[e]);
-        if (args.c_vec) {
+        if (vec) {
             const u32x2 u = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
             __builtin_amdgcn_raw_buffer_store_b64(
                 u, c_rsrc, (int)(row_ok && n < args.N ? off : kOutOfRange), 0, 0);
@@ -226,8 +235,8 @@ __device__ __forceinline__ void store_quad(const f32x4 &v, const KernelArgs &arg
     }
     const uint32_t off = (uint32_t)((row * args.ldc + n) * 4);
     const u32x4 u = u32x4{bits_of(v[0]), bits_of(v[1]), bits_of(v[2]), bits_of(v[3])};
-    if (args.c_vec) {
-        // N % 4 == 0: a vector is either wholly inside C or wholly outside
+    if (vec) {
+        // the vector is either wholly inside C or wholly outside
         __builtin_amdgcn_raw_buffer_store_b128(u, c_rsrc,
                                                (int)(row_ok && n < args.N ? off : kOutOfRange),
                                                0, 0);
@@ -247,12 +256,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t c_rows(const KernelArgs &args,
 
 __device__ __forceinline__ void store_block(const f32x16 &blk, const KernelArgs &args,
                                             __amdgpu_buffer_rsrc_t c_rsrc, int m0, int n0,
-                                            int row, int col, int half)
+                                            int row, int col, int half, bool vec)
 {
 #pragma unroll
     for (int g = 0; g < 4; ++g)
         store_quad(f32x4{blk[4 * g], blk[4 * g + 1], blk[4 * g + 2], blk[4 * g + 3]}, args,
-                   c_rsrc, m0, n0, row, col, half, g);
+                   c_rsrc, m0, n0, row, col, half, g, vec);
+}
+
+// Vector stores for a tile at columns n0 .. n0 + BN - 1 (see store_quad).
+template <int BN>
+__device__ __forceinline__ bool vector_stores(const KernelArgs &args, int n0)
+{
+    return args.c_vec || n0 + BN <= args.N;
 }
 
 // Wave 0 waits until the flags of workgroups q_first .. q_last are all set;
@@ -359,6 +375,7 @@ __device__ __forceinline__ void finish_tile(f32x16 (&acc)[MT][NT], const KernelA
         return;
     }
     const __amdgpu_buffer_rsrc_t c_rsrc = c_rows(args, m0);
+    const bool vec = vector_stores<BN>(args, n0);
     if (w.role == ROLE_OWNER) {
         // Head of a split tile: wait for every later workgroup on the tile,
         // then add their partials in ascending workgroup (= ascending k) order.
@@ -391,7 +408,7 @@ __device__ __forceinline__ void finish_tile(f32x16 (&acc)[MT][NT], const KernelA
                     }
                 }
                 store_block(blk, args, c_rsrc, m0, n0, row0 + mt * 32 + l32, col0 + nt * 32,
-                            half);
+                            half, vec);
             }
         return;
     }
@@ -400,15 +417,9 @@ __device__ __forceinline__ void finish_tile(f32x16 (&acc)[MT][NT], const KernelA
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
             store_block(acc[mt][nt], args, c_rsrc, m0, n0, row0 + mt * 32 + l32, col0 + nt * 32,
-                        half);
+                        half, vec);
 }
 
-// Split fixup, after the workgroup's MAC work: for each split tile it took
-// part in, reduce its share of the tile's 32x32 blocks.  Every element adds
-// the pieces in ascending k order (head piece first), which is the order the
-// head's workgroup would use, so the result does not depend on who reduces.
-// The last workgroup to finish with a tile clears its flags and counter.
-// Blocks are numbered in the writer's fragment order (wave, mt, nt).
 // Reduce blocks [b0, b1) of split tile t (pieces of workgroups pf .. pl) and
 // store them to C.  Every element adds the pieces in ascending k order (head
 // piece first), the order the head's workgroup would use, so the result does
@@ -427,6 +438,7 @@ __device__ __forceinline__ void reduce_tile_blocks(const KernelArgs &args, int32
     tile_coords(args.P, t, &tm, &tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const __amdgpu_buffer_rsrc_t c_rsrc = c_rows(args, m0);
+    const bool vec = vector_stores<BN>(args, n0);
     const __amdgpu_buffer_rsrc_t slots = make_rsrc(args.partials);
     const uint32_t slot_bytes = (uint32_t)(BM * BN * 4);
     constexpr int QB = 16;
@@ -453,7 +465,7 @@ __device__ __forceinline__ void reduce_tile_blocks(const KernelArgs &args, int32
                     sum = q0 + i == pf ? v[i] : acc_add4<IACC>(sum, v[i]);
         }
         store_quad(sum, args, c_rsrc, m0, n0, (ww / WN) * WTM + mt * 32 + l32,
-                   (ww % WN) * WTN + nt * 32, half, g);
+                   (ww % WN) * WTN + nt * 32, half, g, vec);
     }
 }
 
