@@ -146,7 +146,18 @@ enum {
     /* fp16/bf16: never the ping-pong kernel; 256x256 tiles then run the ring
      * kernel (kernel_kind 2), which is otherwise the default for the other
      * tiles (for comparing the two). */
-    GEMM_FLAG_RING_KERNEL = 1u << 12
+    GEMM_FLAG_RING_KERNEL = 1u << 12,
+    /* Stream-K / hybrid: cut each of the T_sk Stream-K tiles into
+     * s = min(floor(g / T_sk), ipt) pieces, one per workgroup, by the same
+     * even-split rule Stream-K applies to the whole range (pieces of
+     * floor(ipt/s) or ceil(ipt/s) iterations), instead of splitting all
+     * T_sk * ipt iterations evenly over the g workgroups.  No workgroup's
+     * range then crosses a tile boundary (a workgroup that runs pieces of two
+     * tiles pays a second pipeline fill and a second parked piece, and both
+     * tiles' fixups wait for it); workgroups p >= s * T_sk get no Stream-K
+     * work.  With g = s * T_sk and s dividing ipt this is the pages' own split
+     * (a fixed split-K).  Not on the pages.  Needs g >= T_sk. */
+    GEMM_FLAG_TILE_SPLIT = 1u << 13
 };
 
 /* Tile and schedule knobs.  Every field 0 means "default". */
@@ -317,7 +328,8 @@ typedef struct {
     int32_t tiles_sk;     /* T_sk: tiles [0, T_sk) are split by Stream-K */
     int32_t tiles_dp;     /* T - T_sk */
     int64_t iters_sk;     /* T_sk * ipt */
-    int32_t q, r;         /* iters_sk = q * g + r */
+    int32_t q, r;         /* iters_sk = q * g + r; with GEMM_FLAG_TILE_SPLIT
+                             ipt = q * pieces_per_tile + r */
     int32_t g;            /* Stream-K / persistent workgroup count */
     int32_t launch_grid;  /* workgroups launched */
     int32_t threads;      /* threads per workgroup */
@@ -325,6 +337,8 @@ typedef struct {
     int32_t pack_a, pack_b; /* operand repacked into the workspace */
     size_t workspace;
     size_t lds_bytes;
+    int32_t pieces_per_tile; /* GEMM_FLAG_TILE_SPLIT: s (each Stream-K tile cut
+                                into s pieces); 0 otherwise */
 } gemm_plan_info;
 
 int gemm_plan_get_info(const gemm_plan *plan, gemm_plan_info *out);

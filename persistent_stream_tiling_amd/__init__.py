@@ -6,7 +6,7 @@ marshals arguments.  PyTorch supplies device memory and the current stream.
 """
 from ._lib import (BF16, DP, DTYPES, F16, F32, I8, FLAG_C_INPUT_DTYPE,
                    FLAG_DEBUG_DROP_SIGNAL, FLAG_FIXUP_TWO_KERNEL, FLAG_STREAM_COPIES,
-                   FLAG_PING_PONG, FLAG_HILBERT_ORDER, FLAG_RING_KERNEL,
+                   FLAG_PING_PONG, FLAG_HILBERT_ORDER, FLAG_RING_KERNEL, FLAG_TILE_SPLIT,
                    FLAG_FIXUP_HEAD, FLAG_FIXUP_SPLIT, FLAG_NO_XCD_REMAP, FLAG_ONE_TILE, HYBRID,
                    PERSISTENT, ROLE_CONTRIB, ROLE_FULL, ROLE_OWNER, SCHEDULES, STREAMK, load,
                    variants)
@@ -16,4 +16,5 @@ __all__ = ["GemmPlan", "FixupError", "matmul", "plan_for_device", "load", "varia
            "SCHEDULES", "DTYPES", "DP", "PERSISTENT", "STREAMK", "HYBRID", "F32", "F16", "BF16",
            "I8", "FLAG_ONE_TILE", "FLAG_NO_XCD_REMAP", "FLAG_FIXUP_HEAD", "FLAG_FIXUP_SPLIT",
            "FLAG_C_INPUT_DTYPE", "FLAG_DEBUG_DROP_SIGNAL", "FLAG_FIXUP_TWO_KERNEL",
-           "FLAG_STREAM_COPIES", "FLAG_PING_PONG", "FLAG_HILBERT_ORDER", "FLAG_RING_KERNEL", "ROLE_FULL", "ROLE_CONTRIB", "ROLE_OWNER"]
+           "FLAG_STREAM_COPIES", "FLAG_PING_PONG", "FLAG_HILBERT_ORDER", "FLAG_RING_KERNEL",
+           "FLAG_TILE_SPLIT", "ROLE_FULL", "ROLE_CONTRIB", "ROLE_OWNER"]

@@ -18,6 +18,7 @@ FLAG_STREAM_COPIES = 1 << 9
 FLAG_HILBERT_ORDER = 1 << 10
 FLAG_PING_PONG = 1 << 11
 FLAG_RING_KERNEL = 1 << 12
+FLAG_TILE_SPLIT = 1 << 13
 ROLE_FULL, ROLE_CONTRIB, ROLE_OWNER = 0, 1, 2
 NOALLOC_MAX_WORKSPACE = 80 << 20  # GEMM_NOALLOC_MAX_WORKSPACE
 
@@ -52,7 +53,7 @@ class PlanInfo(ctypes.Structure):
                 ("threads", ctypes.c_int32), ("cus", ctypes.c_int32), ("xcds", ctypes.c_int32),
                 ("wg_capacity", ctypes.c_int32), ("pack_a", ctypes.c_int32),
                 ("pack_b", ctypes.c_int32), ("workspace", ctypes.c_size_t),
-                ("lds_bytes", ctypes.c_size_t)]
+                ("lds_bytes", ctypes.c_size_t), ("pieces_per_tile", ctypes.c_int32)]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}

@@ -400,9 +400,23 @@ gemm_plan *create(int64_t M, int64_t N, int64_t K, gemm_dtype dtype, gemm_schedu
         T_sk = 0;  // nothing to split: K = 0 is a fill, an empty C is a no-op
     P.T_sk = (int32_t)T_sk;
     p->iters_sk = T_sk * ipt;
-    if (T_sk > 0) {
+    if (T_sk > 0 && (t.flags & GEMM_FLAG_TILE_SPLIT)) {
+        // each Stream-K tile cut into s pieces, one per workgroup
+        if (g < T_sk) {
+            set_error("GEMM_FLAG_TILE_SPLIT needs g >= the %lld Stream-K tiles (g = %d)",
+                      (long long)T_sk, g);
+            delete p;
+            return nullptr;
+        }
+        const int64_t s = std::min<int64_t>(g / T_sk, ipt);
+        P.sk_split = (int32_t)s;
+        P.q = (int32_t)(ipt / s);
+        P.r = (int32_t)(ipt % s);
+    } else if (T_sk > 0) {
         P.q = (int32_t)(p->iters_sk / g);
         P.r = (int32_t)(p->iters_sk % g);
+    }
+    if (T_sk > 0) {
         // the in-kernel fixups wait on other workgroups, which must all be
         // running; the two-kernel fixup never waits
         if (g > p->wg_capacity && !(t.flags & GEMM_FLAG_FIXUP_TWO_KERNEL)) {
@@ -592,6 +606,7 @@ int gemm_plan_get_info(const gemm_plan *p, gemm_plan_info *o)
     o->pack_b = p->pack_b;
     o->workspace = p->ws_size;
     o->lds_bytes = p->variant->lds_bytes;
+    o->pieces_per_tile = p->P.sk_split;
     return 0;
 }
 
@@ -601,6 +616,9 @@ int gemm_plan_describe(const gemm_plan *p, char *buf, size_t len)
         set_error("NULL plan");
         return -1;
     }
+    char split[48] = "";
+    if (p->P.sk_split > 0)
+        snprintf(split, sizeof split, " tile-split x%d", p->P.sk_split);
     char order[32];
     if (p->P.hilbert)
         snprintf(order, sizeof order, "hilbert");
@@ -610,7 +628,7 @@ int gemm_plan_describe(const gemm_plan *p, char *buf, size_t len)
         snprintf(order, sizeof order, "rows");
     return snprintf(buf, buf ? len : 0,
                     "M,N,K=%lld,%lld,%lld %s C=%s %s tile=%dx%dx%d waves=%dx%d %s%d order=%s | tiles %dx%d=%d "
-                    "ipt=%d | T_sk=%d T_dp=%d I_sk=%lld g=%d%s q=%d r=%d | grid=%d x %d threads, "
+                    "ipt=%d | T_sk=%d T_dp=%d I_sk=%lld g=%d%s%s q=%d r=%d | grid=%d x %d threads, "
                     "lds=%zu B, capacity=%d wg, xcds=%d | fixup=%s pieces<=%d | pack A=%d B=%d | "
                     "workspace=%zu B",
                     (long long)p->M, (long long)p->N, (long long)p->K, dtype_name(p->dtype),
@@ -623,7 +641,7 @@ int gemm_plan_describe(const gemm_plan *p, char *buf, size_t len)
                     p->variant->kind ? p->variant->stages : 2,
                     order, p->P.tiles_m,
                     p->P.tiles_n, p->P.T, p->P.ipt, p->P.T_sk, p->P.T - p->P.T_sk,
-                    (long long)p->iters_sk, p->P.g, p->grid_from_model ? " (cost model)" : "",
+                    (long long)p->iters_sk, p->P.g, p->grid_from_model ? " (cost model)" : "", split,
                     p->P.q, p->P.r, p->P.grid,
                     p->variant->threads, p->variant->lds_bytes, p->wg_capacity, p->xcds,
                     p->P.T_sk == 0 ? "none"

@@ -13,6 +13,11 @@
 //   T_sk   tiles [0, T_sk) whose iterations are spread over the g workgroups
 //   q, r   T_sk * ipt = q * g + r; workgroup p owns iterations
 //          [p*q + min(p, r), (p+1)*q + min(p+1, r))
+// With a per-tile split (sk_split = s > 0, not on the pages) each Stream-K
+// tile t is instead cut into s pieces by the same rule, ipt = q * s + r:
+// workgroup p = t*s + j owns iterations t*ipt + [j*q + min(j, r),
+// (j+1)*q + min(j+1, r)), so no range crosses a tile boundary; workgroups
+// p >= s * T_sk get no Stream-K work.
 #pragma once
 
 #include <stdint.h>
@@ -38,6 +43,8 @@ struct Partition {
     int32_t k_aligned; // walk a Stream-K range as whole tiles, head piece, tail
                        // piece (see work_next); only with the split fixup
     int32_t hilbert;   // tile order: 1 = Hilbert curve over the tile grid
+    int32_t sk_split;  // 0: the even split of all T_sk * ipt iterations over g
+                       // workgroups; s > 0: each Stream-K tile cut into s pieces
 };
 
 GSK_HD int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
@@ -47,6 +54,12 @@ GSK_HD int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
 // by at most one (issue #1393, the first-wave kernel's start/last iteration).
 GSK_HD int64_t sk_begin(const Partition &P, int64_t p)
 {
+    if (P.sk_split > 0) {
+        const int64_t t = p / P.sk_split, j = p - t * P.sk_split;
+        if (t >= P.T_sk)
+            return (int64_t)P.T_sk * P.ipt;
+        return t * P.ipt + j * P.q + min64(j, P.r);
+    }
     return p * P.q + min64(p, P.r);
 }
 
@@ -55,6 +68,12 @@ GSK_HD int64_t sk_begin(const Partition &P, int64_t p)
 GSK_HD int32_t sk_wg_of_iter(const Partition &P, int64_t it)
 {
     int64_t long_part = (int64_t)P.r * (P.q + 1);  // the r ranges of length q+1
+    if (P.sk_split > 0) {
+        // within tile t, the same rule over its ipt iterations (q >= 1)
+        const int64_t t = it / P.ipt, k = it - t * P.ipt;
+        const int64_t j = k < long_part ? k / (P.q + 1) : P.r + (k - long_part) / P.q;
+        return (int32_t)(t * P.sk_split + j);
+    }
     if (it < long_part)
         return (int32_t)(it / (P.q + 1));
     return (int32_t)(P.r + (it - long_part) / P.q);  // q > 0 whenever this is reached

@@ -39,7 +39,7 @@ using namespace gsk;
 struct Header {
     int32_t M, N, K, bm, bn, bk;
     int32_t tiles_m, tiles_n, T, ipt, T_sk, g, q, r, grid, group_m, xcds, k_aligned;
-    int32_t split, drop, spin_limit, seed, jitter_us, reserved;
+    int32_t split, drop, spin_limit, seed, jitter_us, sk_split;
 };
 
 struct Shared {
@@ -186,6 +186,7 @@ int main(int argc, char **argv)
     P.group_m = h.group_m;
     P.xcds = h.xcds;
     P.k_aligned = h.k_aligned;
+    P.sk_split = h.sk_split;
     const size_t slots = h.split ? 2 * (size_t)h.g : (size_t)h.g;
     Shared S(h, slots, (size_t)(h.T_sk > 0 ? h.T_sk : 1));
     S.P = P;

@@ -55,7 +55,8 @@ def emulate(exe, plan, a, b, tmp_path, seed, jitter_us=200, drop=-1, spin_limit=
     split = i["split_fixup"] if split is None else split
     header = [M, N, K, i["bm"], i["bn"], i["bk"], i["tiles_m"], i["tiles_n"], i["tiles"],
               i["iters_per_tile"], i["tiles_sk"], i["g"], i["q"], i["r"], i["launch_grid"],
-              i["group_m"], 1, split, split, drop, spin_limit, seed, jitter_us, 0]
+              i["group_m"], 1, split, split, drop, spin_limit, seed, jitter_us,
+              i["pieces_per_tile"]]
     src, dst = tmp_path / f"in{seed}", tmp_path / f"out{seed}"
     with open(src, "wb") as f:
         f.write(struct.pack("<24i", *header))
@@ -74,6 +75,9 @@ CASES = [
     (300, 200, 704, "hybrid", dict(bm=64, bn=64), 7),
     (128, 96, 4096, "streamk", dict(bm=64, bn=64), 23),
     (257, 203, 701, "hybrid", dict(bm=128, bn=128), 5),
+    # each Stream-K tile cut into its own pieces (GEMM_FLAG_TILE_SPLIT)
+    (200, 136, 2050, "streamk", dict(bm=64, bn=64, flags=gsk.FLAG_TILE_SPLIT), 37),
+    (257, 203, 701, "hybrid", dict(bm=64, bn=64, flags=gsk.FLAG_TILE_SPLIT | gsk.FLAG_ONE_TILE), 17),
 ]
 
 
@@ -85,7 +89,9 @@ def test_interleavings_and_fixup_modes_agree_bitwise(case, emulator, tmp_path):
     ref, scale = oracle.gemm(a_bits, b_bits, "f32")
     outs = []
     for flag in (gsk.FLAG_FIXUP_HEAD, gsk.FLAG_FIXUP_SPLIT, gsk.FLAG_FIXUP_TWO_KERNEL):
-        plan = gsk.plan_for_device(M, N, K, "f32", sched, grid=g, flags=flag, **tiles)
+        t = dict(tiles)
+        t["flags"] = t.get("flags", 0) | flag
+        plan = gsk.plan_for_device(M, N, K, "f32", sched, grid=g, **t)
         assert plan.info["max_pieces"] >= 2
         for seed in (1, 2, 3):
             status, c, _ = emulate(emulator, plan, a, b, tmp_path, seed)

@@ -65,14 +65,31 @@ def check_plan(p):
     if T and ipt:
         assert (cover == 1).all(), "every (tile, k-iteration) pair exactly once"
 
-    # Stream-K ranges: contiguous, ascending, lengths q or q+1
+    # Stream-K ranges: contiguous, ascending, lengths q or q+1 (per-tile split:
+    # each tile cut into s such ranges, workgroups past s * T_sk idle)
+    s = info["pieces_per_tile"]
+
+    def sk_begin(w):
+        if s == 0:
+            return w * q + min(w, r)
+        t, j = divmod(w, s)
+        return T_sk * ipt if t >= T_sk else t * ipt + j * q + min(j, r)
     if T_sk:
-        assert info["iters_sk"] == T_sk * ipt == q * g + r
+        if s:
+            assert ipt == q * s + r and 1 <= s <= ipt and s * T_sk <= g
+        else:
+            assert info["iters_sk"] == T_sk * ipt == q * g + r
         prev_end = 0
         for w in range(g):
             its = [t * ipt + k for (t, kb, ke, _, _) in segs[w] if t < T_sk for k in range(kb, ke)]
-            begin = w * q + min(w, r)
-            end = (w + 1) * q + min(w + 1, r)
+            begin, end = sk_begin(w), sk_begin(w + 1)
+            if s:
+                # no range crosses a tile boundary
+                assert begin == end or begin // ipt == (end - 1) // ipt
+                if w >= s * T_sk:
+                    assert begin == end
+                    prev_end = end
+                    continue
             # the walk may reorder whole segments (k-aligned mode), never iterations
             assert sorted(its) == list(range(begin, end))
             if not split:
@@ -119,6 +136,50 @@ CONFIGS = [
 def test_invariants_on_workloads(cfg, schedule):
     M, N, K, dt, kw = cfg
     check_plan(plan(M, N, K, dt, schedule, **kw))
+
+
+TILE_SPLIT_CASES = [
+    # (M, N, K, dtype, tiles, schedule, g): s = min(g // T_sk, ipt)
+    (1536, 1536, 8192, "f16", dict(bm=256, bn=256), "streamk", 256),   # 36 tiles x 7, 4 idle
+    (1536, 1536, 8192, "f16", dict(bm=256, bn=128), "streamk", 256),   # 72 tiles x 3
+    (512, 512, 65536, "bf16", dict(bm=256, bn=128), "streamk", 256),   # 8 x 32: even split
+    (300, 200, 704, "f16", dict(bm=64, bn=64), "streamk", 37),         # 20 tiles x 1: whole tiles
+    (300, 200, 100, "f16", dict(bm=128, bn=128), "streamk", 256),      # s clamped to ipt = 2
+    (257, 203, 701, "f32", dict(bm=64, bn=64), "streamk", 100),        # 20 tiles x 5, ragged
+    (4000, 3000, 2000, "f16", dict(bm=256, bn=256), "hybrid", 256),    # one-tile hybrid below
+    (2000, 900, 3000, "bf16", dict(bm=128, bn=128), "streamk", 201),   # odd g
+]
+
+
+@pytest.mark.parametrize("fixup", [0, gsk.FLAG_FIXUP_HEAD, gsk.FLAG_FIXUP_TWO_KERNEL])
+@pytest.mark.parametrize("case", TILE_SPLIT_CASES, ids=lambda c: f"{c[0]}x{c[1]}x{c[2]}-{c[5]}-g{c[6]}")
+def test_tile_split_partitions(case, fixup):
+    M, N, K, dt, tiles, schedule, g = case
+    flags = gsk.FLAG_TILE_SPLIT | fixup | (gsk.FLAG_ONE_TILE if schedule == "hybrid" else 0)
+    p = plan(M, N, K, dt, schedule, grid=g, flags=flags, **tiles)
+    i = p.info
+    ipt, T_sk = i["iters_per_tile"], i["tiles_sk"]
+    s = min(g // T_sk, ipt)
+    assert i["pieces_per_tile"] == s and (i["q"], i["r"]) == divmod(ipt, s)
+    assert i["max_pieces"] == s and "tile-split" in p.describe()
+    check_plan(p)
+    # every Stream-K tile has exactly s workgroups, t*s .. t*s + s - 1
+    segs = all_segments(p)
+    for t in range(T_sk):
+        holders = sorted({w for w in range(g) for seg in segs[w] if seg[0] == t})
+        assert holders == list(range(t * s, t * s + s))
+
+
+def test_tile_split_needs_a_grid_of_at_least_the_stream_k_tiles():
+    with pytest.raises(ValueError, match="TILE_SPLIT"):
+        plan(1536, 1536, 8192, "f16", "streamk", bm=128, bn=128, grid=100,
+             flags=gsk.FLAG_TILE_SPLIT)
+    # two-tile hybrid: T_sk = T mod g + g can exceed g (192 tiles, g = 80: T_sk = 112)
+    with pytest.raises(ValueError, match="TILE_SPLIT"):
+        plan(4000, 3000, 2000, "f16", "hybrid", bm=256, bn=256, grid=80,
+             flags=gsk.FLAG_TILE_SPLIT)
+    # no Stream-K tiles: the flag changes nothing
+    assert plan(4096, 4096, 4096, "f16", "dp", flags=gsk.FLAG_TILE_SPLIT).info["pieces_per_tile"] == 0
 
 
 def test_invariants_large_mlp_shape():

@@ -8,8 +8,9 @@ in all four schedules on two shapes:
   (both operands repacked), every element compared;
 - 320 x 200 x 9000 (a few tiles, long K): Stream-K and hybrid at g = 256 and
   g = 37 split every tile into pieces, in the in-kernel split fixup, the head
-  fixup and the two-kernel fixup; compared on seeded samples plus the ragged
-  edges.
+  fixup and the two-kernel fixup, with Stream-K's even split of all the
+  iterations and with each tile cut into its own pieces (GEMM_FLAG_TILE_SPLIT);
+  compared on seeded samples plus the ragged edges.
 
 Integer-valued inputs (int8) must match exactly; the others within
 tol * sum_k |a_ik||b_kj|.
@@ -115,11 +116,16 @@ def test_variant_split_long_k(v):
             continue
         for g in (0, 37):
             for fix in (gsk.FLAG_FIXUP_SPLIT, gsk.FLAG_FIXUP_HEAD, gsk.FLAG_FIXUP_TWO_KERNEL):
-                t = _tiles(v)
-                t["flags"] = t.get("flags", 0) | fix
-                plan, ws, c = run_gemm(da, db, M, N, K, dtype, sched, grid=g, **t)
-                assert plan.info["max_pieces"] >= 2, plan.describe()
-                _check(plan, c, idx, ref, scale, dtype, v)
+                for split in (0, gsk.FLAG_TILE_SPLIT):
+                    t = _tiles(v)
+                    t["flags"] = t.get("flags", 0) | fix | split
+                    plan, ws, c = run_gemm(da, db, M, N, K, dtype, sched, grid=g, **t)
+                    s = plan.info["pieces_per_tile"]
+                    assert (s > 0) == (split != 0)
+                    # (a per-tile split over fewer workgroups than twice the
+                    # tiles leaves every tile whole)
+                    assert plan.info["max_pieces"] >= 2 or s == 1, plan.describe()
+                    _check(plan, c, idx, ref, scale, dtype, v)
 
 
 PP_SHAPES = [(257, 203, 701), (512, 768, 1000), (300, 520, 4096), (1024, 1024, 2112)]
