@@ -214,8 +214,12 @@ def schedule_table(args, out):
     lines = [f"# Schedules per workload: `python bench.py --workload {args.workload} "
              f"--steps {args.steps} --table <file>`", "",
              f"Kernel source hash: {kernel_source_hash()}.  Median of {TABLE_ROUNDS * per} timed "
-             "runs per schedule (rounds interleaved, 512 MiB cache flush before each run), tuned "
-             "tiles, default grid (one workgroup per CU); one process per workload.", "",
+             "runs per schedule (rounds interleaved, 512 MiB cache flush before each run), each "
+             "schedule in its tuned launch configuration (tuning.py: tile, order, copy hint, "
+             "Stream-K partition; grid one workgroup per CU, or the library's default plan where "
+             "the entry is empty); one process per workload.  'splits tiles' names the Stream-K "
+             "partition: the pages' even split of all iterations over the workgroups, or each tile "
+             "cut into its own pieces (GEMM_FLAG_TILE_SPLIT).", "",
              "| workload | M x N x K | tiles T | dp us | persistent us | Stream-K us | hybrid us "
              "| best | best TFLOP/s | Stream-K / DP | hybrid / DP | Stream-K splits tiles | "
              "hybrid T_sk (splits) |",
@@ -260,8 +264,11 @@ def schedule_table_row(args):
         best = min(med, key=med.get)
         T = runs["dp"][0].info["tiles"]
         sk, hy = runs["streamk"][0].info, runs["hybrid"][0].info
-        sk_split = "yes" if sk["max_pieces"] >= 2 else "no"
-        hy_split = f"{hy['tiles_sk']} ({'yes' if hy['tiles_sk'] and hy['max_pieces'] >= 2 else 'no'})"
+        def how(i):  # Stream-K partition: the even split, or each tile in its own pieces
+            return f"per-tile x{i['pieces_per_tile']}" if i["pieces_per_tile"] else "even split"
+        sk_split = f"yes, {how(sk)}" if sk["max_pieces"] >= 2 else "no"
+        hy_split = (f"{hy['tiles_sk']} (yes, {how(hy)})" if hy["tiles_sk"] and hy["max_pieces"] >= 2
+                    else f"{hy['tiles_sk']} (no)")
         print(f"| {name} | {M} x {N} x {K} | {T} | " +
               " | ".join(f"{med[s]:.1f}" for s in SCHEDULES) +
               f" | {best} | {2.0 * M * N * K / (med[best] * 1e-6) / 1e12:.0f} | "
@@ -269,7 +276,8 @@ def schedule_table_row(args):
               f"{sk_split} | {hy_split} |", flush=True)
 
 
-SWEEP_VARIANTS = (("streamk", 0), ("hybrid", 0), ("hybrid", "one_tile"), ("streamk", "two_kernel"))
+SWEEP_VARIANTS = (("streamk", 0), ("streamk", "tile_split"), ("hybrid", 0), ("hybrid", "tile_split"),
+                  ("hybrid", "one_tile"), ("streamk", "two_kernel"))
 
 
 def sweep_grids(name, T):
@@ -305,7 +313,9 @@ def grid_sweep(args, out):
              "above 256 are refused by the in-kernel fixups (they need every workgroup "
              "resident); `two_kernel` parks every piece and reduces the split tiles in a second "
              "kernel, which allows them.  `one_tile` is the hybrid without two_tiles (Stream-K "
-             "over T mod g tiles only).", "",
+             "over T mod g tiles only).  `tile_split` cuts each Stream-K tile into its own "
+             "floor(g / T_sk) pieces (GEMM_FLAG_TILE_SPLIT) instead of splitting all the "
+             "iterations evenly; the other lines use the even split.", "",
              "| workload | tiles T | schedule | g | T_sk | splits tiles | us | TFLOP/s | DP us "
              "(interleaved) | DP / this |",
              "|---|---|---|---|---|---|---|---|---|---|"]
@@ -322,7 +332,8 @@ def grid_sweep(args, out):
 def grid_sweep_rows(args):
     import torch
     import persistent_stream_tiling_amd as gsk
-    from persistent_stream_tiling_amd import FLAG_FIXUP_TWO_KERNEL, FLAG_ONE_TILE, inputs, tuning
+    from persistent_stream_tiling_amd import (FLAG_FIXUP_TWO_KERNEL, FLAG_ONE_TILE, FLAG_TILE_SPLIT,
+                                              inputs, tuning)
     wl = workload_table()[args.workload]
     M, N, K, dt = wl["M"], wl["N"], wl["K"], wl["dtype"]
     log(f"[sweep] {args.workload}: {M}x{N}x{K} {dt}")
@@ -350,6 +361,10 @@ def grid_sweep_rows(args):
     dp_ws = dp.new_workspace()
     for sched, variant in SWEEP_VARIANTS:
         tiles = tuning.bench_tiles(args.workload, sched, dt)
+        # the partition is the variant's: Stream-K's even split unless tile_split
+        tiles["flags"] = tiles.get("flags", 0) & ~FLAG_TILE_SPLIT
+        if variant == "tile_split":
+            tiles["flags"] |= FLAG_TILE_SPLIT
         if variant == "one_tile":
             tiles["flags"] = tiles.get("flags", 0) | FLAG_ONE_TILE
         if variant == "two_kernel":

@@ -5,7 +5,7 @@ exactly these, so what is measured is what is checked.  fp16/bf16 256x256
 tiles in the default wave layout run the library's default kernel for that
 tile, the wave-specialised ping-pong kernel.
 """
-from ._lib import FLAG_NO_XCD_REMAP, FLAG_STREAM_COPIES
+from ._lib import FLAG_NO_XCD_REMAP, FLAG_STREAM_COPIES, FLAG_TILE_SPLIT
 
 SCHEDULES = ("dp", "persistent", "streamk", "hybrid")
 
@@ -50,80 +50,83 @@ BENCH_TILES = {
 
 
 # The 16 seeded irregular bf16 shapes: each schedule's fastest tile, wave layout,
-# workgroup order and copy hint from a sweep on MI355X (median of 8 cold runs; DP and
-# persistent over 256x256, 256x128, 128x256, 128x128; Stream-K and hybrid over 256x256
-# and 256x128 with die-contiguous or hardware order and plain or non-temporal copies).
+# workgroup order, copy hint and Stream-K partition from a sweep on MI355X (median of
+# 8 cold runs, rounds interleaved over every configuration of a shape; DP and
+# persistent over 256x256, 256x128, 128x256, 128x128; Stream-K and hybrid over the
+# library's default plan and 256x256 and 256x128 with die-contiguous or hardware
+# order, plain or non-temporal copies, and Stream-K's even split or per-tile pieces
+# (FLAG_TILE_SPLIT)).  dict() is the library's default plan.
 IRREGULAR_TILES = {
     "bf16_irregular_00_2372x5997x6089": dict(
         dp=dict(bm=256, bn=256),
         persistent=dict(bm=256, bn=256),
-        streamk=dict(bm=256, bn=128, wave_m=4, wave_n=2),
-        hybrid=dict(bm=256, bn=128, wave_m=4, wave_n=2)),
+        streamk=dict(bm=256, bn=256, flags=FLAG_NO_XCD_REMAP | FLAG_TILE_SPLIT),
+        hybrid=dict(bm=256, bn=256, flags=FLAG_NO_XCD_REMAP | FLAG_TILE_SPLIT)),
     "bf16_irregular_01_1095x6981x15363": dict(
         dp=dict(bm=128, bn=256),
         persistent=dict(bm=128, bn=256),
         streamk=dict(bm=256, bn=256),
-        hybrid=dict(bm=256, bn=128, wave_m=4, wave_n=2)),
+        hybrid=dict(bm=256, bn=128, wave_m=4, wave_n=2, flags=FLAG_TILE_SPLIT)),
     "bf16_irregular_02_2086x5147x4877": dict(
         dp=dict(bm=256, bn=256),
         persistent=dict(bm=256, bn=256),
-        streamk=dict(bm=256, bn=128, wave_m=4, wave_n=2),
-        hybrid=dict(bm=256, bn=128, wave_m=4, wave_n=2)),
+        streamk=dict(bm=256, bn=256, flags=FLAG_NO_XCD_REMAP | FLAG_TILE_SPLIT),
+        hybrid=dict(bm=256, bn=256, flags=FLAG_NO_XCD_REMAP | FLAG_TILE_SPLIT)),
     "bf16_irregular_03_5477x2935x1139": dict(
-        dp=dict(bm=256, bn=128),
+        dp=dict(bm=128, bn=128),
         persistent=dict(bm=256, bn=128),
-        streamk=dict(bm=256, bn=128, wave_m=4, wave_n=2),
-        hybrid=dict(bm=256, bn=128, wave_m=4, wave_n=2, flags=FLAG_NO_XCD_REMAP)),
+        streamk=dict(bm=256, bn=128, wave_m=4, wave_n=2, flags=FLAG_NO_XCD_REMAP),
+        hybrid=dict(bm=256, bn=128, wave_m=4, wave_n=2, flags=FLAG_NO_XCD_REMAP | FLAG_TILE_SPLIT)),
     "bf16_irregular_04_3470x4884x10138": dict(
-        dp=dict(bm=128, bn=256),
+        dp=dict(bm=256, bn=256),
         persistent=dict(bm=128, bn=256),
         streamk=dict(bm=256, bn=256),
-        hybrid=dict(bm=256, bn=256, flags=FLAG_NO_XCD_REMAP)),
+        hybrid=dict(bm=256, bn=256, flags=FLAG_NO_XCD_REMAP | FLAG_TILE_SPLIT)),
     "bf16_irregular_05_1295x7998x6460": dict(
         dp=dict(bm=256, bn=256),
         persistent=dict(bm=256, bn=256),
-        streamk=dict(bm=256, bn=128, wave_m=4, wave_n=2),
-        hybrid=dict(bm=256, bn=128, wave_m=4, wave_n=2)),
+        streamk=dict(),
+        hybrid=dict(bm=256, bn=256, flags=FLAG_NO_XCD_REMAP | FLAG_TILE_SPLIT)),
     "bf16_irregular_06_6347x2237x3547": dict(
         dp=dict(bm=256, bn=256),
         persistent=dict(bm=256, bn=256),
-        streamk=dict(bm=256, bn=128, wave_m=4, wave_n=2),
-        hybrid=dict(bm=256, bn=128, wave_m=4, wave_n=2)),
+        streamk=dict(bm=256, bn=256, flags=FLAG_NO_XCD_REMAP | FLAG_TILE_SPLIT),
+        hybrid=dict(bm=256, bn=256, flags=FLAG_NO_XCD_REMAP | FLAG_TILE_SPLIT)),
     "bf16_irregular_07_1613x5603x2096": dict(
         dp=dict(bm=256, bn=256),
         persistent=dict(bm=256, bn=256),
-        streamk=dict(bm=256, bn=256),
-        hybrid=dict(bm=256, bn=128, wave_m=4, wave_n=2)),
+        streamk=dict(),
+        hybrid=dict(bm=256, bn=128, wave_m=4, wave_n=2, flags=FLAG_TILE_SPLIT)),
     "bf16_irregular_08_6620x3734x6086": dict(
         dp=dict(bm=256, bn=256),
         persistent=dict(bm=256, bn=256),
         streamk=dict(bm=256, bn=256),
-        hybrid=dict(bm=256, bn=256)),
+        hybrid=dict(bm=256, bn=256, flags=FLAG_NO_XCD_REMAP | FLAG_TILE_SPLIT)),
     "bf16_irregular_09_6446x6520x7081": dict(
         dp=dict(bm=256, bn=256),
         persistent=dict(bm=256, bn=256),
-        streamk=dict(bm=256, bn=256),
+        streamk=dict(),
         hybrid=dict(bm=256, bn=256)),
     "bf16_irregular_10_5081x4376x4677": dict(
         dp=dict(bm=256, bn=256),
         persistent=dict(bm=128, bn=256),
         streamk=dict(bm=256, bn=256),
-        hybrid=dict(bm=256, bn=256)),
+        hybrid=dict(bm=256, bn=256, flags=FLAG_NO_XCD_REMAP | FLAG_TILE_SPLIT)),
     "bf16_irregular_11_4622x6539x9711": dict(
         dp=dict(bm=256, bn=256),
         persistent=dict(bm=256, bn=256),
-        streamk=dict(bm=256, bn=256),
-        hybrid=dict(bm=256, bn=256)),
+        streamk=dict(),
+        hybrid=dict(bm=256, bn=256, flags=FLAG_NO_XCD_REMAP | FLAG_TILE_SPLIT)),
     "bf16_irregular_12_3374x4491x2854": dict(
         dp=dict(bm=256, bn=256),
         persistent=dict(bm=256, bn=256),
-        streamk=dict(bm=256, bn=256),
-        hybrid=dict(bm=256, bn=256, flags=FLAG_NO_XCD_REMAP)),
+        streamk=dict(),
+        hybrid=dict()),
     "bf16_irregular_13_4141x5473x12021": dict(
         dp=dict(bm=256, bn=256),
         persistent=dict(bm=128, bn=256),
         streamk=dict(bm=256, bn=256),
-        hybrid=dict(bm=256, bn=256)),
+        hybrid=dict(bm=256, bn=256, flags=FLAG_NO_XCD_REMAP | FLAG_TILE_SPLIT)),
     "bf16_irregular_14_6262x5667x14876": dict(
         dp=dict(bm=256, bn=256),
         persistent=dict(bm=256, bn=256),
@@ -132,8 +135,8 @@ IRREGULAR_TILES = {
     "bf16_irregular_15_2108x4087x8760": dict(
         dp=dict(bm=256, bn=256),
         persistent=dict(bm=256, bn=256),
-        streamk=dict(bm=256, bn=256),
-        hybrid=dict(bm=256, bn=128, wave_m=4, wave_n=2, flags=FLAG_NO_XCD_REMAP)),
+        streamk=dict(),
+        hybrid=dict(bm=256, bn=128, wave_m=4, wave_n=2, flags=FLAG_NO_XCD_REMAP | FLAG_TILE_SPLIT)),
 }
 
 BENCH_TILES.update(IRREGULAR_TILES)
