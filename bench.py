@@ -369,7 +369,8 @@ def grid_sweep_rows(args):
             tiles["flags"] = tiles.get("flags", 0) | FLAG_ONE_TILE
         if variant == "two_kernel":
             tiles["flags"] = tiles.get("flags", 0) | FLAG_FIXUP_TWO_KERNEL
-        T = gsk.GemmPlan(M, N, K, dt, sched, **tiles).info["tiles"]
+        T = gsk.GemmPlan(M, N, K, dt, sched,
+                         **dict(tiles, flags=tiles["flags"] & ~FLAG_TILE_SPLIT)).info["tiles"]
         label = sched + (f" {variant}" if variant else "")
         for g in sweep_grids(args.workload, T):
             try:
