@@ -181,9 +181,10 @@ bool streamk_default_plan(int64_t M, int64_t N, int64_t K, int cus, int *bm, int
 const Variant *find_variant(int dtype, const gemm_tiles &t)
 {
     // fp16/bf16 prefer the direct-to-LDS ring kernel and fall back to the
-    // register-staged one for tiles it does not cover (64x64); fp32 and int8
-    // run the register-staged kernel
-    const bool staged_only = dtype == GEMM_F32 || dtype == GEMM_I8;
+    // register-staged one for tiles it does not cover (64x64); int8 has the
+    // ping-pong kernel (256x256) and the register-staged one; fp32 runs the
+    // register-staged kernel only
+    const bool staged_only = dtype == GEMM_F32;
     int n = 0;
     const Variant *v = variants(&n);
     // kinds in order of preference: the ping-pong kernel where one is built

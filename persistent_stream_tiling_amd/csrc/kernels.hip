@@ -724,6 +724,12 @@ __device__ __forceinline__ uint32_t swz_b(int krow)
     return (0xCA60u >> ((krow & 3) * 4)) & 0xF;  // {0, 6, 10, 12}[krow & 3]
 }
 
+// int8 B (256-byte k-rows, read with ds_read_b64_tr_b8): chunk c of k-row r
+// sits at c ^ 2*(r & 7).  A 32-lane half of a read touches 8 k-rows at two
+// adjacent chunks (even c, c + 1), in both 8-byte halves: the 8 distinct
+// even offsets 2*(r & 7) put the 32 reads on 32 distinct 8-byte bank pairs.
+__device__ __forceinline__ uint32_t swz_b8(int krow) { return (uint32_t)(krow & 7) << 1; }
+
 __device__ __forceinline__ void barrier_only()
 {
     // A workgroup barrier with no memory fence: the copies it orders are
@@ -734,6 +740,7 @@ __device__ __forceinline__ void barrier_only()
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int s32x2 __attribute__((ext_vector_type(2)));
 #define GSK_LDS(T, p) ((__attribute__((address_space(3))) T *)(p))
 
 // Raw buffer descriptor (base, no stride, 2^31 - 1 bytes, untyped) as four
@@ -828,17 +835,20 @@ __device__ __forceinline__ void wait_vmcnt()
 template <int DT, int BM, int BN, int WM, int WN>
 struct PairTile {
     static constexpr int NW = WM * WN, NTH = 64 * NW;
-    static constexpr int BK = 64, HK = 32;                 // iteration and half depth
+    static constexpr int E = DT == 3 ? 1 : 2;              // bytes per element
+    static constexpr int V = 16 / E;                       // elements per 16-byte chunk
+    // iteration and half depth: one 128-byte A row segment per iteration
+    static constexpr int BK = 128 / E, HK = 64 / E;
     static constexpr int SA = 3, SB = 4;                   // A slots, B stages
-    static constexpr int B_ROW = BN * 2;                   // bytes per B k-row
-    static constexpr int A_SLOT = BM * 128, B_STAGE = HK * BN * 2;
+    static constexpr int B_ROW = BN * E;                   // bytes per B k-row
+    static constexpr int A_SLOT = BM * 128, B_STAGE = HK * BN * E;
     static constexpr int A_BASE = SB * B_STAGE;
     static constexpr int LDS = SB * B_STAGE + SA * A_SLOT;
     static constexpr int A_INSTR = A_SLOT / 2 / 1024 / NW; // 1 KiB copies per wave and half slab
     static constexpr int B_INSTR = B_STAGE / 1024 / NW;
     static constexpr int LPI = A_INSTR + B_INSTR;          // copies per wave and half-iteration
     static constexpr int WTM = BM / WM, WTN = BN / WN, MT = WTM / 32, NT = WTN / 32;
-    static_assert(DT == 1 || DT == 2, "fp16 / bf16 only");
+    static_assert(DT == 1 || DT == 2 || DT == 3, "fp16 / bf16 / int8 only");
     static_assert(A_INSTR >= 1 && A_INSTR * 2 * 1024 * NW == A_SLOT &&
                       B_INSTR >= 1 && B_INSTR * 1024 * NW == B_STAGE,
                   "copies must split evenly over the waves");
@@ -861,6 +871,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel_pair(KernelArgs a
     constexpr int NMFMA = MT * NT;  // MFMAs per slab
     constexpr int NREAD = MT + NT;  // fragment reads per slab
     static_assert(2 * NMFMA >= NREAD, "two fragment reads per MFMA");
+    static_assert(DT == 1 || DT == 2, "the ring kernel's B layout is for 16-bit elements");
 
     __shared__ __attribute__((aligned(1024))) uint8_t lds[Cfg::LDS];
 
@@ -1140,6 +1151,7 @@ __device__ __forceinline__ void gemm_pp_group(const KernelArgs &args, uint8_t *l
     constexpr int MT = Cfg::MT, NT = Cfg::NT, HK = Cfg::HK, BK = Cfg::BK;
     constexpr int A_SLOT = Cfg::A_SLOT, B_STAGE = Cfg::B_STAGE, A_BASE = Cfg::A_BASE;
     constexpr int B_ROW = Cfg::B_ROW, SB = Cfg::SB, SA = Cfg::SA;
+    constexpr int E = Cfg::E, V = Cfg::V;  // bytes per element, elements per 16-byte chunk
     static_assert(MT == 4 && NT == 2 && SB == 4 && SA == 3, "256x256, 2x4 waves");
     const Partition &P = args.P;
     const int wave = GRP * 4 + q;
@@ -1150,16 +1162,21 @@ __device__ __forceinline__ void gemm_pp_group(const KernelArgs &args, uint8_t *l
     // 16 KiB piece.  Group 0: rows 8*(4j + q) + lane/8 of the A row half,
     // position lane & 7 holding 16-byte chunk (lane & 7) ^ swizzle(row) (the
     // swizzle is the same for both row halves: they differ by 128 rows).
-    // Group 1: k-rows 2*(4j + q) + lane/32 of the B stage.
+    // Group 1: k-rows 2*(4j + q) + lane/32 of the B stage (512-byte rows of
+    // 16-bit elements), or 4*(4j + q) + lane/16 (256-byte rows of int8), each
+    // position holding the swizzled 16-byte chunk of its row (swz_b, swz_b8).
     int cp_row[4], cp_chunk[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         if constexpr (GRP == 0) {
             cp_row[j] = 8 * (4 * j + q) + (lane >> 3);
             cp_chunk[j] = (lane & 7) ^ (int)swz_row128(cp_row[j]);
-        } else {
+        } else if constexpr (E == 2) {
             cp_row[j] = 2 * (4 * j + q) + (lane >> 5);
             cp_chunk[j] = (lane & 31) ^ (int)swz_b(cp_row[j]);
+        } else {
+            cp_row[j] = 4 * (4 * j + q) + (lane >> 4);
+            cp_chunk[j] = (lane & 15) ^ (int)swz_b8(cp_row[j]);
         }
     }
     const uint32_t cp_lds = lds_base + (uint32_t)q * 1024;
@@ -1169,13 +1186,27 @@ __device__ __forceinline__ void gemm_pp_group(const KernelArgs &args, uint8_t *l
     const int r0 = GRP * Cfg::WTM + l32;
     const uint32_t a_lane = A_BASE + (uint32_t)(r0 * 128) + ((half ^ swz_row128(r0)) << 4);
     uint32_t b_rd[NT];
-    {
+    if constexpr (E == 2) {
         const int g = lane >> 4, si = lane & 15;
         const int krow = 8 * (g >> 1) + (si >> 2);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             const int n = q * Cfg::WTN + nt * 32 + 16 * (g & 1) + 4 * (si & 3);
             b_rd[nt] = krow * B_ROW + (((n >> 3) ^ swz_b(krow)) << 4) + (n & 7) * 2;
+        }
+    } else {
+        // int8 (ds_read_b64_tr_b8): within each 16-lane group, lane i receives
+        // byte i % 8 of the 8-byte chunks that source lanes 2j + i / 8 (j = 0..7)
+        // address.  Source lane s of group g points at k-row 16*(g/2) + s/2 and
+        // columns 16*(g%2) + 8*(s%2) .. + 7 of the wave's 32-column block, so
+        // lane i of the group gets 8 consecutive k of column 16*(g%2) + i;
+        // lanes 32..63 take the next 16 k, as the MFMA operand wants.
+        const int g = lane >> 4, s = lane & 15;
+        const int krow = 16 * (g >> 1) + (s >> 1);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const int n = q * Cfg::WTN + nt * 32 + 16 * (g & 1) + 8 * (s & 1);
+            b_rd[nt] = krow * B_ROW + (((n >> 4) ^ swz_b8(krow)) << 4) + (n & 15);
         }
     }
     // a_x: the lane's A address with the half-iteration's parity folded in
@@ -1184,12 +1215,21 @@ __device__ __forceinline__ void gemm_pp_group(const KernelArgs &args, uint8_t *l
         const uint32_t x = (uint32_t)((st << 5) | ((mt & 1) << 6));
         return *(const u32x4 *)(lds + slot_off + mt * 4096 + (a_x ^ x));
     };
+    // a slab (one MFMA step) is 16 k-rows of 16-bit B or 32 k-rows of int8
     auto read_b = [&](uint32_t stage_off, int st, int nt) {
-        const uint8_t *base = lds + stage_off + b_rd[nt] + st * 16 * B_ROW;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(GSK_LDS(i16x4, base));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(GSK_LDS(i16x4, base + 4 * B_ROW));
-        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-        return u32x4{l2[0], l2[1], h2[0], h2[1]};
+        if constexpr (E == 2) {
+            const uint8_t *base = lds + stage_off + b_rd[nt] + st * 16 * B_ROW;
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(GSK_LDS(i16x4, base));
+            const i16x4 hi =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16(GSK_LDS(i16x4, base + 4 * B_ROW));
+            const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+            return u32x4{l2[0], l2[1], h2[0], h2[1]};
+        } else {
+            const uint8_t *base = lds + stage_off + b_rd[nt] + st * 32 * B_ROW;
+            const s32x2 lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32(GSK_LDS(s32x2, base));
+            const s32x2 hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32(GSK_LDS(s32x2, base + 8 * B_ROW));
+            return u32x4{(uint32_t)lo[0], (uint32_t)lo[1], (uint32_t)hi[0], (uint32_t)hi[1]};
+        }
     };
 
     f32x16 acc[MT][NT];
@@ -1217,14 +1257,14 @@ __device__ __forceinline__ void gemm_pp_group(const KernelArgs &args, uint8_t *l
             if constexpr (GRP == 0) {
                 const int row = cp_row[j];
                 off0[j] = m0 + row < args.M
-                              ? (uint32_t)(row * args.lda * 2 + (cp_chunk[j] << 4))
+                              ? (uint32_t)(row * args.lda * E + (cp_chunk[j] << 4))
                               : kOutOfRange;
                 off1[j] = m0 + row + 128 < args.M
-                              ? (uint32_t)((row + 128) * args.lda * 2 + (cp_chunk[j] << 4))
+                              ? (uint32_t)((row + 128) * args.lda * E + (cp_chunk[j] << 4))
                               : kOutOfRange;
             } else {
-                off0[j] = n0 + cp_chunk[j] * 8 < args.N
-                              ? (uint32_t)(cp_row[j] * args.ldb * 2 + (cp_chunk[j] << 4))
+                off0[j] = n0 + cp_chunk[j] * V < args.N
+                              ? (uint32_t)(cp_row[j] * args.ldb * E + (cp_chunk[j] << 4))
                               : kOutOfRange;
                 off1[j] = kOutOfRange;
             }
@@ -1240,13 +1280,13 @@ __device__ __forceinline__ void gemm_pp_group(const KernelArgs &args, uint8_t *l
                 const bool whole = ka + BK <= k_hi;
                 const int left = k_hi - ka;  // k values of this slab inside the item
                 const uint8_t *src =
-                    args.A + ((int64_t)m0 * args.lda + (ka <= ka_last ? ka : ka_last)) * 2;
+                    args.A + ((int64_t)m0 * args.lda + (ka <= ka_last ? ka : ka_last)) * E;
                 const uint32_t dst = cp_lds + A_BASE + (uint32_t)(((hc >> 1) % SA) * A_SLOT) +
                                      (uint32_t)(ph * (A_SLOT / 2));
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const uint32_t off = ph ? off1[j] : off0[j];
-                    copy16(rsrc_words(src), whole || cp_chunk[j] * 8 < left ? off : kOutOfRange,
+                    copy16(rsrc_words(src), whole || cp_chunk[j] * V < left ? off : kOutOfRange,
                            dst + j * 4096);
                 }
             } else {
@@ -1254,7 +1294,7 @@ __device__ __forceinline__ void gemm_pp_group(const KernelArgs &args, uint8_t *l
                 const bool whole = kb + HK <= k_hi;
                 const int left = k_hi - kb;
                 const uint8_t *src =
-                    args.B + ((int64_t)(kb <= kb_last ? kb : kb_last) * args.ldb + n0) * 2;
+                    args.B + ((int64_t)(kb <= kb_last ? kb : kb_last) * args.ldb + n0) * E;
                 const uint32_t dst = cp_lds + (uint32_t)((hc & (SB - 1)) * B_STAGE);
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
@@ -1334,8 +1374,8 @@ __device__ __forceinline__ void gemm_pp_group(const KernelArgs &args, uint8_t *l
         }
         wait_vmcnt<0>();  // zero-fill copies past the end have landed
 
-        finish_tile<256, 256, MT, NT>(acc, args, w, p, m0, n0, wave, lane, GRP * Cfg::WTM,
-                                      q * Cfg::WTN);
+        finish_tile<256, 256, MT, NT, DT == 3>(acc, args, w, p, m0, n0, wave, lane,
+                                               GRP * Cfg::WTM, q * Cfg::WTN);
     }
 }
 
@@ -1352,7 +1392,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel_pp(KernelArgs args)
     else
         gemm_pp_group<DT, 1>(args, lds, wave - 4, lane, p);
     if (args.split_fixup == 1)
-        reduce_split_tiles<256, 256, 2, 4>(args, p, wave, lane);
+        reduce_split_tiles<256, 256, 2, 4, DT == 3>(args, p, wave, lane);
 }
 
 template <int DT>
@@ -1378,12 +1418,13 @@ static int launch_gemm_pair(const KernelArgs &args, int grid, hipStream_t stream
     return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
-// Wave-specialised ping-pong kernel (fp16/bf16, 256x256)
+// Wave-specialised ping-pong kernel (fp16/bf16/int8, 256x256)
 #define GSK_PP(DT)                                                                               \
-    Variant{DT, 256, 256, 64, 2, 4, 512, (size_t)PairTile<DT, 256, 256, 2, 4>::LDS, 3,              \
-            PairTile<DT, 256, 256, 2, 4>::SB, &launch_gemm_pp<DT>,                                 \
-            (const void *)&gemm_kernel_pp<DT>, &launch_fixup<256, 256, 2, 4, false>, 0}
-// Register-staged kernel (fp32, int8, fp16/bf16 64x64)
+    Variant{DT, 256, 256, PairTile<DT, 256, 256, 2, 4>::BK, 2, 4, 512,                          \
+            (size_t)PairTile<DT, 256, 256, 2, 4>::LDS, 3, PairTile<DT, 256, 256, 2, 4>::SB,       \
+            &launch_gemm_pp<DT>, (const void *)&gemm_kernel_pp<DT>,                              \
+            &launch_fixup<256, 256, 2, 4, DT == 3>, 0}
+// Register-staged kernel (fp32, int8 tiles the ping-pong kernel does not take, fp16/bf16 64x64)
 #define GSK_STAGED(DT, BM, BN, WM, WN)                                                           \
     Variant{DT, BM, BN, Tile<DT, BM, BN, WM, WN>::BK, WM, WN, Tile<DT, BM, BN, WM, WN>::NTH,     \
             (size_t)Tile<DT, BM, BN, WM, WN>::LDS, 0, 0, &launch_gemm<DT, BM, BN, WM, WN>,        \
@@ -1412,8 +1453,8 @@ static const Variant kVariants[] = {
     GSK_PAIR(2, 128, 128, 2, 2),
     GSK_PAIR_STREAM(1, 256, 256, 2, 4), GSK_PAIR_STREAM(1, 256, 128, 4, 2),
     GSK_PAIR_STREAM(2, 256, 256, 2, 4), GSK_PAIR_STREAM(2, 256, 128, 4, 2),
-    // fp16 / bf16: wave-specialised ping-pong kernel (GEMM_FLAG_PING_PONG)
-    GSK_PP(1), GSK_PP(2),
+    // fp16 / bf16 / int8: wave-specialised ping-pong kernel (256x256)
+    GSK_PP(1), GSK_PP(2), GSK_PP(3),
     // fp16 / bf16 64x64 tiles (below the ring kernel's smallest tile), fp32, int8:
     // register-staged kernel
     GSK_STAGED(1, 64, 64, 2, 2), GSK_STAGED(2, 64, 64, 2, 2),

@@ -156,5 +156,10 @@ def test_ping_pong_is_the_256x256_default():
     with pytest.raises(ValueError, match="exclude"):
         gsk.plan_for_device(4096, 4096, 4096, "f16", "dp", bm=256, bn=256,
                             flags=gsk.FLAG_PING_PONG | gsk.FLAG_RING_KERNEL)
-    # fp32 and int8 keep the register-staged kernel
-    assert gsk.plan_for_device(1024, 1024, 1024, "i8", "dp", bm=256, bn=256).info["kernel_kind"] == 0
+    # int8 at 256x256: the ping-pong kernel; its other tile and GEMM_FLAG_RING_KERNEL
+    # (no int8 ring kernel) take the register-staged one, as fp32 always does
+    p = gsk.plan_for_device(1024, 1024, 1024, "i8", "dp", bm=256, bn=256)
+    assert p.info["kernel_kind"] == 3 and p.info["bk"] == 128
+    assert gsk.plan_for_device(1024, 1024, 1024, "i8", "dp", bm=128, bn=128).info["kernel_kind"] == 0
+    assert gsk.plan_for_device(1024, 1024, 1024, "i8", "dp", bm=256, bn=256,
+                               flags=gsk.FLAG_RING_KERNEL).info["kernel_kind"] == 0
