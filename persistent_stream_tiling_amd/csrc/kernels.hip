@@ -208,12 +208,12 @@ __device__ __forceinline__ uint32_t bf16_bits(float x)
 // 16-byte loads from element-aligned rows also rely on.  Otherwise (the tile
 // on the right edge of a C whose rows are not whole vectors) each element is
 // stored on its own.
-__device__ __forceinline__ void store_quad(const f32x4 &v, const KernelArgs &args,
-                                           __amdgpu_buffer_rsrc_t c_rsrc, int m0, int n0, int row,
-                                           int col, int half, int g, bool vec)
+// (row: tile row; n: the first of the four columns of C)
+__device__ __forceinline__ void store_quad_at(const f32x4 &v, const KernelArgs &args,
+                                              __amdgpu_buffer_rsrc_t c_rsrc, int m0, int row, int n,
+                                              bool vec)
 {
     const bool row_ok = m0 + row < args.M;
-    const int n = n0 + col + 8 * g + 4 * half;
     if (args.c_dtype != 0) {
         const uint32_t off = (uint32_t)((row * args.ldc + n) * 2);
         uint32_t h[4];
@@ -248,20 +248,57 @@ __device__ __forceinline__ void store_quad(const f32x4 &v, const KernelArgs &arg
     }
 }
 
+// Quad g of the lane (row and half as in the accumulator layout).
+__device__ __forceinline__ void store_quad(const f32x4 &v, const KernelArgs &args,
+                                           __amdgpu_buffer_rsrc_t c_rsrc, int m0, int n0, int row,
+                                           int col, int half, int g, bool vec)
+{
+    store_quad_at(v, args, c_rsrc, m0, row, n0 + col + 8 * g + 4 * half, vec);
+}
+
 // Descriptor for the C rows of a tile starting at row m0.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t c_rows(const KernelArgs &args, int m0)
 {
     return make_rsrc(args.C + (int64_t)m0 * args.ldc * (args.c_dtype != 0 ? 2 : 4));
 }
 
+// One 32x32 block at tile rows brow.., columns col.. (lane l holds row brow +
+// l % 32 at columns 8g + 4(l / 32) .. + 3 in quad g).  As laid out, a store of
+// quad g touches 32 rows with 32 bytes each.  For vector stores the quads are
+// first exchanged in pairs (2j, 2j + 1) with v_permlane16_swap, which swaps
+// lanes 16-31 and 48-63 of quad 2j with lanes 0-15 and 32-47 of quad 2j + 1:
+// afterwards quad 2j holds rows brow + (l % 16) and quad 2j + 1 rows brow +
+// 16 + (l % 16), at columns 16j + 8((l / 16) % 2) + 4(l / 32) .. + 3, so each
+// store covers 16 rows with 64 contiguous bytes (fp32 / int32 C; 32 bytes for
+// 16-bit C): half the cache lines per store.
 __device__ __forceinline__ void store_block(const f32x16 &blk, const KernelArgs &args,
                                             __amdgpu_buffer_rsrc_t c_rsrc, int m0, int n0,
-                                            int row, int col, int half, bool vec)
+                                            int brow, int col, int lane, bool vec)
 {
+    if (vec) {
+        const int r16 = lane & 15, c = 8 * ((lane >> 4) & 1) + 4 * (lane >> 5);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            f32x4 lo, hi;  // quads 2j and 2j + 1 after the exchange
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const auto r = __builtin_amdgcn_permlane16_swap(bits_of(blk[8 * j + e]),
+                                                                bits_of(blk[8 * j + 4 + e]), false,
+                                                                false);
+                lo[e] = __builtin_bit_cast(float, (uint32_t)r[0]);
+                hi[e] = __builtin_bit_cast(float, (uint32_t)r[1]);
+            }
+            const int n = n0 + col + 16 * j + c;
+            store_quad_at(lo, args, c_rsrc, m0, brow + r16, n, true);
+            store_quad_at(hi, args, c_rsrc, m0, brow + 16 + r16, n, true);
+        }
+        return;
+    }
+    const int row = brow + (lane & 31), half = lane >> 5;
 #pragma unroll
     for (int g = 0; g < 4; ++g)
         store_quad(f32x4{blk[4 * g], blk[4 * g + 1], blk[4 * g + 2], blk[4 * g + 3]}, args,
-                   c_rsrc, m0, n0, row, col, half, g, vec);
+                   c_rsrc, m0, n0, row, col, half, g, false);
 }
 
 // Vector stores for a tile at columns n0 .. n0 + BN - 1 (see store_quad).
@@ -342,7 +379,6 @@ __device__ __forceinline__ void finish_tile(f32x16 (&acc)[MT][NT], const KernelA
                                             int lane, int row0, int col0)
 {
     const int tid = threadIdx.x;
-    const int half = lane >> 5, l32 = lane & 31;
     const uint32_t lane_off = (uint32_t)lane * 16;
     if (w.role == ROLE_CONTRIB || (w.role == ROLE_OWNER && args.split_fixup)) {
         // A piece of a split tile: park it in this workgroup's slot, then
@@ -407,8 +443,8 @@ __device__ __forceinline__ void finish_tile(f32x16 (&acc)[MT][NT], const KernelA
                         blk[4 * g + 3] = acc_add<IACC>(blk[4 * g + 3], v[3]);
                     }
                 }
-                store_block(blk, args, c_rsrc, m0, n0, row0 + mt * 32 + l32, col0 + nt * 32,
-                            half, vec);
+                store_block(blk, args, c_rsrc, m0, n0, row0 + mt * 32, col0 + nt * 32, lane,
+                            vec);
             }
         return;
     }
@@ -416,8 +452,8 @@ __device__ __forceinline__ void finish_tile(f32x16 (&acc)[MT][NT], const KernelA
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
-            store_block(acc[mt][nt], args, c_rsrc, m0, n0, row0 + mt * 32 + l32, col0 + nt * 32,
-                        half, vec);
+            store_block(acc[mt][nt], args, c_rsrc, m0, n0, row0 + mt * 32, col0 + nt * 32, lane,
+                        vec);
 }
 
 // Reduce blocks [b0, b1) of split tile t (pieces of workgroups pf .. pl) and
