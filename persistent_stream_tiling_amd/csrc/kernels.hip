@@ -262,43 +262,49 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t c_rows(const KernelArgs &args,
     return make_rsrc(args.C + (int64_t)m0 * args.ldc * (args.c_dtype != 0 ? 2 : 4));
 }
 
-// One 32x32 block at tile rows brow.., columns col.. (lane l holds row brow +
-// l % 32 at columns 8g + 4(l / 32) .. + 3 in quad g).  As laid out, a store of
-// quad g touches 32 rows with 32 bytes each.  For vector stores the quads are
-// first exchanged in pairs (2j, 2j + 1) with v_permlane16_swap, which swaps
-// lanes 16-31 and 48-63 of quad 2j with lanes 0-15 and 32-47 of quad 2j + 1:
-// afterwards quad 2j holds rows brow + (l % 16) and quad 2j + 1 rows brow +
-// 16 + (l % 16), at columns 16j + 8((l / 16) % 2) + 4(l / 32) .. + 3, so each
-// store covers 16 rows with 64 contiguous bytes (fp32 / int32 C; 32 bytes for
-// 16-bit C): half the cache lines per store.
+// Quads 2j and 2j + 1 of one 32x32 block at tile rows brow.., columns col..
+// (lane l holds row brow + l % 32 at columns 8g + 4(l / 32) .. + 3 in quad
+// g).  As laid out, a store of one quad touches 32 rows with 32 bytes each.
+// For vector stores the two quads are first exchanged with
+// v_permlane16_swap, which swaps lanes 16-31 and 48-63 of quad 2j with lanes
+// 0-15 and 32-47 of quad 2j + 1: afterwards quad 2j holds rows brow + (l % 16)
+// and quad 2j + 1 rows brow + 16 + (l % 16), at columns 16j + 8((l / 16) % 2)
+// + 4(l / 32) .. + 3, so each store covers 16 rows with 64 contiguous bytes
+// (fp32 / int32 C; 32 bytes for 16-bit C): half the cache lines per store.
+__device__ __forceinline__ void store_quad_pair(const f32x4 &q0, const f32x4 &q1,
+                                                const KernelArgs &args,
+                                                __amdgpu_buffer_rsrc_t c_rsrc, int m0, int n0,
+                                                int brow, int col, int j, int lane, bool vec)
+{
+    if (vec) {
+        f32x4 lo, hi;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const auto r =
+                __builtin_amdgcn_permlane16_swap(bits_of(q0[e]), bits_of(q1[e]), false, false);
+            lo[e] = __builtin_bit_cast(float, (uint32_t)r[0]);
+            hi[e] = __builtin_bit_cast(float, (uint32_t)r[1]);
+        }
+        const int r16 = lane & 15;
+        const int n = n0 + col + 16 * j + 8 * ((lane >> 4) & 1) + 4 * (lane >> 5);
+        store_quad_at(lo, args, c_rsrc, m0, brow + r16, n, true);
+        store_quad_at(hi, args, c_rsrc, m0, brow + 16 + r16, n, true);
+        return;
+    }
+    const int row = brow + (lane & 31), half = lane >> 5;
+    store_quad(q0, args, c_rsrc, m0, n0, row, col, half, 2 * j, false);
+    store_quad(q1, args, c_rsrc, m0, n0, row, col, half, 2 * j + 1, false);
+}
+
 __device__ __forceinline__ void store_block(const f32x16 &blk, const KernelArgs &args,
                                             __amdgpu_buffer_rsrc_t c_rsrc, int m0, int n0,
                                             int brow, int col, int lane, bool vec)
 {
-    if (vec) {
-        const int r16 = lane & 15, c = 8 * ((lane >> 4) & 1) + 4 * (lane >> 5);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            f32x4 lo, hi;  // quads 2j and 2j + 1 after the exchange
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const auto r = __builtin_amdgcn_permlane16_swap(bits_of(blk[8 * j + e]),
-                                                                bits_of(blk[8 * j + 4 + e]), false,
-                                                                false);
-                lo[e] = __builtin_bit_cast(float, (uint32_t)r[0]);
-                hi[e] = __builtin_bit_cast(float, (uint32_t)r[1]);
-            }
-            const int n = n0 + col + 16 * j + c;
-            store_quad_at(lo, args, c_rsrc, m0, brow + r16, n, true);
-            store_quad_at(hi, args, c_rsrc, m0, brow + 16 + r16, n, true);
-        }
-        return;
-    }
-    const int row = brow + (lane & 31), half = lane >> 5;
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-        store_quad(f32x4{blk[4 * g], blk[4 * g + 1], blk[4 * g + 2], blk[4 * g + 3]}, args,
-                   c_rsrc, m0, n0, row, col, half, g, false);
+    for (int j = 0; j < 2; ++j)
+        store_quad_pair(f32x4{blk[8 * j], blk[8 * j + 1], blk[8 * j + 2], blk[8 * j + 3]},
+                        f32x4{blk[8 * j + 4], blk[8 * j + 5], blk[8 * j + 6], blk[8 * j + 7]},
+                        args, c_rsrc, m0, n0, brow, col, j, lane, vec);
 }
 
 // Vector stores for a tile at columns n0 .. n0 + BN - 1 (see store_quad).
@@ -460,16 +466,16 @@ __device__ __forceinline__ void finish_tile(f32x16 (&acc)[MT][NT], const KernelA
 // store them to C.  Every element adds the pieces in ascending k order (head
 // piece first), the order the head's workgroup would use, so the result does
 // not depend on who reduces.  Blocks are numbered in the writer's fragment
-// order (wave, mt, nt); work units are quarter blocks (4 values per lane,
-// 1 KiB per piece) dealt to this workgroup's nwaves waves, and a unit's pieces
-// are loaded QB at a time, all in flight together, then added in order.
+// order (wave, mt, nt); work units are half blocks (quads 2j and 2j + 1: 8
+// values per lane, 2 KiB per piece) dealt to this workgroup's nwaves waves,
+// and a unit's pieces are loaded QB at a time, all in flight together, then
+// added in order.
 template <int BM, int BN, int WM, int WN, bool IACC>
 __device__ __forceinline__ void reduce_tile_blocks(const KernelArgs &args, int32_t t, int32_t pf,
                                                    int32_t pl, int32_t b0, int32_t b1, int wave,
                                                    int nwaves, int lane)
 {
     constexpr int WTM = BM / WM, WTN = BN / WN, MT = WTM / 32, NT = WTN / 32;
-    const int half = lane >> 5, l32 = lane & 31;
     int tm, tn;
     tile_coords(args.P, t, &tm, &tn);
     const int m0 = tm * BM, n0 = tn * BN;
@@ -477,31 +483,35 @@ __device__ __forceinline__ void reduce_tile_blocks(const KernelArgs &args, int32
     const bool vec = vector_stores<BN>(args, n0);
     const __amdgpu_buffer_rsrc_t slots = make_rsrc(args.partials);
     const uint32_t slot_bytes = (uint32_t)(BM * BN * 4);
-    constexpr int QB = 16;
-    const int units = (b1 - b0) * 4;
+    constexpr int QB = 8;
+    const int units = (b1 - b0) * 2;
     for (int u = wave; u < units; u += nwaves) {
-        const int b = b0 + (u >> 2), g = u & 3;
+        const int b = b0 + (u >> 1), j = u & 1;
         const int ww = b / (MT * NT), mt = (b / NT) % MT, nt = b % NT;
-        const uint32_t frag_off = (uint32_t)(b * 4 * 64 + lane) * 16 + g * 1024;
-        f32x4 sum = f32x4{};
+        const uint32_t frag_off = (uint32_t)(b * 4 * 64 + lane) * 16 + j * 2048;
+        f32x4 s0 = f32x4{}, s1 = f32x4{};
         for (int32_t q0 = pf; q0 <= pl; q0 += QB) {
-            f32x4 v[QB];
+            f32x4 v[QB][2];
 #pragma unroll
             for (int i = 0; i < QB; ++i)
-                if (q0 + i <= pl)
-                    v[i] = __builtin_bit_cast(
-                        f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                   slots,
-                                   (int)((uint32_t)split_slot(q0 + i, q0 + i == pf) * slot_bytes +
-                                         frag_off),
-                                   0, kAgentCoherent));
+                if (q0 + i <= pl) {
+                    const int off =
+                        (int)((uint32_t)split_slot(q0 + i, q0 + i == pf) * slot_bytes + frag_off);
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+                        v[i][h] = __builtin_bit_cast(
+                            f32x4, __builtin_amdgcn_raw_buffer_load_b128(slots, off, h * 1024,
+                                                                         kAgentCoherent));
+                }
 #pragma unroll
             for (int i = 0; i < QB; ++i)
-                if (q0 + i <= pl)
-                    sum = q0 + i == pf ? v[i] : acc_add4<IACC>(sum, v[i]);
+                if (q0 + i <= pl) {
+                    s0 = q0 + i == pf ? v[i][0] : acc_add4<IACC>(s0, v[i][0]);
+                    s1 = q0 + i == pf ? v[i][1] : acc_add4<IACC>(s1, v[i][1]);
+                }
         }
-        store_quad(sum, args, c_rsrc, m0, n0, (ww / WN) * WTM + mt * 32 + l32,
-                   (ww % WN) * WTN + nt * 32, half, g, vec);
+        store_quad_pair(s0, s1, args, c_rsrc, m0, n0, (ww / WN) * WTM + mt * 32,
+                        (ww % WN) * WTN + nt * 32, j, lane, vec);
     }
 }
 
