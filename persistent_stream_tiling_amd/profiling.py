@@ -254,10 +254,11 @@ def kernel_resources(out, cmd_note):
              f"Command: `{cmd_note}`", "",
              f"Kernel source hash: {source_hash()}.  Template arguments: <dtype (0 fp32, 1 fp16, "
              "2 bf16, 3 int8), bm, bn, waves along M, waves along N[, non-temporal copies]>; "
-             "gemm_kernel_pp<dtype> is 256x256 with 2x4 waves.  gemm_kernel_pp is the fp16/bf16 "
-             "default at 256x256 (wave-specialised ping-pong), gemm_kernel_pair the direct-to-LDS "
-             "ring kernel (the other fp16/bf16 tiles), gemm_kernel the register-staged kernel "
-             "(fp32, int8, fp16/bf16 64x64).", "",
+             "gemm_kernel_pp<dtype> is 256x256 with 2x4 waves.  gemm_kernel_pp is the fp16/bf16/"
+             "int8 default at 256x256 (wave-specialised ping-pong), gemm_kernel_pair the "
+             "direct-to-LDS ring kernel (the other fp16/bf16 tiles), gemm_kernel the "
+             "register-staged kernel (fp32, the other int8 tiles, fp16/bf16 64x64); "
+             "fixup_kernel the two-kernel Stream-K fixup.", "",
              "| kernel | VGPRs | AGPRs | SGPRs | VGPR spills | SGPR spills | scratch B/lane | "
              "waves/SIMD | LDS B |", "|---|---|---|---|---|---|---|---|---|"]
     for r in gemm:
