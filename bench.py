@@ -648,7 +648,7 @@ def main():
 # Workloads measured after the headline one (the 16 irregular shapes follow
 # unless --configs standard).
 CONFIG_WORKLOADS = ["fp16_4096", "fp32_256", "fp16_1536x1536x8192", "bf16_512x512x65536",
-                    "bf16_8192x28672x8192"]
+                    "bf16_8192x28672x8192", "i8_4096"]
 HBM_BOUND = {"bf16_512x512x65536"}
 
 
