@@ -131,7 +131,7 @@ enum {
      * consecutive ids (what one die and one wave of workgroups hold) cover
      * compact blocks of tiles on any grid shape.  group_m is ignored. */
     GEMM_FLAG_HILBERT_ORDER = 1u << 10,
-    /* fp16/bf16, 256x256 tiles: the wave-specialised ping-pong kernel
+    /* fp16/bf16/int8, 256x256 tiles: the wave-specialised ping-pong kernel
      * (kernel_kind 3), the default wherever it is built (256x256 tiles in
      * the 2x4 wave layout, without GEMM_FLAG_STREAM_COPIES); this flag asks
      * for it explicitly and refuses tiles without it.  Its eight waves form
@@ -143,9 +143,10 @@ enum {
      * for NVIDIA's warp groups).  Same results as the ring kernel with the
      * same tile (the same MFMAs in the same order per element). */
     GEMM_FLAG_PING_PONG = 1u << 11,
-    /* fp16/bf16: never the ping-pong kernel; 256x256 tiles then run the ring
+    /* Never the ping-pong kernel: fp16/bf16 256x256 tiles then run the ring
      * kernel (kernel_kind 2), which is otherwise the default for the other
-     * tiles (for comparing the two). */
+     * fp16/bf16 tiles (for comparing the two); int8 256x256 tiles run the
+     * register-staged kernel (there is no int8 ring kernel). */
     GEMM_FLAG_RING_KERNEL = 1u << 12,
     /* Stream-K / hybrid: cut each of the T_sk Stream-K tiles into
      * s = min(floor(g / T_sk), ipt) pieces, one per workgroup, by the same
