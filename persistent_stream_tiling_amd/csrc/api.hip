@@ -742,19 +742,17 @@ int gemm_run(const gemm_plan *p, const void *A, const void *B, void *C, void *wo
     uint8_t *ws = (uint8_t *)workspace;
     const uint8_t *a = (const uint8_t *)A;
     const uint8_t *b = (const uint8_t *)B;
-    if (p->pack_a) {
-        if (launch_pack(A, ws + p->off_pack_a, p->M, p->K, p->K, p->lda, E, stream)) {
+    if (p->pack_a || p->pack_b) {
+        if (launch_pack_pair(A, ws + p->off_pack_a, p->pack_a ? p->M : 0, p->K, p->K, p->lda, B,
+                             ws + p->off_pack_b, p->pack_b ? p->K : 0, p->N, p->N, p->ldb, E,
+                             stream)) {
             set_error("pack launch failed");
             return -3;
         }
-        a = ws + p->off_pack_a;
-    }
-    if (p->pack_b) {
-        if (launch_pack(B, ws + p->off_pack_b, p->K, p->N, p->N, p->ldb, E, stream)) {
-            set_error("pack launch failed");
-            return -3;
-        }
-        b = ws + p->off_pack_b;
+        if (p->pack_a)
+            a = ws + p->off_pack_a;
+        if (p->pack_b)
+            b = ws + p->off_pack_b;
     }
     KernelArgs args;
     args.A = a;

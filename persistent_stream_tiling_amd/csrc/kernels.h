@@ -59,6 +59,13 @@ const Variant *variants(int *count);
 int launch_pack(const void *src, void *dst, int64_t rows, int64_t cols, int64_t ld_src,
                 int64_t ld_dst, int elem_size, hipStream_t stream);
 
+// Both operands' repacks (as launch_pack) in one launch; an operand with
+// rows = 0 is skipped.
+int launch_pack_pair(const void *a_src, void *a_dst, int64_t a_rows, int64_t a_cols,
+                     int64_t a_ld_src, int64_t a_ld_dst, const void *b_src, void *b_dst,
+                     int64_t b_rows, int64_t b_cols, int64_t b_ld_src, int64_t b_ld_dst,
+                     int elem_size, hipStream_t stream);
+
 // C[0 .. count) = 0 for elements of elem_size bytes (the K = 0 product).
 int launch_zero(void *C, int64_t count, int elem_size, hipStream_t stream);
 

@@ -1579,6 +1579,111 @@ int launch_pack(const void *src, void *dst, int64_t rows, int64_t cols, int64_t 
     return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
+// Both operands' repacks in one launch, over one flat index of destination
+// chunks: chunks [0, a.chunks) are A's, the rest B's.  A thread takes chunk
+// k of its operand at row k / cpr, chunk k mod cpr, so every lane has work
+// whatever the row length, where the row-per-workgroup kernel above leaves
+// lanes idle on short rows and pays a workgroup per row.  The division is a
+// multiply by a precomputed reciprocal: with s = ceil(log2 cpr), magic =
+// ceil(2^(31+s) / cpr) and k < 2^31, (k * magic) >> (31 + s) equals k / cpr
+// exactly (the rounding error of magic times k stays below 2^(31+s)).
+// Chunk contents as in pack_kernel.
+struct PackJob {
+    const void *src;
+    void *dst;
+    int64_t ld_src, ld_dst;  // elements
+    int64_t cols;            // elements of a source row
+    uint64_t magic;          // ceil(2^shift / cpr)
+    uint32_t shift;          // 31 + ceil(log2 cpr)
+    uint32_t cpr;            // 16-byte chunks per destination row (ld_dst / V)
+    uint32_t chunks;         // rows * cpr
+};
+
+template <typename T>
+__global__ __launch_bounds__(kPackThreads) void pack_pair_kernel(PackJob a, PackJob b)
+{
+    constexpr int V = 16 / (int)sizeof(T);
+    const uint32_t total = a.chunks + b.chunks;
+    const uint32_t stride = gridDim.x * kPackThreads;
+    for (uint32_t c = blockIdx.x * kPackThreads + threadIdx.x; c < total; c += stride) {
+        const bool second = c >= a.chunks;
+        const uint32_t k = second ? c - a.chunks : c;
+        const uint32_t cpr = second ? b.cpr : a.cpr;
+        const uint32_t r =
+            (uint32_t)(((uint64_t)k * (second ? b.magic : a.magic)) >> (second ? b.shift : a.shift));
+        const int64_t c0 = (int64_t)(k - r * cpr) * V;
+        const int64_t cols = second ? b.cols : a.cols;
+        const T *s = (const T *)(second ? b.src : a.src) + (int64_t)r * (second ? b.ld_src : a.ld_src) +
+                     c0;
+        T *d = (T *)(second ? b.dst : a.dst) + (int64_t)r * (second ? b.ld_dst : a.ld_dst) + c0;
+        u32x4 v;
+        if (c0 + V <= cols) {
+            __builtin_memcpy(&v, s, 16);
+        } else {
+            T e[V];
+#pragma unroll
+            for (int i = 0; i < V; ++i)
+                e[i] = c0 + i < cols ? s[i] : T(0);
+            __builtin_memcpy(&v, e, 16);
+        }
+        *(u32x4 *)d = v;
+    }
+}
+
+template <typename T>
+static void launch_pack_pair_t(const PackJob &a, const PackJob &b, hipStream_t stream)
+{
+    const uint32_t total = a.chunks + b.chunks;
+    // one chunk per thread: a thread that strides over several chunks has
+    // only one load in flight at a time (each store waits for its load), so
+    // a grid capped at a few workgroups per CU moved the large repacks ~7%
+    // slower than one workgroup per 256 chunks (total < 2^31: < 2^23 blocks)
+    const uint32_t blocks = (total + kPackThreads - 1) / kPackThreads;
+    hipLaunchKernelGGL(pack_pair_kernel<T>, dim3(blocks), dim3(kPackThreads), 0, stream, a, b);
+}
+
+int launch_pack_pair(const void *a_src, void *a_dst, int64_t a_rows, int64_t a_cols,
+                     int64_t a_ld_src, int64_t a_ld_dst, const void *b_src, void *b_dst,
+                     int64_t b_rows, int64_t b_cols, int64_t b_ld_src, int64_t b_ld_dst,
+                     int elem_size, hipStream_t stream)
+{
+    const int64_t V = 16 / elem_size;
+    const int64_t a_chunks = a_rows > 0 ? a_rows * (a_ld_dst / V) : 0;
+    const int64_t b_chunks = b_rows > 0 ? b_rows * (b_ld_dst / V) : 0;
+    if (a_chunks + b_chunks == 0)
+        return 0;
+    if (a_chunks + b_chunks >= ((int64_t)1 << 31)) {
+        // beyond the flat 32-bit chunk index: one row-per-workgroup launch each
+        if (a_chunks && launch_pack(a_src, a_dst, a_rows, a_cols, a_ld_src, a_ld_dst, elem_size,
+                                    stream))
+            return -3;
+        if (b_chunks && launch_pack(b_src, b_dst, b_rows, b_cols, b_ld_src, b_ld_dst, elem_size,
+                                    stream))
+            return -3;
+        return 0;
+    }
+    auto job = [V](const void *src, void *dst, int64_t ld_src, int64_t ld_dst, int64_t cols,
+                   int64_t chunks) {
+        const uint32_t cpr = (uint32_t)(ld_dst / V > 0 ? ld_dst / V : 1);
+        uint32_t s = 0;
+        while (((uint64_t)1 << s) < cpr)
+            ++s;
+        const uint64_t shift = 31 + s;
+        const uint64_t magic = (((uint64_t)1 << shift) + cpr - 1) / cpr;
+        return PackJob{src, dst, ld_src, ld_dst, cols, magic, (uint32_t)shift, cpr,
+                       (uint32_t)chunks};
+    };
+    const PackJob a = job(a_src, a_dst, a_ld_src, a_ld_dst, a_cols, a_chunks);
+    const PackJob b = job(b_src, b_dst, b_ld_src, b_ld_dst, b_cols, b_chunks);
+    if (elem_size == 1)
+        launch_pack_pair_t<uint8_t>(a, b, stream);
+    else if (elem_size == 2)
+        launch_pack_pair_t<uint16_t>(a, b, stream);
+    else
+        launch_pack_pair_t<uint32_t>(a, b, stream);
+    return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
 template <typename T>
 __global__ void zero_kernel(T *__restrict__ C, int64_t count)
 {
