@@ -258,6 +258,10 @@ gemm_plan *create(int64_t M, int64_t N, int64_t K, gemm_dtype dtype, gemm_schedu
     }
     const int E = elem_size(dtype);
     bool grid_from_model = false;
+    // the default hybrid plan where the cost model does not apply (more tiles
+    // than CUs for every tile shape): its Stream-K tiles are cut into their
+    // own pieces when there are at most g of them
+    bool default_hybrid_split = false;
     if (t.bm == 0 && t.bn == 0) {
         if (dtype == GEMM_F32)
             t.bm = t.bn = (M * N <= 512 * 512) ? 64 : 128;
@@ -268,12 +272,15 @@ gemm_plan *create(int64_t M, int64_t N, int64_t K, gemm_dtype dtype, gemm_schedu
             // asked for): the cost model picks both
             const uint32_t kernel_flags =
                 GEMM_FLAG_PING_PONG | GEMM_FLAG_RING_KERNEL | GEMM_FLAG_STREAM_COPIES;
-            if ((schedule == GEMM_STREAMK || schedule == GEMM_HYBRID) && t.grid == 0 &&
-                t.bk == 0 && t.wave_m == 0 && t.wave_n == 0 && t.stages == 0 &&
-                !(t.flags & kernel_flags) &&
-                streamk_default_plan(M, N, K, dev.cus, &t.bm, &t.bn, &t.grid)) {
+            const bool default_plan = (schedule == GEMM_STREAMK || schedule == GEMM_HYBRID) &&
+                                      t.grid == 0 && t.bk == 0 && t.wave_m == 0 &&
+                                      t.wave_n == 0 && t.stages == 0 && !(t.flags & kernel_flags);
+            int bm = 0, bn = 0, grid = 0;
+            if (default_plan && streamk_default_plan(M, N, K, dev.cus, &bm, &bn, &grid)) {
+                t.bm = bm, t.bn = bn, t.grid = grid;
                 grid_from_model = true;
             } else {
+                default_hybrid_split = default_plan && schedule == GEMM_HYBRID;
                 default_tile(M, N, K, schedule, dev.cus, &t.bm, &t.bn);
                 // a wave layout, ring depth or kernel family asked for may
                 // exist only at the 256x256 tile
@@ -401,7 +408,7 @@ gemm_plan *create(int64_t M, int64_t N, int64_t K, gemm_dtype dtype, gemm_schedu
         T_sk = 0;  // nothing to split: K = 0 is a fill, an empty C is a no-op
     P.T_sk = (int32_t)T_sk;
     p->iters_sk = T_sk * ipt;
-    if (T_sk > 0 && (t.flags & GEMM_FLAG_TILE_SPLIT)) {
+    if (T_sk > 0 && ((t.flags & GEMM_FLAG_TILE_SPLIT) || (default_hybrid_split && T_sk <= g))) {
         // each Stream-K tile cut into s pieces, one per workgroup
         if (g < T_sk) {
             set_error("GEMM_FLAG_TILE_SPLIT needs g >= the %lld Stream-K tiles (g = %d)",

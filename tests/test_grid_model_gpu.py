@@ -45,3 +45,19 @@ def test_default_plans_match_the_oracle(shape, dtype):
         compare(c.cpu().numpy(), ref, scale, dtype, what=plan.describe())
         if ws is not None:
             assert plan.workspace_status(ws) == 0
+
+
+@pytest.mark.parametrize("shape", [(4352, 4352, 640), (4160, 4224, 1000)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_default_hybrid_above_the_model(shape):
+    # more than 256 tiles for every tile shape: the default hybrid cuts each of
+    # its Stream-K tiles (fewer than g of them) into its own pieces
+    M, N, K = shape
+    a, b = inputs.operands(M, N, K, "f16", "normal", seed=M + N + K)
+    ref, scale = oracle.gemm(a, b, "f16")
+    plan, ws, c = run_gemm(to_device(a, "f16"), to_device(b, "f16"), M, N, K, "f16", "hybrid")
+    info = plan.info
+    assert grid_model.choose(M, N, K) is None
+    assert 0 < info["tiles_sk"] <= info["g"] and info["pieces_per_tile"] >= 2, plan.describe()
+    compare(c.cpu().numpy(), ref, scale, "f16", what=plan.describe())
+    assert plan.workspace_status(ws) == 0
