@@ -177,9 +177,10 @@ typedef struct {
                          s equal pieces (s in 1, 2, 3, 4, 6, 8, 16 dividing
                          the iterations per tile, g <= CUs) and g = CUs;
                          where every tile shape gives more than CUs tiles,
-                         g = CUs, and the hybrid cuts each of its Stream-K
-                         tiles into its own pieces (as GEMM_FLAG_TILE_SPLIT)
-                         when there are at most g of them.  (Issue #1393's
+                         g = CUs, and the hybrid keeps one Stream-K wave
+                         (T_sk = T mod g, as with GEMM_FLAG_ONE_TILE) and
+                         cuts each of its Stream-K tiles into its own pieces
+                         (as GEMM_FLAG_TILE_SPLIT).  (Issue #1393's
                          benchmark picks g per shape from a sweep; a library
                          call cannot.) */
     int32_t group_m;  /* tile-order group height (issue #1393 GROUP_M);

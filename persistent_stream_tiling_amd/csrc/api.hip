@@ -259,8 +259,8 @@ gemm_plan *create(int64_t M, int64_t N, int64_t K, gemm_dtype dtype, gemm_schedu
     const int E = elem_size(dtype);
     bool grid_from_model = false;
     // the default hybrid plan where the cost model does not apply (more tiles
-    // than CUs for every tile shape): its Stream-K tiles are cut into their
-    // own pieces when there are at most g of them
+    // than CUs for every tile shape): one Stream-K wave (T_sk = T mod g, as
+    // with GEMM_FLAG_ONE_TILE), its tiles cut into their own pieces
     bool default_hybrid_split = false;
     if (t.bm == 0 && t.bn == 0) {
         if (dtype == GEMM_F32)
@@ -398,7 +398,9 @@ gemm_plan *create(int64_t M, int64_t N, int64_t K, gemm_dtype dtype, gemm_schedu
         // plus one more full wave when two_tiles is on and more than g tiles
         // would stay data-parallel.
         T_sk = T % g;
-        if (!(t.flags & GEMM_FLAG_ONE_TILE) && T - T_sk > g)
+        // (the default plan above the cost model's range keeps one wave: its
+        // Stream-K tiles are then fewer than g and cut per tile, below)
+        if (!(t.flags & GEMM_FLAG_ONE_TILE) && !default_hybrid_split && T - T_sk > g)
             T_sk += g;
         P.g = g;
         P.grid = T_sk > 0 ? g : (int32_t)(T < g ? T : g);

@@ -100,16 +100,18 @@ def test_fit_recovers_known_coefficients():
 
 
 def test_default_hybrid_above_the_model_splits_per_tile():
-    # more than 256 tiles for every tile shape: 256x256 tiles, g = 256, and the
-    # hybrid's Stream-K tiles cut into their own pieces when there are at most g
+    # more than 256 tiles for every tile shape: 256x256 tiles, g = 256, one
+    # Stream-K wave (T_sk = T mod g) and its tiles cut into their own pieces
     for (M, N, K) in [(4608, 4352, 4096), (6144, 3072, 2048), (5120, 5120, 1024), (4352, 4352, 640),
-                      (9000, 9000, 1000), (8192, 28672, 8192), (4160, 4224, 1000)]:
+                      (9000, 9000, 1000), (8192, 28672, 8192), (4160, 4224, 1000),
+                      (6400, 6208, 320), (7680, 7168, 4096)]:
         assert grid_model.choose(M, N, K) is None
         for dtype in ("f16", "bf16"):
             info = gsk.plan_for_device(M, N, K, dtype, "hybrid").info
             T, ipt, g, t_sk = info["tiles"], -(-K // 64), info["g"], info["tiles_sk"]
             assert (info["bm"], info["bn"], g) == (256, 256, 256)
-            if 0 < t_sk <= g:
+            assert t_sk == T % g
+            if t_sk > 0:
                 s = min(g // t_sk, ipt)
                 assert info["pieces_per_tile"] == s and info["q"] == ipt // s
                 assert info["r"] == ipt % s

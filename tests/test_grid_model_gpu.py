@@ -47,11 +47,11 @@ def test_default_plans_match_the_oracle(shape, dtype):
             assert plan.workspace_status(ws) == 0
 
 
-@pytest.mark.parametrize("shape", [(4352, 4352, 640), (4160, 4224, 1000)],
+@pytest.mark.parametrize("shape", [(4352, 4352, 640), (4160, 4224, 1000), (6400, 6208, 320)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_default_hybrid_above_the_model(shape):
-    # more than 256 tiles for every tile shape: the default hybrid cuts each of
-    # its Stream-K tiles (fewer than g of them) into its own pieces
+    # more than 256 tiles for every tile shape: the default hybrid keeps one
+    # Stream-K wave (T mod g tiles) and cuts each of its tiles into its own pieces
     M, N, K = shape
     a, b = inputs.operands(M, N, K, "f16", "normal", seed=M + N + K)
     ref, scale = oracle.gemm(a, b, "f16")
