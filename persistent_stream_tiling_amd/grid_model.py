@@ -211,7 +211,7 @@ def _measured(r, bm, bn, g):
     return r["sk"].get(f"{bm}x{bn}/{g}")
 
 
-def report(records, coef, nfit, med_err, p90_err, cmd):
+def report(records, coef, nfit, med_err, p90_err, cmd, kernel_source=None):
     def gmean(x):
         return float(np.exp(np.mean(np.log(x))))
     rows, changed = [], 0
@@ -236,7 +236,8 @@ def report(records, coef, nfit, med_err, p90_err, cmd):
              "Stream-K with 256x256, 256x128 and 128x128 tiles at g in {256, 192, 128, 96, 64, "
              "32} and s*T for s in {1, 2, 3, 4, 6, 8, 16}; per shape, median over rounds "
              "interleaved across all these configurations, 512 MiB cache flush before each "
-             "run.", "",
+             "run." + (f"  Kernel source hash of the timed device code: {kernel_source}."
+                       if kernel_source else ""), "",
              "## Fit", "",
              f"Least squares over the {nfit} measured aligned splits (g = s*T, s dividing the "
              "iterations per tile): median relative error "
@@ -263,8 +264,9 @@ def report(records, coef, nfit, med_err, p90_err, cmd):
              f"{int((best < dp).sum())} |",
              f"| geomean pick / best measured | {gmean(old / best):.3f} | {gmean(pick / best):.3f} | 1 |",
              "", f"({len(rows)} shapes where the model applies; on the other "
-             f"{len(records) - len(rows)} every tile shape has more than 256 tiles and the "
-             "planner keeps one workgroup per CU.)", "",
+             f"{len(records) - len(rows)} every tile shape has more than 256 tiles: the planner "
+             "keeps one workgroup per CU for Stream-K, and the hybrid one Stream-K wave cut per "
+             "tile.)", "",
              "First 40 shapes (us):", "",
              "| M | N | K | dp | g = 256 (previous default) | planner's pick | pick | best measured |",
              "|---|---|---|---|---|---|---|---|"]
@@ -283,19 +285,25 @@ def main(argv=None):
     ap.add_argument("--from-json", default=None, help="fit and report from kept measurements")
     args = ap.parse_args(argv)
     from .inputs import log_sampled_shapes
+    kernel_source = None
     if args.from_json:
-        records = json.load(open(args.from_json))
+        kept = json.load(open(args.from_json))
+        # {"kernel_source": hash, "records": [...]}, or a bare record list
+        records = kept["records"] if isinstance(kept, dict) else kept
+        kernel_source = kept.get("kernel_source") if isinstance(kept, dict) else None
     else:
         import torch
         if not torch.cuda.is_available():
             sys.exit("the sweep needs a GPU (or --from-json)")
+        from .profiling import source_hash
+        kernel_source = source_hash()
         records = sweep(log_sampled_shapes(args.shapes), args.steps,
                         log=lambda m: print(m, flush=True))
         if args.json:
-            json.dump(records, open(args.json, "w"))
+            json.dump({"kernel_source": kernel_source, "records": records}, open(args.json, "w"))
     coef, nfit, med_err, p90 = fit(records)
     cmd = f"python -m persistent_stream_tiling_amd.grid_model --shapes {args.shapes} --out <file>"
-    text = report(records, coef, nfit, med_err, p90, cmd)
+    text = report(records, coef, nfit, med_err, p90, cmd, kernel_source)
     open(args.out, "w").write(text)
     print(text)
 
