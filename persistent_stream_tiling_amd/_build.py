@@ -39,8 +39,12 @@ PROBES = os.path.join(PKG, "probes")
 
 
 def build_probes(verbose=False):
-    """Compile the hardware-ceiling probe program (probes/ceilings.hip), a
-    measurement tool kept out of the library; returns its path."""
+    """Compile the measurement probes kept out of the library: the
+    hardware-ceiling program (probes/ceilings.hip) and the phase-timing copy of
+    the kernels (probes/libphase.so, see probes/phases.py); returns the
+    ceiling program's path."""
+    from .probes import phases
+    phases.build()
     src = os.path.join(PROBES, "ceilings.hip")
     out = os.path.join(PROBES, "ceilings")
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17",

@@ -6,6 +6,16 @@ under profiles/ (kernel-time table, HBM traffic per launch).
         --workload NAME --schedule NAME --out profiles/traffic.json --cmd "..."
   python -m persistent_stream_tiling_amd.profiling counters --csv DIR --workload NAME \
         --out profiles/FILE.md --cmd "..."
+  python -m persistent_stream_tiling_amd.profiling l2 --csv-a DIR --csv-b DIR --out FILE
+  python -m persistent_stream_tiling_amd.profiling tile-order --time F... --l2 DIR... \
+        --fetch DIR... --workload NAME... --order NAME... --out FILE
+  python -m persistent_stream_tiling_amd.profiling pack-share --csv DIR... \
+        --workload NAME... --out FILE
+
+`trace` with --bench-log also sets the traced bench run's own event timings
+beside the kernel times.  `l2`, `tile-order` and `pack-share` summarise the
+L2 counters of the 4096^3 kernel, the two tile orders, and the repack's share
+of the repacked shapes' steps (the commands they expect are in their output).
 
 `trace` reads a --kernel-trace --stats run of `bench.py` and reports, per
 schedule, the mean duration of the GEMM kernel over the timed steps (the
@@ -271,6 +281,166 @@ def kernel_resources(out, cmd_note):
     return text
 
 
+def pmc_table(dirs, labels, workloads, schedules, warmup, steps, title, cmds):
+    """Markdown table of counter means per (workload, schedule, run label)."""
+    groups = {}
+    for d, lab, w in zip(dirs, labels, workloads):
+        for sched, vals in pmc_summary(d, schedules, warmup, steps).items():
+            groups.setdefault((w, sched), {})[lab] = vals
+    counters = sorted({k for g in groups.values() for v in g.values() for k in v} - {"us"})
+    hits = {"TCC_HIT_sum", "TCC_MISS_sum"} <= set(counters)
+    lines = [f"# {title}", "", "Commands (one rocprofv3 run per line; counters summed over "
+             "dies and channels per dispatch, then averaged over the timed dispatches):", ""]
+    lines += [f"    {c}" for c in cmds]
+    lines += ["", f"Kernel source hash: {source_hash()}.", "",
+              "| workload | schedule | run | us | " + " | ".join(counters) +
+              (" | L2 hit rate |" if hits else " |"),
+              "|---" * (4 + len(counters) + hits) + "|"]
+    for (w, sched), labs in groups.items():
+        for lab, v in labs.items():
+            row = f"| {w} | {sched} | {lab} | {v['us']:.1f} | " + \
+                  " | ".join(f"{v.get(c, 0.0):.4g}" for c in counters)
+            if hits:
+                h, mi = v.get("TCC_HIT_sum", 0.0), v.get("TCC_MISS_sum", 0.0)
+                row += f" | {100 * h / max(h + mi, 1.0):.1f}%"
+            lines.append(row + " |")
+    return "\n".join(lines) + "\n"
+
+
+def bench_line(log):
+    """The JSON line a bench.py run printed (its last line starting with '{')."""
+    return json.loads([ln for ln in open(log) if ln.startswith("{")][-1])
+
+
+def trace_vs_events(means, line):
+    """The traced run's own HIP-event timings next to the kernel times."""
+    M, N, K = line["config"]["M"], line["config"]["N"], line["config"]["K"]
+    flop, rl = 2.0 * M * N * K, line["roofline"]
+    lines = ["", "## The same run's bench line (HIP events on the launch stream, one pair per step)",
+             "", f"The traced command printed its JSON line: value {line['value']:.2f} "
+             f"{line['unit']} ({line['config'].get('schedule')}), ms_per_step "
+             f"{line['ms_per_step']:.5f}, roofline.frac {rl['frac']:.4f}, roofline.traffic "
+             + (f"{rl['traffic'] / 1e6:.1f} MB per launch (from profiles/traffic.json)."
+                if rl.get("traffic") else "null."), "",
+             "| schedule | trace mean us (kernel only) | bench event mean us | events / trace | "
+             "rate from the trace | rate from the events |", "|---|---|---|---|---|---|"]
+    for sched, tr in means.items():
+        ev = line["schedules"][sched]["ms"] * 1e3
+        lines.append(f"| {sched} | {tr:.2f} | {ev:.2f} | {ev / tr:.3f} | "
+                     f"{flop / tr / 1e6:.0f} | {flop / ev / 1e6:.0f} |")
+    lines += ["", "The events also cover the kernel's dispatch after the cache flush and its "
+              "completion signal, so the bench's event-based figures err low against the kernel "
+              "time.", ""]
+    return "\n".join(lines)
+
+
+L2_CMDS = ["rocprofv3 --pmc TCC_READ_sum TCC_HIT_sum TCC_MISS_sum TCC_BUSY_sum GRBM_GUI_ACTIVE "
+           "--output-format csv -d <dir> -o run -- python3 bench.py --schedules dp --steps 3 "
+           "--warmup 1 --no-cpu-baseline --configs none",
+           "rocprofv3 --pmc TCC_READ_SECTORS_sum TCC_REQ_sum GRBM_GUI_ACTIVE --output-format csv "
+           "-d <dir> -o run -- python3 bench.py --schedules dp --steps 3 --warmup 1 "
+           "--no-cpu-baseline --configs none"]
+
+
+def l2_report(dir_a, dir_b):
+    """L2 reads of the 4096^3 fp16 kernel (data-parallel): the two counter runs
+    of L2_CMDS, then the derived rates."""
+    text = pmc_table([dir_a, dir_b], ["a", "b"], ["fp16_4096"] * 2, ["dp"], 1, 3,
+                     "L2 (TCC) reads of the 4096^3 fp16 ping-pong kernel, data-parallel schedule",
+                     L2_CMDS)
+    a = pmc_summary(dir_a, ["dp"], 1, 3)["dp"]
+    b = pmc_summary(dir_b, ["dp"], 1, 3)["dp"]
+    cyc = a["GRBM_GUI_ACTIVE"] / 8
+    reads, sect = a["TCC_READ_sum"], b["TCC_READ_SECTORS_sum"] * 32
+    hit = a["TCC_HIT_sum"] / max(a["TCC_HIT_sum"] + a["TCC_MISS_sum"], 1.0)
+    bw = sect / (a["us"] * 1e-6) / 1e12
+    lines = ["", "## Derived (from the table above)", "", "| quantity | value |", "|---|---|",
+             f"| dispatch duration (under counter collection) | {a['us']:.1f} us |",
+             f"| GPU-active cycles per die (GRBM_GUI_ACTIVE / 8) | {cyc:,.0f} (clock "
+             f"{cyc / a['us'] / 1e3:.2f} GHz) |",
+             f"| L2 read requests (TCC_READ_sum) | {reads:,.0f} |",
+             f"| L2 read sectors x 32 B (TCC_READ_SECTORS_sum) | {sect / 1e9:.3f} GB "
+             f"({b['TCC_READ_SECTORS_sum'] / reads:.2f} sectors = {sect / reads:.0f} B per "
+             "request) |",
+             f"| operand bytes the tiles copy into LDS (256 tiles x (256 + 256) x 4096 x 2 B) | "
+             f"{256 * 512 * 4096 * 2 / 1e9:.3f} GB |",
+             f"| L2 hit rate (TCC_HIT_sum / (TCC_HIT_sum + TCC_MISS_sum)) | {100 * hit:.1f}% |",
+             f"| L2 read bandwidth delivered | {bw:.2f} TB/s ({bw * 1e3 / 256:.0f} GB/s per CU) |",
+             "| L2 channel cycles with a request pending (TCC_BUSY_sum / (8 dies x 16 channels) "
+             f"/ die cycles) | {100 * a['TCC_BUSY_sum'] / 128 / cyc:.0f}% |", "",
+             "Every L2 read is a whole 128-byte line, and the lines read equal the operand bytes "
+             "the 256 tiles copy into LDS: the copies fetch nothing twice from L2.  The misses "
+             "are the lines each die fetches for its own share of A and B from HBM or the "
+             "Infinity Cache.", ""]
+    return text + "\n".join(lines)
+
+
+ORDER_CMD = ("python3 bench.py --workload <workload> --configs none --no-cpu-baseline "
+             "--schedules dp,hybrid --order <bands|hilbert>")
+
+
+def tile_order_report(times, l2_dirs, fetch_dirs, workloads, orders):
+    """Bands against the Hilbert order: per (workload, order) one timed bench
+    line, one L2 hit/miss counter run and one FETCH_SIZE run."""
+    rec = {(w, o): bench_line(t) for t, w, o in zip(times, workloads, orders)}
+    lines = ["# Tile order: GROUP_M bands against the Hilbert curve (L2 hits, HBM fetch, time)",
+             "", "Each workload's tuned launch configuration (tuning.py), once with its band "
+             "order (`--order bands`) and once with the Hilbert curve (`--order hilbert`, "
+             "GEMM_FLAG_HILBERT_ORDER); the die remap flag is the tuned one.", "",
+             "## Time (bench.py, mean of 20 cold runs)", "", f"    {ORDER_CMD} --steps 20", "",
+             "| workload | schedule | bands us | hilbert us | bands TFLOP/s | hilbert TFLOP/s |",
+             "|---|---|---|---|---|---|"]
+    for w in dict.fromkeys(workloads):
+        for sched in ("dp", "hybrid"):
+            x = rec[(w, "bands")]["schedules"][sched]
+            y = rec[(w, "hilbert")]["schedules"][sched]
+            lines.append(f"| {w} | {sched} | {x['ms'] * 1e3:.1f} | {y['ms'] * 1e3:.1f} | "
+                         f"{x['tflops']:.0f} | {y['tflops']:.0f} |")
+    for title, dirs, counters in (("L2 hit rate", l2_dirs, "TCC_HIT_sum TCC_MISS_sum GRBM_GUI_ACTIVE"),
+                                  ("HBM fetch (FETCH_SIZE, KiB per dispatch, uncalibrated)",
+                                   fetch_dirs, "FETCH_SIZE")):
+        cmd = (f"rocprofv3 --pmc {counters} --output-format csv -d <dir> -o run -- "
+               f"{ORDER_CMD} --steps 3 --warmup 1")
+        t = pmc_table(dirs, orders, workloads, ["dp", "hybrid"], 1, 3, title, [cmd])
+        lines += ["", "## " + t.split("\n", 1)[0][2:], t.split("\n", 1)[1].strip()]
+    return "\n".join(lines) + "\n"
+
+
+def pack_share(dirs, workloads):
+    """The repack's share of the steps of repacked shapes, from --kernel-trace
+    --stats runs of bench.py (one per workload)."""
+    lines = ["# Repack share of the irregular bf16 shapes (rocprofv3 kernel trace)", "",
+             f"Kernel source hash: {source_hash()}.  Rows whose byte length is not a multiple of "
+             "16 are repacked into the workspace before the GEMM; both operands' repacks run as "
+             "one launch (`pack_pair_kernel`, one thread per 16-byte destination chunk over a "
+             "flat index of both operands).  The 512 MiB fill kernel "
+             "(`vectorized_elementwise_kernel`) is the benchmark's cache flush, outside the "
+             "timed window.  The bench times four schedules, each in its tuned configuration, "
+             "so a workload's GEMM kernels can differ by schedule.", ""]
+    for d, w in zip(dirs, workloads):
+        rows = list(csv.DictReader(open(_find(d, "kernel_stats.csv"))))
+        lines += [f"## {w}", "", "    rocprofv3 --kernel-trace --stats --output-format csv -d "
+                  f"<dir> -o tr -- python3 bench.py --workload {w} --configs none "
+                  "--no-cpu-baseline --steps 5 --warmup 2", "",
+                  "| kernel | calls | average us | percent |", "|---|---|---|---|"]
+        pack = gemm = 0.0
+        calls = 0
+        for r in rows:
+            name = r["Name"].split("(")[0].replace("void ", "")
+            lines.append(f"| `{name[:70]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                         f"{float(r['Percentage']):.1f} |")
+            if "pack" in name:
+                pack += float(r["TotalDurationNs"]) / 1e3
+            elif "gemm_kernel" in name:
+                gemm += float(r["TotalDurationNs"]) / 1e3
+                calls += int(r["Calls"])
+        p, g = pack / max(calls, 1), gemm / max(calls, 1)
+        lines += ["", f"Per GEMM launch: pack {p:.1f} us + GEMM {g:.1f} us (mean over the "
+                  f"schedules' kernels); the pack is {100 * p / max(p + g, 1e-9):.0f}% of a step.",
+                  ""]
+    return "\n".join(lines)
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd_name", required=True)
@@ -281,6 +451,23 @@ def main():
     t.add_argument("--schedules", default="dp,persistent,streamk,hybrid")
     t.add_argument("--warmup", type=int, default=5)
     t.add_argument("--steps", type=int, default=20)
+    t.add_argument("--bench-log", default=None,
+                   help="the traced command's output: add its event timings beside the trace")
+    l2 = sub.add_parser("l2", help="L2 reads of the 4096^3 kernel (two --pmc runs)")
+    l2.add_argument("--csv-a", required=True)
+    l2.add_argument("--csv-b", required=True)
+    l2.add_argument("--out", required=True)
+    to = sub.add_parser("tile-order", help="bands against the Hilbert order")
+    to.add_argument("--time", nargs="+", required=True, help="bench.py output per (workload, order)")
+    to.add_argument("--l2", nargs="+", required=True, help="--pmc TCC_HIT/MISS run directories")
+    to.add_argument("--fetch", nargs="+", required=True, help="--pmc FETCH_SIZE run directories")
+    to.add_argument("--workload", nargs="+", required=True)
+    to.add_argument("--order", nargs="+", required=True)
+    to.add_argument("--out", required=True)
+    ps = sub.add_parser("pack-share", help="the repack's share of repacked shapes' steps")
+    ps.add_argument("--csv", nargs="+", required=True)
+    ps.add_argument("--workload", nargs="+", required=True)
+    ps.add_argument("--out", required=True)
     f = sub.add_parser("traffic")
     f.add_argument("--fetch", required=True)
     f.add_argument("--write", required=True)
@@ -367,28 +554,17 @@ def main():
         open(a.out, "w").write(text)
         print(text)
     elif a.cmd_name == "pmc":
-        groups = {}
-        for d, lab, w in zip(a.csv, a.label, a.workload):
-            for sched, vals in pmc_summary(d, a.schedules.split(","), a.warmup, a.steps).items():
-                groups.setdefault((w, sched), {})[lab] = vals
-        counters = sorted({k for g in groups.values() for v in g.values() for k in v} - {"us"})
-        lines = [f"# {a.title}", "", "Commands (one rocprofv3 run per line; counters summed over "
-                 "dies and channels per dispatch, then averaged over the timed dispatches):", ""]
-        lines += [f"    {c}" for c in a.cmd]
-        lines += ["", f"Kernel source hash: {source_hash()}.", "",
-                  "| workload | schedule | run | us | " + " | ".join(counters) +
-                  (" | L2 hit rate |" if {"TCC_HIT_sum", "TCC_MISS_sum"} <= set(counters) else " |"),
-                  "|---" * (4 + len(counters) + ({"TCC_HIT_sum", "TCC_MISS_sum"} <= set(counters)))
-                  + "|"]
-        for (w, sched), labs in groups.items():
-            for lab, v in labs.items():
-                row = f"| {w} | {sched} | {lab} | {v['us']:.1f} | " + \
-                      " | ".join(f"{v.get(c, 0.0):.4g}" for c in counters)
-                if {"TCC_HIT_sum", "TCC_MISS_sum"} <= set(counters):
-                    h, mi = v.get("TCC_HIT_sum", 0.0), v.get("TCC_MISS_sum", 0.0)
-                    row += f" | {100 * h / max(h + mi, 1.0):.1f}%"
-                lines.append(row + " |")
-        text = "\n".join(lines) + "\n"
+        text = pmc_table(a.csv, a.label, a.workload, a.schedules.split(","), a.warmup, a.steps,
+                         a.title, a.cmd)
+        open(a.out, "w").write(text)
+        print(text)
+    elif a.cmd_name in ("l2", "tile-order", "pack-share"):
+        if a.cmd_name == "l2":
+            text = l2_report(a.csv_a, a.csv_b)
+        elif a.cmd_name == "tile-order":
+            text = tile_order_report(a.time, a.l2, a.fetch, a.workload, a.order)
+        else:
+            text = pack_share(a.csv, a.workload)
         open(a.out, "w").write(text)
         print(text)
     elif a.cmd_name == "resources":
@@ -406,7 +582,13 @@ def main():
         open(a.out, "w").write(text)
         print(text)
     elif a.cmd_name == "trace":
-        text, _ = trace_summary(a.csv, a.schedules.split(","), a.warmup, a.steps, a.cmd)
+        if a.bench_log:
+            line = bench_line(a.bench_log)
+            scheds = list(line["schedules"])
+            text, means = trace_summary(a.csv, scheds, line["warmup"], line["steps"], a.cmd)
+            text += trace_vs_events(means, line)
+        else:
+            text, _ = trace_summary(a.csv, a.schedules.split(","), a.warmup, a.steps, a.cmd)
         open(a.out, "w").write(text)
         print(text)
     else:
