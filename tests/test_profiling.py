@@ -1,7 +1,7 @@
 """The profile summarisers (persistent_stream_tiling_amd.profiling) on small
 synthetic rocprofv3 outputs whose answers are known: which dispatches count
 as timed steps, the traffic calibration against the plain copy, counter
-means, the derived L2 figures and the repack share."""
+means, the derived L2 figures, the repack share and the operand-value table."""
 import csv
 import json
 import os
@@ -116,3 +116,12 @@ def test_pack_share(tmp_path):
         dict(Name=FILL, Calls=4, TotalDurationNs=40000, AverageNs=10000, Percentage=10.0)])
     text = profiling.pack_share([d], ["bf16_irregular_x"])
     assert "pack 10.0 us + GEMM 90.0 us" in text and "the pack is 10% of a step" in text
+
+
+def test_operand_power_report():
+    from persistent_stream_tiling_amd.probes import operand_power
+    med = {"normal": 125.0, "exponents": 105.0, "ones": 100.0, "zeros": 100.0}
+    text = operand_power.report("plan", med, 2.0 * 4096 ** 3, "cmd")
+    # 137.4 GFLOP in 125 us: 1099.5 TFLOP/s, 43.7% of the peak
+    assert "| normal | 125.0 | 1099.5 | 43.7% | 1.000 |" in text
+    assert "| zeros | 100.0 | 1374.4 | 54.6% | 0.800 |" in text
