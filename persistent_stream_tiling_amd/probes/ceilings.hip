@@ -461,6 +461,12 @@ int main()
                   hipLaunchKernelGGL((reads_kernel<4, 2, false, false, true>), dim3(256),
                                      dim3(512), 0, 0, 256, A, B, fout);
               }));
+    reads_row("4 waves of 128x128 (one per SIMD), no copies, no barriers, pseudo-random fp16 "
+              "fragments",
+              T.median_us([&] {
+                  hipLaunchKernelGGL((reads_kernel<4, 4, false, false, true>), dim3(256),
+                                     dim3(256), 0, 0, 256, A, B, fout);
+              }));
     reads_row("the ring kernel's structure (copies, barriers) with pseudo-random fp16 fragments",
               T.median_us([&] {
                   hipLaunchKernelGGL((reads_kernel<4, 2, true, true, true>), dim3(256),
