@@ -19,6 +19,11 @@ median of 24 launches per set.
 
   python -m persistent_stream_tiling_amd.probes.operand_power --out FILE \
       [--workload bf16_8192x28672x8192]
+
+Under `rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES` the same run
+gives each set's clock and MFMA utilisation; `--counters DIR` turns that
+run's counter CSV into a table (the dispatches come in the run's fixed order:
+one warm-up launch per set, then the interleaved rounds).
 """
 import argparse
 
@@ -73,6 +78,51 @@ def run(workload="fp16_4096", rounds=6, per_round=4):
     return plan.describe(), {k: float(np.median(v)) for k, v in times.items()}, flops
 
 
+def counters(csv_dir, rounds=6, per_round=4):
+    """Per operand set: mean dispatch time, clock (GRBM_GUI_ACTIVE of one die
+    per microsecond) and MFMA utilisation (SQ_VALU_MFMA_BUSY_CYCLES over 1024
+    SIMDs x one die's GRBM_GUI_ACTIVE) over its timed GEMM dispatches."""
+    import csv
+    import statistics
+    from ..profiling import SIMDS, XCDS, _find, _is_gemm
+    disp = {}
+    for r in csv.DictReader(open(_find(csv_dir, "counter_collection.csv"))):
+        if not _is_gemm(r["Kernel_Name"]):
+            continue
+        d = disp.setdefault(int(r["Dispatch_Id"]),
+                            {"us": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    seq = [disp[k] for k in sorted(disp)]
+    expected = len(SETS) * (1 + rounds * per_round)
+    if len(seq) != expected:
+        raise ValueError(f"{len(seq)} GEMM dispatches, expected {expected}")
+    out = {}
+    for i, d in enumerate(seq[len(SETS):]):
+        out.setdefault(SETS[(i // per_round) % len(SETS)], []).append(d)
+    res = {}
+    for k, ds in out.items():
+        gui = [d["GRBM_GUI_ACTIVE"] / XCDS for d in ds]
+        res[k] = dict(us=statistics.mean(d["us"] for d in ds),
+                      clock_ghz=statistics.mean(g / (d["us"] * 1e3) for g, d in zip(gui, ds)),
+                      mfma_util=statistics.mean(d["SQ_VALU_MFMA_BUSY_CYCLES"] / (g * SIMDS)
+                                                for g, d in zip(gui, ds)))
+    return res
+
+
+def counters_report(res, cmd, workload="fp16_4096"):
+    lines = [f"# {workload} GEMM: clock and MFMA utilisation against operand values", "",
+             f"Command: `{cmd}`, then `python -m persistent_stream_tiling_amd.probes."
+             "operand_power --counters <dir> --out <file>`.  Means over each set's 24 timed "
+             "dispatches (counter collection serialises dispatches).", "",
+             "- clock = GRBM_GUI_ACTIVE of one die / dispatch duration;",
+             "- MFMA util = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE of one die).",
+             "", "| operands | us | clock GHz | MFMA util |", "|---|---|---|---|"]
+    for k in SETS:
+        r = res[k]
+        lines.append(f"| {k} | {r['us']:.1f} | {r['clock_ghz']:.2f} | {100 * r['mfma_util']:.1f}% |")
+    return "\n".join(lines) + "\n"
+
+
 def report(desc, med, flops, cmd, workload="fp16_4096"):
     lines = [f"# {workload} GEMM: time against operand values", "",
              f"Command: `{cmd}` (`persistent_stream_tiling_amd/probes/operand_power.py`).", "",
@@ -90,7 +140,17 @@ def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--out", required=True)
     ap.add_argument("--workload", default="fp16_4096")
+    ap.add_argument("--counters", default=None,
+                    help="summarise this rocprofv3 --pmc output directory instead of timing")
     a = ap.parse_args(argv)
+    if a.counters:
+        cmd = ("rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES --output-format csv "
+               "-d <dir> -o run -- python3 -m persistent_stream_tiling_amd.probes.operand_power "
+               "--out <file>" + ("" if a.workload == "fp16_4096" else " --workload " + a.workload))
+        text = counters_report(counters(a.counters), cmd, a.workload)
+        open(a.out, "w").write(text)
+        print(text)
+        return
     desc, med, flops = run(a.workload)
     cmd = "python -m persistent_stream_tiling_amd.probes.operand_power --out " + a.out
     if a.workload != "fp16_4096":

@@ -125,3 +125,26 @@ def test_operand_power_report():
     # 137.4 GFLOP in 125 us: 1099.5 TFLOP/s, 43.7% of the peak
     assert "| normal | 125.0 | 1099.5 | 43.7% | 1.000 |" in text
     assert "| zeros | 100.0 | 1374.4 | 54.6% | 0.800 |" in text
+
+
+def test_operand_power_counters(tmp_path):
+    from persistent_stream_tiling_amd.probes import operand_power
+    # one warm-up dispatch per set, then 6 rounds of 4 per set; the clock of
+    # set k is 2.0 - 0.1 k GHz (GRBM_GUI_ACTIVE summed over 8 dies) and the
+    # MFMA busy cycles half of 1024 SIMDs' cycles
+    seq = []
+    for k in range(4):
+        seq.append((GEMM, 100, {"GRBM_GUI_ACTIVE": 1.0, "SQ_VALU_MFMA_BUSY_CYCLES": 1.0}))
+    for _ in range(6):
+        for k in range(4):
+            ghz = 2.0 - 0.1 * k
+            cyc = ghz * 1e3 * 100  # one die, 100 us
+            seq += [(GEMM, 100, {"GRBM_GUI_ACTIVE": 8 * cyc,
+                                 "SQ_VALU_MFMA_BUSY_CYCLES": 0.5 * 1024 * cyc})] * 4
+    _counters(str(tmp_path), seq)
+    res = operand_power.counters(str(tmp_path))
+    assert res["normal"]["clock_ghz"] == pytest.approx(2.0)
+    assert res["zeros"]["clock_ghz"] == pytest.approx(1.7)
+    assert res["ones"]["mfma_util"] == pytest.approx(0.5)
+    text = operand_power.counters_report(res, "cmd")
+    assert "| exponents | 100.0 | 1.90 | 50.0% |" in text
