@@ -1,4 +1,4 @@
-"""How the operand values set the speed of an fp16/bf16 GEMM (measurement only).
+"""How the operand values set the speed of a GEMM (measurement only).
 
 The matrix cores draw more power the more operand bits toggle from one MFMA
 to the next, and under sustained MFMA load the card's power limit sets the
@@ -8,7 +8,8 @@ with four operand sets:
 
   normal     the benchmark's seeded operands
   exponents  the same values with their mantissa bits cleared (signs and
-             exponents kept: powers of two)
+             exponents kept: powers of two; for int8, magnitudes rounded
+             down to a power of two)
   ones       every element 1.0
   zeros      every element 0.0
 
@@ -30,32 +31,53 @@ import argparse
 import numpy as np
 
 SETS = ("normal", "exponents", "ones", "zeros")
-# per dtype: the sign-and-exponent mask and the bits of 1.0 (as int16)
+# per 16-bit dtype: the sign-and-exponent mask and the bits of 1.0 (as int16)
 _BITS = {"f16": (-1024, 0x3C00), "bf16": (-128, 0x3F80)}  # 0xFC00, 0xFF80
+
+
+def pow2_int8(v):
+    """int8 values with their magnitude rounded down to a power of two (sign
+    kept, 0 stays 0): the int8 counterpart of clearing a float's mantissa."""
+    v = np.asarray(v, dtype=np.int8)
+    mag = np.abs(v.astype(np.int16))
+    p = np.zeros_like(mag)
+    nz = mag > 0
+    p[nz] = 1 << np.floor(np.log2(mag[nz])).astype(np.int16)
+    return (np.sign(v.astype(np.int16)) * p).astype(np.int8)
+
+
+def _operand_sets(dt, a_bits, b_bits):
+    """Host arrays (int16 bit patterns, or int8 values) per operand set."""
+    if dt == "i8":
+        a, b = a_bits.view(np.int8), b_bits.view(np.int8)
+        return {"normal": (a, b), "exponents": (pow2_int8(a), pow2_int8(b)),
+                "ones": (np.ones_like(a), np.ones_like(b)),
+                "zeros": (np.zeros_like(a), np.zeros_like(b))}
+    mask, one = _BITS[dt]
+    a, b = a_bits.view(np.int16), b_bits.view(np.int16)
+    return {"normal": (a, b), "exponents": (a & np.int16(mask), b & np.int16(mask)),
+            "ones": (np.full_like(a, one), np.full_like(b, one)),
+            "zeros": (np.zeros_like(a), np.zeros_like(b))}
 
 
 def run(workload="fp16_4096", rounds=6, per_round=4):
     import torch
     from .. import inputs, tuning
     from ..plan import GemmPlan
-    w = inputs.WORKLOADS[workload]
+    w = dict(inputs.WORKLOADS, **inputs.EXTRA_WORKLOADS)[workload]
     M, N, K, dt = w["M"], w["N"], w["K"], w["dtype"]
-    if dt not in _BITS:
-        raise ValueError(f"{workload}: fp16 or bf16 workloads only")
+    if dt not in ("f16", "bf16", "i8"):
+        raise ValueError(f"{workload}: fp16, bf16 or int8 workloads only")
     a_bits, b_bits = inputs.operands(M, N, K, dt, w["dist"], w["seed"], w["scale"])
-    a = torch.from_numpy(a_bits.view(np.int16)).cuda()
-    b = torch.from_numpy(b_bits.view(np.int16)).cuda()
-    mask, one = _BITS[dt]
-    keep = torch.tensor(mask, dtype=torch.int16, device="cuda")
-    ops = {"normal": (a, b), "exponents": (a & keep, b & keep),
-           "ones": (torch.full_like(a, one), torch.full_like(b, one)),
-           "zeros": (torch.zeros_like(a), torch.zeros_like(b))}
-    tt = torch.float16 if dt == "f16" else torch.bfloat16
-    ops = {k: (x.view(tt), y.view(tt)) for k, (x, y) in ops.items()}
+    tt = {"f16": torch.float16, "bf16": torch.bfloat16, "i8": torch.int8}[dt]
+    ops = {}
+    for k, (x, y) in _operand_sets(dt, a_bits, b_bits).items():
+        x, y = torch.from_numpy(np.ascontiguousarray(x)), torch.from_numpy(np.ascontiguousarray(y))
+        ops[k] = (x.cuda().view(tt), y.cuda().view(tt))
     tiles = tuning.bench_tiles(workload, "dp", dt)
     plan = GemmPlan(M, N, K, dt, "dp", **tiles)
     ws = plan.new_workspace()
-    c = torch.empty((M, N), device="cuda", dtype=torch.float32)
+    c = torch.empty((M, N), device="cuda", dtype=torch.int32 if dt == "i8" else torch.float32)
     flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
     for x, y in ops.values():
@@ -75,7 +97,7 @@ def run(workload="fp16_4096", rounds=6, per_round=4):
                 e.synchronize()
                 times[k].append(s.elapsed_time(e) * 1e3)
     flops = 2.0 * M * N * K
-    return plan.describe(), {k: float(np.median(v)) for k, v in times.items()}, flops
+    return plan.describe(), {k: float(np.median(v)) for k, v in times.items()}, flops, dt
 
 
 def counters(csv_dir, rounds=6, per_round=4):
@@ -123,15 +145,16 @@ def counters_report(res, cmd, workload="fp16_4096"):
     return "\n".join(lines) + "\n"
 
 
-def report(desc, med, flops, cmd, workload="fp16_4096"):
+def report(desc, med, flops, cmd, workload="fp16_4096", int8=False):
+    unit, peak = ("TOP/s", 5033.2) if int8 else ("TFLOP/s", 2516.6)
     lines = [f"# {workload} GEMM: time against operand values", "",
              f"Command: `{cmd}` (`persistent_stream_tiling_amd/probes/operand_power.py`).", "",
              f"Plan: `{desc[:120]}`", "",
-             "| operands | us | TFLOP/s | % of 2516.6 | time / normal |",
+             f"| operands | us | {unit} | % of {peak} | time / normal |",
              "|---|---|---|---|---|"]
     for k in SETS:
         tf = flops / med[k] / 1e6
-        lines.append(f"| {k} | {med[k]:.1f} | {tf:.1f} | {100 * tf / 2516.6:.1f}% | "
+        lines.append(f"| {k} | {med[k]:.1f} | {tf:.1f} | {100 * tf / peak:.1f}% | "
                      f"{med[k] / med['normal']:.3f} |")
     return "\n".join(lines) + "\n"
 
@@ -151,11 +174,11 @@ def main(argv=None):
         open(a.out, "w").write(text)
         print(text)
         return
-    desc, med, flops = run(a.workload)
+    desc, med, flops, dt = run(a.workload)
     cmd = "python -m persistent_stream_tiling_amd.probes.operand_power --out " + a.out
     if a.workload != "fp16_4096":
         cmd += " --workload " + a.workload
-    text = report(desc, med, flops, cmd, a.workload)
+    text = report(desc, med, flops, cmd, a.workload, int8=dt == "i8")
     open(a.out, "w").write(text)
     print(text)
 

@@ -148,3 +148,10 @@ def test_operand_power_counters(tmp_path):
     assert res["ones"]["mfma_util"] == pytest.approx(0.5)
     text = operand_power.counters_report(res, "cmd")
     assert "| exponents | 100.0 | 1.90 | 50.0% |" in text
+
+
+def test_int8_powers_of_two():
+    import numpy as np
+    from persistent_stream_tiling_amd.probes import operand_power
+    v = np.array([0, 1, 2, 3, 5, 127, -1, -3, -100, -128], dtype=np.int8)
+    assert operand_power.pow2_int8(v).tolist() == [0, 1, 2, 2, 4, 64, -1, -2, -64, -128]
