@@ -14,6 +14,15 @@ device buffer the host hands over with gemm_dbg_set():
 The stamps sit outside the MAC loops, so the timed code is the library's.
 The library itself carries none of this.
 
+In the ping-pong kernel, wave 0 of each group also reads s_memtime at the
+end of each of its MFMA bursts and after every phase barrier, and keeps, in
+registers, the summed burst lengths and the summed lengths of its MFMA
+phases (barrier exit to barrier exit); they are stored once, after its work
+loop.  Their ratio is the share of an MFMA phase the burst takes: the rest
+is the wait for the other group's memory work, the copies and the barrier.
+(The clock read waits for the wave's outstanding LDS reads, which the next
+MFMA needs anyway.)
+
   python -m persistent_stream_tiling_amd.probes.phases \\
       --case fp16_4096:dp:'{"bm":256,"bn":256,"group_m":4,"flags":2}' \\
       --case f16:4096x4096x64:dp:'{}'
@@ -37,6 +46,7 @@ from .. import _build
 LIB = os.path.join(_build.PROBES, "libphase.so")
 
 _HEADER = '''
+constexpr size_t PS_BASE = PS_BASE_VALUE;
 __device__ uint64_t *g_dbg;
 extern "C" int gemm_dbg_set(void *p)
 {
@@ -66,10 +76,60 @@ _PATCHES = [
      '''    WorkCursor cur = work_begin(P, p);
     WorkItem w;
     if (GRP == 0) dbg_stamp(p, 0);
+    const bool ps_on = g_dbg != nullptr && q == 0;
+    uint64_t ps_prev = 0, ps_burst = 0, ps_phase = 0;
+    uint32_t ps_n = 0;
+    bool ps_mfma = false;
     while (work_next(P, p, cur, w)) {
         int tm, tn;
         tile_coords(P, w.tile, &tm, &tn);
         const int m0 = tm * 256, n0 = tn * 256;'''),
+    # ping-pong kernel: MFMA burst and MFMA phase lengths
+    ('''        auto phase_end = [&]() {
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vmcnt<8>();
+            barrier_only();
+            __builtin_amdgcn_sched_barrier(0);
+        };''',
+     '''        auto phase_end = [&]() {
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vmcnt<8>();
+            barrier_only();
+            if (ps_on) {
+                const uint64_t t = __builtin_amdgcn_s_memtime();
+                if (ps_mfma)
+                    ps_phase += t - ps_prev;
+                ps_prev = t;
+                ps_mfma = false;
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        auto burst_end = [&]() {
+            if (ps_on) {
+                __builtin_amdgcn_sched_barrier(0);
+                ps_burst += __builtin_amdgcn_s_memtime() - ps_prev;
+                ps_mfma = true;
+                ++ps_n;
+            }
+        };'''),
+    ('''            if constexpr (GRP == 0) {
+                multiply();
+                phase_end();''',
+     '''            if constexpr (GRP == 0) {
+                multiply();
+                burst_end();
+                phase_end();'''),
+    ('''                phase_end();
+                multiply();
+                phase_end();
+            }
+        }''',
+     '''                phase_end();
+                multiply();
+                burst_end();
+                phase_end();
+            }
+        }'''),
     ('''            read_frags(0);
         }
         phase_end();
@@ -117,11 +177,32 @@ _PATCHES = [
 ]
 
 
+# where the ping-pong group body ends (its work loop closed): store the sums
+_PP_END = '''    }
+}
+
+template <int DT>
+__global__ __launch_bounds__(512, 1) void gemm_kernel_pp(KernelArgs args)'''
+_PP_SUMS = '''    }
+    if (ps_on && (threadIdx.x & 63) == 0) {
+        g_dbg[PS_BASE + ((size_t)p * 2 + GRP) * 4 + 0] = ps_burst;
+        g_dbg[PS_BASE + ((size_t)p * 2 + GRP) * 4 + 1] = ps_phase;
+        g_dbg[PS_BASE + ((size_t)p * 2 + GRP) * 4 + 2] = ps_n;
+    }
+}
+
+template <int DT>
+__global__ __launch_bounds__(512, 1) void gemm_kernel_pp(KernelArgs args)'''
+# u64 offset of the per-group sums in the stamp buffer (8 stamps per
+# workgroup come first)
+PS_BASE = 65536
+
+
 def instrument(src):
     """The instrumented text of kernels.hip."""
     i = src.index("namespace gsk {") + len("namespace gsk {")
-    src = src[:i] + _HEADER + src[i:]
-    for old, new in _PATCHES:
+    src = src[:i] + _HEADER.replace("PS_BASE_VALUE", str(PS_BASE)) + src[i:]
+    for old, new in _PATCHES + [(_PP_END, _PP_SUMS)]:
         if src.count(old) != 1:
             raise RuntimeError("kernels.hip changed: a phase stamp no longer has its place:\n" + old)
         src = src.replace(old, new)
@@ -189,7 +270,7 @@ def run(cases, runs=3):
         M, N, K, dt, a, b = _operands(spec, torch, inputs)
         plan = GemmPlan(M, N, K, dt, sched, **tiles)
         g = plan.info["launch_grid"]
-        if g * 8 * 8 > dbg.numel():
+        if (PS_BASE + g * 8) * 8 > dbg.numel():
             raise ValueError(f"{g} workgroups exceed the stamp buffer")
         ws = plan.new_workspace()
         c = torch.empty((M, N), device="cuda",
@@ -222,6 +303,19 @@ def run(cases, runs=3):
         print("  per-die mean (start to last MAC end) us: " +
               " ".join(f"{np.mean(m[die == x]):.1f}" for x in range(8) if (die == x).any()),
               flush=True)
+        if plan.info["kernel_kind"] == 3:
+            ps = dbg.cpu().numpy().view(np.uint64)[PS_BASE:PS_BASE + g * 8].reshape(g, 2, 4)
+            ps = ps.astype(np.float64)
+            for grp in range(2):
+                nb = ps[:, grp, 2]
+                ok = nb > 0
+                if not ok.any():
+                    continue
+                burst = ps[ok, grp, 0] / nb[ok]
+                phase = ps[ok, grp, 1] / nb[ok]
+                print(f"  group {grp}, per MFMA phase (s_memtime ticks, median over workgroups): "
+                      f"burst {np.median(burst):.0f}, phase {np.median(phase):.0f}, "
+                      f"burst / phase {np.median(burst / phase):.3f}", flush=True)
 
 
 def main(argv=None):
