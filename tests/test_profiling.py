@@ -155,3 +155,14 @@ def test_int8_powers_of_two():
     from persistent_stream_tiling_amd.probes import operand_power
     v = np.array([0, 1, 2, 3, 5, 127, -1, -3, -100, -128], dtype=np.int8)
     assert operand_power.pow2_int8(v).tolist() == [0, 1, 2, 2, 4, 64, -1, -2, -64, -128]
+
+
+def test_phase_probe_instruments_the_current_kernels():
+    # every stamp of the phase probe still finds its place in kernels.hip
+    from persistent_stream_tiling_amd import _build
+    from persistent_stream_tiling_amd.probes import phases
+    src = open(os.path.join(_build.CSRC, "kernels.hip")).read()
+    out = phases.instrument(src)
+    assert out.count("dbg_stamp(p, 0)") == 2      # ping-pong and ring kernels
+    assert out.count("burst_end();") == 2          # both ping-pong groups' bursts
+    assert "ps_burst" in out and f"PS_BASE = {phases.PS_BASE}" in out
