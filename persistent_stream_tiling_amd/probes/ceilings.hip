@@ -7,7 +7,8 @@
 //            the matrix-core rate the power limit allows with no memory work;
 //            with the same operands in every MFMA, or with four pseudo-random
 //            operand pairs taken in turn (every MFMA's operands differ from
-//            the previous one's, as in a GEMM).
+//            the previous one's, as in a GEMM); and v_mfma_i32_32x32x32_i8 on
+//            pseudo-random bytes.
 //   lds      16-byte LDS reads (ds_read_b128), 4..16 waves per CU.
 //   copy     the 4096^3 fp16 GEMM's operand traffic: 256 workgroups of 8
 //            waves, one 256x256 tile each, copying the A slab (256 rows x 128
@@ -92,6 +93,35 @@ __global__ __launch_bounds__(256) void mfma_kernel(float *out, int iters, float 
             acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc[j], 0, 0, 0);
     float s = 0.0f;
     for (int j = 0; j < 4; ++j)
+        for (int e = 0; e < 16; ++e)
+            s += acc[j][e];
+    out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+typedef int s32x4 __attribute__((ext_vector_type(4)));
+typedef int s32x16 __attribute__((ext_vector_type(16)));
+
+// int8: back-to-back v_mfma_i32_32x32x32_i8 (32x32x32, int32 sums), eight
+// independent accumulators per wave, pseudo-random operands (four pairs taken
+// in turn, as in mfma_rand_kernel), one or two waves per SIMD
+__global__ __launch_bounds__(256) void mfma_i8_kernel(int *out, int iters)
+{
+    s32x16 acc[8] = {};
+    s32x4 a[4], b[4];
+    for (int j = 0; j < 4; ++j)
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t h = ((uint32_t)(threadIdx.x * 37 + j * 4 + e) + 1u) * 2654435761u;
+            a[j][e] = (int)h;
+            b[j][e] = (int)((h ^ (h >> 13)) * 2246822519u);
+        }
+    for (int it = 0; it < iters; it += 2)
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int j = u & 7, k = (u + (u >> 3)) & 3;
+            acc[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[u & 3], b[k], acc[j], 0, 0, 0);
+        }
+    int s = 0;
+    for (int j = 0; j < 8; ++j)
         for (int e = 0; e < 16; ++e)
             s += acc[j][e];
     out[blockIdx.x * blockDim.x + threadIdx.x] = s;
@@ -396,6 +426,16 @@ int main()
         printf("| mfma | %d wave(s) per SIMD, %d x 4 MFMA 32x32x16 f16 per wave, pseudo-random "
                "operands | %.1f | %.1f TFLOP/s (%.1f%% of 2516.6) |\n",
                wps, iters, us, flops / us / 1e6, flops / us / 1e6 / 2516.6 * 100);
+    }
+    for (int wps : {1, 2}) {
+        const int g = cus * wps, iters = 20000;
+        const float us = T.median_us([&] {
+            hipLaunchKernelGGL(mfma_i8_kernel, dim3(g), dim3(256), 0, 0, (int *)fout, iters);
+        });
+        const double ops = (double)g * 4 * iters * 8 * 65536.0;
+        printf("| mfma | %d wave(s) per SIMD, %d x 8 MFMA 32x32x32 i8 per wave, pseudo-random "
+               "operands | %.1f | %.1f TOP/s (%.1f%% of 5033.2) |\n",
+               wps, iters, us, ops / us / 1e6, ops / us / 1e6 / 5033.2 * 100);
     }
     for (int wpc : {1, 2, 4}) {  // workgroups of 4 waves per CU
         const int g = cus * wpc, iters = 20000;
