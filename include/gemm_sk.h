@@ -172,7 +172,8 @@ typedef struct {
                          fp16/bf16 Stream-K and hybrid with bm = bn = 0 and
                          grid = 0 (and no wave layout, stages or kernel
                          flag): the planner picks the tile (256x256,
-                         256x128 or 128x128) and g from a cost model fitted
+                         256x128, 128x128, or 64x64 where that gives at
+                         most one tile per CU) and g from a cost model fitted
                          on MI355X, among g = s*T that cut every tile into
                          s equal pieces (s in 1, 2, 3, 4, 6, 8, 16 dividing
                          the iterations per tile, g <= CUs) and g = CUs;

@@ -108,7 +108,8 @@ void default_tile(int64_t M, int64_t N, int64_t K, gemm_schedule schedule, int c
 // tile nor a grid.  The Triton Stream-K issue's benchmark picks g per shape
 // from a sweep; a library call cannot sweep, so the planner estimates a few
 // candidate plans and takes the cheapest.  Candidates, for each of the tiles
-// 256x256, 256x128, 128x128 with T tiles of ipt 64-deep iterations:
+// 256x256, 256x128, 128x128, and 64x64 where it gives at most CUs tiles, with
+// T tiles of ipt 64-deep iterations:
 //   - g = s*T for s in {1, 2, 3, 4, 6, 8, 16} dividing ipt, g <= CUs: every
 //     workgroup runs one piece of exactly ipt/s iterations of one tile (s = 1
 //     is one whole tile per workgroup, no fixup);
@@ -119,17 +120,21 @@ void default_tile(int64_t M, int64_t N, int64_t K, gemm_schedule schedule, int c
 //      + [ranges cross tiles]*cross
 // The numbers are a least-squares fit to MI355X measurements of these
 // candidates on 260 log-sampled fp16 shapes (mean data-parallel time / model
-// pick 1.17, against 0.92 for one workgroup per CU); `cross` is what a
+// pick 1.22 there, also in two-fold cross-validation, against 0.99 for one
+// workgroup per CU); `cross` is what a
 // workgroup running pieces of two tiles costs: a second pipeline fill and a
 // second parked piece, which the tile's whole fixup then waits for.  Returns
 // false (keep the one-workgroup-per-CU default) when every tile shape has more
 // than CUs tiles.
 struct StreamKModel {
-    double c0, it[3], split[3], c_log, cross;
+    double c0, it[4], split[4], c_log, cross;
 };
-static const StreamKModel kSkModel = {13.12, {1.299, 0.975, 0.766}, {24.85, 14.02, 9.09}, -3.29,
-                                      13.36};
-static const int kSkTiles[3][2] = {{256, 256}, {256, 128}, {128, 128}};
+static const StreamKModel kSkModel = {13.31, {1.313, 0.979, 0.772, 0.929},
+                                      {15.36, 9.15, 6.42, 2.35}, 0.08, 10.03};
+static const int kSkTiles[4][2] = {{256, 256}, {256, 128}, {128, 128}, {64, 64}};
+// 64x64 (the register-staged kernel) is a candidate only while it gives at most
+// one tile per CU: slow per FLOP, it wins only where fixed per-tile costs dominate
+constexpr int kSkSmallTile = 3;
 static const int kSkSplits[] = {1, 2, 3, 4, 6, 8, 16};
 
 double streamk_estimate(int ti, int64_t T, int64_t ipt, int64_t g)
@@ -150,9 +155,9 @@ bool streamk_default_plan(int64_t M, int64_t N, int64_t K, int cus, int *bm, int
     const int64_t ipt = cdiv(K > 0 ? K : 1, 64);
     double best = 0.0;
     bool found = false, any_aligned = false;
-    for (int ti = 0; ti < 3; ++ti) {
+    for (int ti = 0; ti < 4; ++ti) {
         const int64_t T = cdiv(M, kSkTiles[ti][0]) * cdiv(N, kSkTiles[ti][1]);
-        if (T <= 0)
+        if (T <= 0 || (ti == kSkSmallTile && T > cus))
             continue;
         auto consider = [&](int64_t g) {
             const double e = streamk_estimate(ti, T, ipt, g);

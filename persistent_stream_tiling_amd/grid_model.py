@@ -13,8 +13,8 @@ the least-squares fit of the rule's coefficients, and the report that
 compares the rule's picks with one workgroup per CU and with the best plan
 measured.
 
-Candidates, per tile (256x256, 256x128, 128x128) with T tiles of ipt 64-deep
-iterations:
+Candidates, per tile (256x256, 256x128, 128x128, and 64x64 where it gives at
+most one tile per CU) with T tiles of ipt 64-deep iterations:
   * aligned splits: g = s*T for s in CANDIDATE_S dividing ipt with g <= CUs.
     Each workgroup then runs one piece of exactly ipt/s iterations inside one
     tile (s = 1: one whole tile per workgroup, no fixup);
@@ -39,14 +39,23 @@ import sys
 
 import numpy as np
 
-TILES = ((256, 256), (256, 128), (128, 128))
+TILES = ((256, 256), (256, 128), (128, 128), (64, 64))
+NT = len(TILES)
+# 64x64 (the register-staged kernel) is a candidate only while it gives at
+# most one tile per CU: it is slow per FLOP and wins only on the smallest
+# shapes, where fixed per-tile costs dominate
+SMALL_TILE = 3
+
+
+def tile_allowed(ti, T, cus=256):
+    return ti != SMALL_TILE or T <= cus
 CANDIDATE_S = (1, 2, 3, 4, 6, 8, 16)
 BK = 64
 # Fitted by `python -m persistent_stream_tiling_amd.grid_model` on MI355X (the
 # report is kept under profiles/); the planner in csrc/api.hip holds the same
 # numbers (a CPU test checks that both pick the same plan).
-COEF = dict(c0=13.12, it=(1.299, 0.975, 0.766), split=(24.85, 14.02, 9.09), c_log=-3.29,
-            cross=13.36)
+COEF = dict(c0=13.31, it=(1.313, 0.979, 0.772, 0.929), split=(15.36, 9.15, 6.42, 2.35),
+            c_log=0.08, cross=10.03)
 
 
 def cdiv(a, b):
@@ -78,6 +87,8 @@ def choose(M, N, K, cus=256, coef=None):
     best, any_aligned = None, False
     for ti, (bm, bn) in enumerate(TILES):
         T = cdiv(M, bm) * cdiv(N, bn)
+        if not tile_allowed(ti, T, cus):
+            continue
         for s in CANDIDATE_S:
             if ipt % s or s * T > cus:
                 continue
@@ -120,8 +131,10 @@ def sweep(shapes, steps, log=print):
         b = torch.randn((K, N), device="cuda", generator=gen).half()
         c = torch.empty((M, N), dtype=torch.float16, device="cuda")
         runs = [("dp", gsk.GemmPlan(M, N, K, "f16", "dp", flags=gsk.FLAG_C_INPUT_DTYPE))]
-        for bm, bn in TILES:
+        for ti, (bm, bn) in enumerate(TILES):
             T = cdiv(M, bm) * cdiv(N, bn)
+            if not tile_allowed(ti, T):
+                continue
             for g in candidate_grids(T):
                 if g <= T * cdiv(K, BK) or g == 256:
                     runs.append((f"{bm}x{bn}/{g}",
@@ -159,8 +172,8 @@ def _features(ti, T, ipt, s):
     bm, bn = TILES[ti]
     area = bm * bn / 65536.0
     q = ipt // s
-    f = [1.0] + [q * (ti == i) for i in range(3)]
-    f += [float(s > 1 and ti == i) for i in range(3)] + [(s > 1) * area * math.log2(s)]
+    f = [1.0] + [q * (ti == i) for i in range(NT)]
+    f += [float(s > 1 and ti == i) for i in range(NT)] + [(s > 1) * area * math.log2(s)]
     return f
 
 
@@ -186,8 +199,9 @@ def fit(records):
     X, y = np.array(X), np.array(y)
     c, *_ = np.linalg.lstsq(X, y, rcond=None)
     rel = np.abs(X @ c - y) / y
-    coef = dict(c0=float(c[0]), it=tuple(float(v) for v in c[1:4]),
-                split=tuple(float(v) for v in c[4:7]), c_log=float(c[7]), cross=0.0)
+    coef = dict(c0=float(c[0]), it=tuple(float(v) for v in c[1:1 + NT]),
+                split=tuple(float(v) for v in c[1 + NT:1 + 2 * NT]), c_log=float(c[1 + 2 * NT]),
+                cross=0.0)
     resid = []
     for r in records:
         ipt = cdiv(r["K"], BK)
@@ -233,7 +247,8 @@ def report(records, coef, nfit, med_err, p90_err, cmd, kernel_source=None):
     lines = [f"# Stream-K default plan model: `{cmd}`", "",
              f"{len(records)} log-sampled fp16 shapes (M, N, K in [256, 8192], multiples of 256, "
              "seeded), fp16 C.  Per shape: data-parallel with the library's default tile, and "
-             "Stream-K with 256x256, 256x128 and 128x128 tiles at g in {256, 192, 128, 96, 64, "
+             "Stream-K with 256x256, 256x128 and 128x128 tiles (and 64x64 where it gives at most "
+             "256 tiles) at g in {256, 192, 128, 96, 64, "
              "32} and s*T for s in {1, 2, 3, 4, 6, 8, 16}; per shape, median over rounds "
              "interleaved across all these configurations, 512 MiB cache flush before each "
              "run." + (f"  Kernel source hash of the timed device code: {kernel_source}."
@@ -242,10 +257,10 @@ def report(records, coef, nfit, med_err, p90_err, cmd, kernel_source=None):
              f"Least squares over the {nfit} measured aligned splits (g = s*T, s dividing the "
              "iterations per tile): median relative error "
              f"{med_err:.3f}, 90th percentile {p90_err:.3f}.", "",
-             "| coefficient | 256x256 | 256x128 | 128x128 |", "|---|---|---|---|",
-             f"| us per 64-deep iteration | {c['it'][0]:.3f} | {c['it'][1]:.3f} | {c['it'][2]:.3f} |",
-             f"| split tiles: us | {c['split'][0]:.2f} | {c['split'][1]:.2f} | "
-             f"{c['split'][2]:.2f} |", "",
+             "| coefficient | " + " | ".join(f"{bm}x{bn}" for bm, bn in TILES) + " |",
+             "|---|" + "---|" * NT,
+             "| us per 64-deep iteration | " + " | ".join(f"{v:.3f}" for v in c["it"]) + " |",
+             "| split tiles: us | " + " | ".join(f"{v:.2f}" for v in c["split"]) + " |", "",
              f"Constant {c['c0']:.2f} us; split tiles also "
              f"{c['c_log']:.2f} us x log2(s) x bm*bn/65536; ranges that cross tiles "
              f"{c['cross']:.1f} us (median residual of the measured g = 256 plans that cross).", "",

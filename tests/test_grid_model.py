@@ -81,13 +81,20 @@ def test_explicit_tile_or_grid_keeps_one_workgroup_per_cu():
 def test_fit_recovers_known_coefficients():
     # synthetic measurements made by the model itself: the fit returns the
     # coefficients it was given, and the crossing cost from the g = 256 plans
-    coef = dict(c0=10.0, it=(1.3, 1.0, 0.75), split=(23.0, 12.0, 6.75), c_log=-3.0, cross=12.0)
+    coef = dict(c0=10.0, it=(1.3, 1.0, 0.75, 0.6), split=(23.0, 12.0, 6.75, 4.0), c_log=-3.0,
+                cross=12.0)
     records = []
-    for (M, N, K) in log_sampled_shapes(60, seed=3):
+    # small shapes too, so that the 64x64 tile (at most 256 tiles) is measured
+    shapes = list(log_sampled_shapes(60, seed=3)) + [(256 * i, 256 * j, 512 * k)
+                                                      for i in (1, 2, 3) for j in (1, 2)
+                                                      for k in (1, 3, 8)]
+    for (M, N, K) in shapes:
         sk = {}
         for ti, (bm, bn) in enumerate(grid_model.TILES):
             T = -(-M // bm) * -(-N // bn)
             ipt = -(-K // 64)
+            if not grid_model.tile_allowed(ti, T):
+                continue
             for g in grid_model.candidate_grids(T):
                 sk[f"{bm}x{bn}/{g}"] = grid_model.estimate(coef, ti, T, ipt, g)
         records.append(dict(M=M, N=N, K=K, dp=50.0, sk=sk))
