@@ -22,7 +22,7 @@ if not torch.cuda.is_available():
 
 def _shapes():
     # the smallest log-sampled shapes (whole-matrix oracle in well under a
-    # second each), then ragged ones
+    # second each; four of them pick 64x64 tiles), then ragged ones
     small = sorted(set(log_sampled_shapes(200, seed=11)), key=lambda s: (s[0] * s[1] * s[2], s))[:8]
     # larger ones whose picks are 256x256 tiles, 128x128 at g = CUs or crossing ranges
     larger = [(1536, 1536, 8192), (3328, 768, 1792), (2048, 2048, 1024), (768, 256, 5632)]
