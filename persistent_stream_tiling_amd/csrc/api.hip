@@ -61,13 +61,19 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // Default output tile for fp16/bf16 when the caller names none.
 //
 // Tile-per-workgroup schedules (DP, persistent): a wave-quantisation model.
-// A launch runs ceil(T / CUs) waves of tiles; a tile costs a fixed prologue
-// and epilogue plus ipt MAC iterations (64 deep) at the per-iteration time
-// that tile shape sustains with every CU busy, measured on MI355X with the
-// ring kernel: 1.8 us (256x256), 1.47 / 1.45 us (256x128 / 128x256), 0.78 us
-// (128x128).  The cheapest estimate wins; ties go to the larger tile.  Big
-// tiles win once there are enough of them to fill the CUs (4096^3: 256x256),
-// small ones when the big ones would leave CUs idle (1536x1536x8192: 128x128).
+// A launch runs ceil(T / CUs) waves of tiles; a wave costs the tile shape's
+// fixed part (launch, prologue, C stores) plus ipt MAC iterations (64 deep)
+// at the per-iteration time that shape sustains.  Both are least-squares fits
+// to one-tile-per-workgroup launches of 86-235 log-sampled fp16 shapes on
+// MI355X (fp16 C; the sweep of the Stream-K cost model): 19.0 + 1.22 us per
+// iteration at 256x256, 13.0 + 0.97 at 256x128 (128x256, not in the sweep,
+// 1.3% faster per iteration as an earlier ring-kernel measurement had it),
+// 12.3 + 0.78 at 128x128, 7.9 + 1.00 at 64x64 (the register-staged kernel,
+// a candidate only while it gives at most one tile per CU).  The cheapest
+// estimate wins; ties go to the larger tile.  Big tiles win once there are
+// enough of them to fill the CUs (4096^3: 256x256), smaller ones when the big
+// ones would leave CUs idle (1536x1536x8192: 128x128), and 64x64 on the
+// smallest short-K shapes, where the fixed part dominates.
 //
 // Stream-K and hybrid spread the MAC iterations over all workgroups whatever
 // the tile, so the tile decides the efficiency of the MAC loop and the size
@@ -76,10 +82,13 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // most tiles are split).
 struct TileChoice {
     int bm, bn;
-    double iter_us;
+    double fixed_us, iter_us;
 };
-static const TileChoice kTileModel[] = {
-    {256, 256, 1.8}, {256, 128, 1.47}, {128, 256, 1.45}, {128, 128, 0.78}};
+static const TileChoice kTileModel[] = {{256, 256, 19.0, 1.22},
+                                        {256, 128, 13.0, 0.97},
+                                        {128, 256, 13.0, 0.957},
+                                        {128, 128, 12.3, 0.78},
+                                        {64, 64, 7.9, 1.00}};
 
 void default_tile(int64_t M, int64_t N, int64_t K, gemm_schedule schedule, int cus, int *bm,
                   int *bn)
@@ -90,12 +99,13 @@ void default_tile(int64_t M, int64_t N, int64_t K, gemm_schedule schedule, int c
         *bn = t256 * 2 >= cus ? 256 : 128;
         return;
     }
-    const double t0_us = 4.0;
     const int64_t ipt = cdiv(K > 0 ? K : 1, 64);
     double best = 0.0;
     for (const TileChoice &c : kTileModel) {
         const int64_t T = cdiv(M, c.bm) * cdiv(N, c.bn);
-        const double est = (double)cdiv(T, cus) * (t0_us + (double)ipt * c.iter_us);
+        if (c.bm == 64 && T > cus)
+            continue;
+        const double est = (double)cdiv(T, cus) * (c.fixed_us + (double)ipt * c.iter_us);
         if (&c == kTileModel || est < best) {
             best = est;
             *bm = c.bm;
